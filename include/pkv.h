@@ -1,0 +1,193 @@
+/*
+ * pkv.h -- C ABI of libpkv: attention over a paged KV cache on AMD MI355X
+ * (gfx950).
+ *
+ * The operations follow three web pages:
+ *   [KVP] "KV cache, PagedAttention and FlashAttention"
+ *   [MEM] "Memory Management in LLM Serving Systems"
+ *   [FP ] "The KV Cache from First Principles"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked (device) must point to GPU memory of the current HIP
+ *    device; pointers marked (host) to host memory.  The caller owns every
+ *    buffer, including workspaces, whose sizes the *_workspace() calls give.
+ *    The library allocates nothing and keeps no state between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it and the call returns without synchronising.
+ *  - Cache layout, one layer: cache[num_blocks][n_kv_heads][block_size][d_head],
+ *    row-major, so one (block, KV head) slab of block_size x d_head values is
+ *    contiguous.  A flat slot id is physical_block * block_size + offset.
+ *    One block table serves every layer: a physical block id names the same
+ *    token range in each layer's pool ([KVP] Problem 4, "The idea": a block
+ *    holds a fixed number of tokens across the layers' heads).
+ *  - block_table is int32 [batch][max_blocks_per_seq], row-major; entry j of
+ *    row s is the physical block of sequence s's logical block j.
+ *  - Errors: every argument is checked on the host before anything is
+ *    launched, so a call that returns an error has changed nothing on the
+ *    device (validate before mutate: [FP] "Implementation" checks the head
+ *    ratio before the cache is touched).  pkv_last_error() then describes
+ *    the failure (thread-local).  Device data (block ids, lengths, slots) is
+ *    not validated by the attention calls: ids outside [0, num_blocks) are
+ *    clamped into the pool so no access leaves it, but such a result is
+ *    meaningless; pkv_check_tables() validates tables on the device.
+ *  - Slots past a sequence's length and blocks no table names may hold any
+ *    bytes, NaN included; they never affect a result.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad head ratio */
+  PKV_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_head, block_size, dtype combination) */
+  PKV_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace() size */
+  PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} pkv_status;
+
+/* Element types. FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN), with
+ * one fp32 scale per (block, KV head): value = e4m3fn(byte) * scale. */
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3FN = 2 } pkv_dtype;
+
+int pkv_abi_version(void);
+const char* pkv_status_string(int status);
+/* Message for the last error returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Per-token KV-cache bytes: 2 (K and V) x n_layers x n_kv_heads x d_head x
+ * bytes_per_value ([KVP] Problem 3, "The concepts"; [MEM] "KV cache sizing").
+ * Returns -1 if an argument is negative. Host-only arithmetic. */
+int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head, int32_t bytes_per_value);
+
+/* Slot indexing ([KVP] Problem 4, "The idea": block = p // B, offset = p % B,
+ * address = block_table[seq][block] * block_bytes + offset * token_bytes;
+ * [MEM] "Walking the table"):
+ *   slot[t] = block_table[seq_ids[t]][positions[t] / B] * B + positions[t] % B
+ * seq_ids, positions: (device) int32 [num_tokens]; slot_mapping_out: (device)
+ * int64 [num_tokens].  A pair with seq_id outside [0, batch), position outside
+ * [0, max_blocks_per_seq * B) or a negative table entry yields slot -1
+ * (padding).  num_tokens == 0 is a no-op. */
+pkv_status pkv_slot_mapping(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                            const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                            int32_t block_size, int64_t* slot_mapping_out, void* stream);
+
+/* Append ([FP] "Deriving the cache": compute a token's key and value once and
+ * keep them; [KVP] Problem 4: blocks are filled as tokens arrive):
+ *   k_cache[slot / B][h][slot % B][:] = k[t][h][:]  (and v), for every KV head h.
+ * A bit copy in the cache's element type (FP8 bytes must be pre-quantised).
+ * k, v: (device) [num_tokens][n_kv_heads][d_head]; slot_mapping: (device)
+ * int64 [num_tokens]; a slot < 0 or >= num_blocks * B is skipped.  Two tokens
+ * with the same slot race (the result is one of them). */
+pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, int64_t num_blocks,
+                         const int64_t* slot_mapping, const void* k, const void* v, int32_t num_tokens,
+                         int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
+
+/* Gather (test/debug export of the block-table walk of [MEM] "Walking the
+ * table"): k_out[cu_seq_lens[s] + p][h][:] = k_cache[block_table[s][p / B]][h][p % B][:]
+ * for p < seq_lens[s]; same for v.  k_out, v_out: (device)
+ * [total_tokens][n_kv_heads][d_head] with total_tokens = sum(seq_lens);
+ * seq_lens (device) int32 [batch]; cu_seq_lens (device) int64 [batch + 1]
+ * (exclusive prefix sums).  Rows that would land outside [0, total_tokens)
+ * are not written. */
+pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                            int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int64_t* cu_seq_lens, int64_t total_tokens,
+                            int32_t batch, int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
+
+/* Device-side table check: counts, into *error_count (device int32, which the
+ * caller zeroes first), every sequence with seq_lens[s] < 0 or
+ * > max_blocks_per_seq * B and every table entry a sequence uses (logical
+ * block < ceil(seq_len / B)) that lies outside [0, num_blocks). */
+pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
+                            void* stream);
+
+/* Paged decode attention: one query per sequence attends every cached token
+ * of its sequence, the current one included ([FP] "The redundancy"; [KVP]
+ * Problem 5, "Serving note": decode reads K and V once):
+ *   out[s][h] = sum_p softmax_p(scale * q[s][h] . K_s[p]) V_s[p],  p < seq_lens[s],
+ * with K_s/V_s the rows of KV head h / (n_q_heads / n_kv_heads) gathered
+ * through block_table ([MEM] "MHA, MQA, and GQA"; [FP] "Grouped-query
+ * attention").  Computed FlashAttention-style ([KVP] Problem 5, "Tiling",
+ * "Online softmax"; [MEM] "FlashAttention-2"): the sequence is split into
+ * partitions processed by separate workgroups, each with a running max and
+ * sum, then merged; scores never reach memory.
+ *   q: (device) [batch][n_q_heads][d_head]; out: (device) same shape.
+ *   k_cache, v_cache: (device) [num_blocks][n_kv_heads][block_size][d_head].
+ *   k_scale, v_scale: (device) fp32 [num_blocks][n_kv_heads] for FP8, else NULL.
+ *   seq_lens: (device) int32 [batch], 0 <= seq_lens[s] <= max_blocks_per_seq * B;
+ *   a sequence of length 0 yields zeros.
+ * Supported: d_head in {64, 128}; block_size 16; (q, kv) in {(F32, F32),
+ * (BF16, BF16), (BF16, FP8_E4M3FN)}; out F32 or BF16; n_q_heads a multiple of
+ * n_kv_heads.  workspace: (device) at least
+ * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned.
+ * Accumulation is fp32; with bf16/fp8 KV the softmax weights are rounded to
+ * bf16 before the value product and the normaliser sums the same rounded
+ * weights. */
+pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                 const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                 const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                 int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/* Same as pkv_paged_attn_decode with an explicit partition size in tokens
+ * (0 = the library's choice).  partition_tokens must be a positive multiple of
+ * 256 (of 64 * the library's chunk for the head group).  Used to test that
+ * results do not depend on the split and to tune it. */
+pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                             const float* k_scale, const float* v_scale,
+                                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                                             const int32_t* seq_lens, int32_t batch, int64_t num_blocks,
+                                             int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                             int32_t block_size, float scale, int32_t partition_tokens,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes the decode call needs (partition_tokens as above, 0 = the
+ * library's choice).  Returns 0 for invalid arguments. */
+size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens);
+
+/* Chunked prefill attention: each sequence s brings q_len = cu_q_lens[s+1] -
+ * cu_q_lens[s] new query tokens at absolute positions context_lens[s] + i.
+ * With causal = 1, query i attends keys 0 .. context_lens[s] + i; with
+ * causal = 0, every key of the context and the chunk ([MEM] "FlashAttention":
+ * masked positions get -inf and fully masked blocks are skipped).  The chunk's
+ * own K/V must already be appended to the cache (pkv_kv_append).  Computed
+ * with bf16 MFMA tiles, fp32 accumulation and an online softmax per query row;
+ * the softmax weights enter the value product as bf16.
+ *   q, out: (device) packed [total_q][n_q_heads][d_head];
+ *   cu_q_lens: (device) int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing,
+ *   cu_q_lens[num_seqs] = total_q, each q_len <= max_q_len;
+ *   context_lens: (device) int32 [num_seqs];
+ *   context_lens[s] + q_len <= max_blocks_per_seq * B.
+ * Supported: d_head 128; block_size 16; q and KV BF16; out F32 or BF16.
+ * workspace: pkv_paged_attn_prefill_workspace(...) bytes (may be 0, then the
+ * pointer may be NULL). */
+pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                        const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                        const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale,
+                                        int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
+
+size_t pkv_paged_attn_prefill_workspace(int32_t num_seqs, int32_t max_q_len, int32_t n_q_heads, int32_t d_head);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,218 @@
+"""Python binding of libpkv (attention over a paged KV cache, MI355X / gfx950).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every computation runs in the HIP kernels of ``libpkv.so``.  The
+entry points carry the C ABI's names without the ``pkv_`` prefix.  The first
+call into the library fails loudly (ImportError) if it has not been built
+(``python -m paged_kv_cache_blocks_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+_lib = None
+
+# status codes and element types (include/pkv.h)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+F32, BF16, FP8_E4M3FN = 0, 1, 2
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "pkv_abi_version": ([], ctypes.c_int),
+    "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "pkv_last_error": ([], ctypes.c_char_p),
+    "pkv_kv_bytes_per_token": ([_i32, _i32, _i32, _i32], _i64),
+    "pkv_slot_mapping": ([_vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "pkv_kv_append": ([_vp, _vp, ctypes.c_int, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "pkv_paged_gather": ([_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
+                          _vp],
+                         ctypes.c_int),
+    "pkv_check_tables": ([_vp, _i32, _vp, _i32, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "pkv_paged_attn_decode": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp,
+                               _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp], ctypes.c_int),
+    "pkv_paged_attn_decode_partitioned": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                           _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp],
+                                          ctypes.c_int),
+    "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pkv_paged_attn_prefill_chunk": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                                      ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
+                                      _sz, _vp], ctypes.c_int),
+    "pkv_paged_attn_prefill_workspace": ([_i32, _i32, _i32, _i32], _sz),
+}
+
+
+def load():
+    """The loaded libpkv.so (ctypes.CDLL); raises ImportError if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libpkv.so is not built ({LIB_PATH}); run `python -m paged_kv_cache_blocks_amd.build`")
+        cdll = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(cdll, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = cdll
+    return _lib
+
+
+def __getattr__(name):
+    if name == "lib":
+        return load()
+    raise AttributeError(name)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{load().pkv_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != OK:
+        raise PkvError(status, load().pkv_last_error().decode())
+
+
+def abi_version() -> int:
+    return load().pkv_abi_version()
+
+
+def kv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, bytes_per_value: int) -> int:
+    return load().pkv_kv_bytes_per_token(n_layers, n_kv_heads, d_head, bytes_per_value)
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3FN
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def slot_mapping(block_table: torch.Tensor, seq_ids: torch.Tensor, positions: torch.Tensor, block_size: int = 16,
+                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_ids, torch.int32, "seq_ids")
+    _need(positions, torch.int32, "positions")
+    n = seq_ids.numel()
+    if positions.numel() != n:
+        raise ValueError("seq_ids and positions differ in length")
+    if out is None:
+        out = torch.empty(n, dtype=torch.int64, device=seq_ids.device)
+    _need(out, torch.int64, "out")
+    _check(load().pkv_slot_mapping(_ptr(block_table), block_table.shape[0], block_table.shape[1], _ptr(seq_ids),
+                                _ptr(positions), n, block_size, _ptr(out), _stream(stream)))
+    return out
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.Tensor, k: torch.Tensor,
+              v: torch.Tensor, stream=None) -> None:
+    """Copy k[t], v[t] ([num_tokens, n_kv, d]) into their slots of one layer's caches."""
+    _need(slot_mapping, torch.int64, "slot_mapping")
+    nb, n_kv, bs, d = k_cache.shape
+    if k.dtype != k_cache.dtype or v.dtype != v_cache.dtype or v_cache.shape != k_cache.shape:
+        raise TypeError("k/v must match the caches")
+    if k.shape != (slot_mapping.numel(), n_kv, d) or v.shape != k.shape:
+        raise ValueError("k, v must be [num_tokens, n_kv, d]")
+    _check(load().pkv_kv_append(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, _ptr(slot_mapping), _ptr(k),
+                             _ptr(v), slot_mapping.numel(), n_kv, d, bs, _stream(stream)))
+
+
+def paged_gather(k_cache, v_cache, block_table, seq_lens, cu_seq_lens, total_tokens: int, stream=None):
+    """Rows of every sequence in logical order: returns (k, v) [total_tokens, n_kv, d]."""
+    nb, n_kv, bs, d = k_cache.shape
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _need(cu_seq_lens, torch.int64, "cu_seq_lens")
+    k_out = torch.empty((total_tokens, n_kv, d), dtype=k_cache.dtype, device=k_cache.device)
+    v_out = torch.empty_like(k_out)
+    if total_tokens == 0:
+        return k_out, v_out
+    _check(load().pkv_paged_gather(_ptr(k_out), _ptr(v_out), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb,
+                                _ptr(block_table), block_table.shape[1], _ptr(seq_lens), _ptr(cu_seq_lens),
+                                int(total_tokens), block_table.shape[0], n_kv, d, bs, _stream(stream)))
+    return k_out, v_out
+
+
+def check_tables(block_table, seq_lens, num_blocks: int, block_size: int = 16, stream=None) -> int:
+    """Number of invalid table entries / lengths (synchronises)."""
+    err = torch.zeros(1, dtype=torch.int32, device=block_table.device)
+    _check(load().pkv_check_tables(_ptr(block_table), block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
+                                num_blocks, block_size, _ptr(err), _stream(stream)))
+    return int(err.item())
+
+
+def paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
+                                partition_tokens=0) -> int:
+    return load().pkv_paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq,
+                                               block_size, partition_tokens)
+
+
+def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_kv_heads, d_head, block_size, scale,
+                      *, k_scale=None, v_scale=None, out=None, out_dtype=torch.float32, workspace=None,
+                      partition_tokens: int = 0, stream=None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the seq_lens[s] cached tokens of sequence s."""
+    batch = q.shape[0]
+    nb = k_cache.shape[0]
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if out is None:
+        out = torch.empty((batch, n_q_heads, d_head), dtype=out_dtype, device=q.device)
+    ws_bytes = paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, block_table.shape[1], block_size,
+                                           partition_tokens)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pkv_paged_attn_decode_partitioned(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb, n_q_heads,
+        n_kv_heads, d_head, block_size, float(scale), int(partition_tokens), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def paged_attn_prefill_chunk(q, cu_q_lens, context_lens, max_q_len, k_cache, v_cache, block_table, n_q_heads,
+                             n_kv_heads, d_head, block_size, scale, *, causal: bool = True, out=None,
+                             out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Packed chunk queries [total_q, n_q, d] against cached context + chunk (already appended)."""
+    total_q = q.shape[0]
+    _need(cu_q_lens, torch.int32, "cu_q_lens")
+    _need(context_lens, torch.int32, "context_lens")
+    _need(block_table, torch.int32, "block_table")
+    if out is None:
+        out = torch.empty((total_q, n_q_heads, d_head), dtype=out_dtype, device=q.device)
+    _check(load().pkv_paged_attn_prefill_chunk(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(cu_q_lens), _ptr(context_lens),
+        context_lens.numel(), total_q, int(max_q_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), None, None,
+        _ptr(block_table), block_table.shape[1], k_cache.shape[0], n_q_heads, n_kv_heads, d_head, block_size,
+        float(scale), 1 if causal else 0, None, 0, _stream(stream)))
+    return out

@@ -1,0 +1,346 @@
+// C ABI of libpkv: argument validation, launch-shape choice, error reporting.
+// Every check runs before any launch, so a failing call leaves the device
+// untouched.  No allocation, no global state beyond the thread-local message.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pkv_status fail(pkv_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pkv_status ok() {
+  g_err[0] = '\0';
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(pkv_dtype t) {
+  switch (t) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3FN: return 1;
+  }
+  return 0;
+}
+
+bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3FN; }
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxPartition = 4096;
+
+// heads ratio check, shared by the attention calls
+pkv_status check_heads(int32_t n_q, int32_t n_kv) {
+  if (n_kv < 1 || n_q < 1) return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (n_q=%d, n_kv=%d)", n_q, n_kv);
+  if (n_q % n_kv != 0) return fail(PKV_ERR_INVALID_ARG, "query heads must be a multiple of KV heads (n_q=%d, n_kv=%d)", n_q, n_kv);
+  return PKV_OK;
+}
+
+// The library's partition size: split each sequence so that the grid holds
+// several thousand workgroups, never fewer tokens than one pass of the four
+// waves, never more than 1024 tokens (long sequences keep many partitions so
+// no single workgroup dominates the tail).
+int32_t choose_partition(int32_t batch, int32_t n_kv, int32_t head_chunks, int32_t max_tokens, int32_t quantum) {
+  const int64_t pairs = (int64_t)batch * n_kv * head_chunks;
+  int64_t want = ((int64_t)max_tokens * pairs + 8191) / 8192;
+  int64_t p = ((want + 255) / 256) * 256;
+  if (p < 256) p = 256;
+  if (p > 1024) p = 1024;
+  if (p % quantum) p = ((p + quantum - 1) / quantum) * quantum;
+  return (int32_t)p;
+}
+
+struct DecodePlan {
+  int32_t head_chunks;
+  int32_t part_tokens;
+  int32_t n_parts;
+  size_t ws_o_bytes;
+  size_t ws_bytes;
+};
+
+pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int32_t max_blocks, int32_t block_size,
+                       int32_t partition_tokens, DecodePlan* plan) {
+  pkv_status st = check_heads(n_q, n_kv);
+  if (st != PKV_OK) return st;
+  if (batch < 1 || max_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be positive");
+  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (d != 64 && d != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d unsupported (64 or 128)", d);
+  const int group = n_q / n_kv;
+  const int gw = pkv::decode_heads_per_wg(group);
+  const int quantum = 64 * pkv::decode_chunk_blocks(gw);
+  const int64_t max_tokens = (int64_t)max_blocks * block_size;
+  if (max_tokens > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  int32_t part = partition_tokens;
+  if (part == 0) {
+    part = choose_partition(batch, n_kv, group / gw, (int32_t)max_tokens, quantum);
+  } else if (part < 0 || part % 256 != 0 || part % quantum != 0 || part > kMaxPartition) {
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d must be a multiple of %d in (0, %d]", part,
+                quantum > 256 ? quantum : 256, kMaxPartition);
+  }
+  plan->head_chunks = group / gw;
+  plan->part_tokens = part;
+  plan->n_parts = (int32_t)((max_tokens + part - 1) / part);
+  if (plan->n_parts == 1) {
+    plan->ws_o_bytes = 0;
+    plan->ws_bytes = 0;
+  } else {
+    const size_t n = (size_t)batch * n_q * plan->n_parts;
+    plan->ws_o_bytes = ((n * d * sizeof(float)) + 255) & ~size_t(255);
+    plan->ws_bytes = plan->ws_o_bytes + n * 2 * sizeof(float);
+  }
+  return PKV_OK;
+}
+
+const float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+  }
+  return "PKV_ERR_UNKNOWN";
+}
+
+const char* pkv_last_error(void) { return g_err; }
+
+int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head, int32_t bytes_per_value) {
+  if (n_layers < 0 || n_kv_heads < 0 || d_head < 0 || bytes_per_value < 0) return -1;
+  return (int64_t)2 * n_layers * n_kv_heads * d_head * bytes_per_value;
+}
+
+pkv_status pkv_slot_mapping(const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                            const int32_t* seq_ids, const int32_t* positions, int32_t num_tokens,
+                            int32_t block_size, int64_t* slot_mapping_out, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (num_tokens == 0) return ok();
+  if (!block_table || !seq_ids || !positions || !slot_mapping_out) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (batch < 1 || max_blocks_per_seq < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "batch, max_blocks_per_seq and block_size must be positive");
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "table too wide");
+  return hip_status(pkv::launch_slot_mapping(block_table, batch, max_blocks_per_seq, seq_ids, positions, num_tokens,
+                                             block_size, slot_mapping_out, (hipStream_t)stream),
+                    "slot_mapping launch");
+}
+
+pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, int64_t num_blocks,
+                         const int64_t* slot_mapping, const void* k, const void* v, int32_t num_tokens,
+                         int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (!valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown cache dtype %d", (int)cache_dtype);
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !slot_mapping || !k || !v) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (num_blocks < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  const int row_bytes = d_head * elem_bytes(cache_dtype);
+  if (row_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "a row of %d bytes is not a multiple of 16", row_bytes);
+  return hip_status(pkv::launch_kv_append(k_cache, v_cache, num_blocks, slot_mapping, k, v, num_tokens, n_kv_heads,
+                                          row_bytes, block_size, (hipStream_t)stream),
+                    "kv_append launch");
+}
+
+pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                            int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, const int64_t* cu_seq_lens, int64_t total_tokens, int32_t batch,
+                            int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream) {
+  if (!valid_dtype(kv_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown cache dtype %d", (int)kv_dtype);
+  if (!k_out || !v_out || !k_cache || !v_cache || !block_table || !seq_lens || !cu_seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (batch < 1 || num_blocks < 1 || max_blocks_per_seq < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if (total_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "total_tokens must be >= 0");
+  if (total_tokens == 0) return ok();
+  if (max_blocks_per_seq > 65535 || batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  const int row_bytes = d_head * elem_bytes(kv_dtype);
+  if (row_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "a row of %d bytes is not a multiple of 16", row_bytes);
+  return hip_status(pkv::launch_gather(k_out, v_out, k_cache, v_cache, num_blocks, block_table, max_blocks_per_seq,
+                                       seq_lens, cu_seq_lens, total_tokens, batch, n_kv_heads, row_bytes, block_size,
+                                       (hipStream_t)stream),
+                    "gather launch");
+}
+
+pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
+                            void* stream) {
+  if (!block_table || !seq_lens || !error_count) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (batch < 1 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  return hip_status(pkv::launch_check_tables(block_table, max_blocks_per_seq, seq_lens, batch, num_blocks,
+                                             block_size, error_count, (hipStream_t)stream),
+                    "check_tables launch");
+}
+
+size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens) {
+  DecodePlan plan;
+  if (plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, partition_tokens, &plan) !=
+      PKV_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                             const float* k_scale, const float* v_scale,
+                                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                                             const int32_t* seq_lens, int32_t batch, int64_t num_blocks,
+                                             int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                             int32_t block_size, float scale, int32_t partition_tokens,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  // head ratio first, before anything else (validate before mutate)
+  pkv_status st = check_heads(n_q_heads, n_kv_heads);
+  if (st != PKV_OK) return st;
+  if (!out || !q || !k_cache || !v_cache || !block_table || !seq_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
+  if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
+  DecodePlan plan;
+  st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  const bool combo_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) || (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
+                        (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3FN);
+  if (!combo_ok) return fail(PKV_ERR_UNSUPPORTED, "(q, kv) dtype combination (%d, %d) unsupported", q_dtype, kv_dtype);
+  if (out_dtype == PKV_FP8_E4M3FN) return fail(PKV_ERR_UNSUPPORTED, "fp8 output unsupported");
+  if (kv_dtype == PKV_FP8_E4M3FN && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "fp8 caches need k_scale and v_scale");
+  const int group = n_q_heads / n_kv_heads;
+  const int gw = pkv::decode_heads_per_wg(group);
+  if (!pkv::decode_supported((int)kv_dtype, d_head, gw))
+    return fail(PKV_ERR_UNSUPPORTED, "f32 caches with d_head 128 need at least two query heads per KV head");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PKV_ERR_INVALID_ARG, "scale must be positive and finite");
+  if (batch > 65535 || n_kv_heads * plan.head_chunks > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (plan.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < plan.ws_bytes)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace) & 255) return fail(PKV_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  }
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.ws_o_bytes) : nullptr;
+  a.num_blocks = num_blocks;
+  a.batch = batch;
+  a.max_blocks = max_blocks_per_seq;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = group;
+  a.head_chunks = plan.head_chunks;
+  a.part_tokens = plan.part_tokens;
+  a.n_parts = plan.n_parts;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(pkv::launch_decode(a, (int)kv_dtype, d_head, (hipStream_t)stream), "decode launch");
+}
+
+pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                 const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                 const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                 int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                 int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return pkv_paged_attn_decode_partitioned(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale,
+                                           block_table, max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads,
+                                           n_kv_heads, d_head, block_size, scale, 0, workspace, workspace_bytes,
+                                           stream);
+}
+
+size_t pkv_paged_attn_prefill_workspace(int32_t num_seqs, int32_t max_q_len, int32_t n_q_heads, int32_t d_head) {
+  (void)num_seqs;
+  (void)max_q_len;
+  (void)n_q_heads;
+  (void)d_head;
+  return 0;
+}
+
+pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                        const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                        const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale,
+                                        int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)k_scale;
+  (void)v_scale;
+  (void)workspace;
+  (void)workspace_bytes;
+  pkv_status st = check_heads(n_q_heads, n_kv_heads);
+  if (st != PKV_OK) return st;
+  if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
+  if (num_seqs < 1 || total_q < 0 || max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "bad sequence counts");
+  if (total_q == 0 || max_q_len == 0) return ok();
+  if (!out || !q || !cu_q_lens || !context_lens || !k_cache || !v_cache || !block_table)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (num_blocks < 1 || max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
+  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "prefill supports d_head 128 only");
+  if (q_dtype != PKV_BF16 || kv_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 q and KV");
+  if (out_dtype == PKV_FP8_E4M3FN) return fail(PKV_ERR_UNSUPPORTED, "fp8 output unsupported");
+  const int group = n_q_heads / n_kv_heads;
+  if (!pkv::prefill_supported_group(group))
+    return fail(PKV_ERR_UNSUPPORTED, "prefill needs n_q / n_kv to divide 128 (got %d)", group);
+  if (causal != 0 && causal != 1) return fail(PKV_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PKV_ERR_INVALID_ARG, "scale must be positive and finite");
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "table too wide");
+  if (num_seqs > 65535 || n_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.cu_q = cu_q_lens;
+  a.ctx_lens = context_lens;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_table = block_table;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.max_q_len = max_q_len;
+  a.max_blocks = max_blocks_per_seq;
+  a.n_q = n_q_heads;
+  a.n_kv = n_kv_heads;
+  a.group = group;
+  a.causal = causal;
+  a.out_bf16 = out_dtype == PKV_BF16;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device helpers for the gfx950 (CDNA4) paged-attention kernels: 16-byte
+// vector types, bf16 / OCP-E4M3FN conversions, and wave64 lane-group
+// reductions built from DPP row operations.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// cache element kinds (mirror the C-ABI dtype codes)
+enum Kind : int { KIND_F32 = 0, KIND_BF16 = 1, KIND_FP8 = 2 };
+
+template <int K> struct KindBytes;
+template <> struct KindBytes<KIND_F32> { static constexpr int v = 4; };
+template <> struct KindBytes<KIND_BF16> { static constexpr int v = 2; };
+template <> struct KindBytes<KIND_FP8> { static constexpr int v = 1; };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// low / high bf16 of a packed dword, widened to f32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// f32 pair -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// bf16 rounding of one value, returned widened to f32
+__device__ __forceinline__ float round_bf16(float x) { return __bf16(x); }
+
+// interleave the low halves / high halves of two packed bf16 dwords:
+// lo_pair = (a.lo, b.lo), hi_pair = (a.hi, b.hi)
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// dot of two bf16 pairs accumulated in f32 (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// four OCP E4M3FN bytes -> two packed bf16 dwords (exact: every E4M3FN value
+// is a bf16 value).  gfx950 converts the OCP encoding in hardware.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  lo = pack_bf16(a[0], a[1]);
+  hi = pack_bf16(b[0], b[1]);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// --- lane-group reductions over G consecutive lanes (G a power of two) ---
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int G>
+__device__ __forceinline__ float group_max(float x) {
+  if constexpr (G >= 2) x = fmaxf(x, dpp_f<DPP_QUAD_XOR1>(x));
+  if constexpr (G >= 4) x = fmaxf(x, dpp_f<DPP_QUAD_XOR2>(x));
+  if constexpr (G >= 8) x = fmaxf(x, dpp_f<DPP_ROW_HALF_MIRROR>(x));
+  if constexpr (G >= 16) x = fmaxf(x, dpp_f<DPP_ROW_MIRROR>(x));
+  if constexpr (G >= 32) x = fmaxf(x, __shfl_xor(x, 16));
+  if constexpr (G >= 64) x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (G >= 2) x += dpp_f<DPP_QUAD_XOR1>(x);
+  if constexpr (G >= 4) x += dpp_f<DPP_QUAD_XOR2>(x);
+  if constexpr (G >= 8) x += dpp_f<DPP_ROW_HALF_MIRROR>(x);
+  if constexpr (G >= 16) x += dpp_f<DPP_ROW_MIRROR>(x);
+  if constexpr (G >= 32) x += __shfl_xor(x, 16);
+  if constexpr (G >= 64) x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Order LDS traffic between lanes of one wave: LDS instructions of a wave
+// execute in order, so a compiler-level barrier with wavefront-scope fences is
+// enough for one lane to read what another lane of the same wave wrote.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace pkv

@@ -1,0 +1,75 @@
+// Host-side launch interfaces shared by the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* ws_o;    // [batch][n_q][n_parts][d] partial outputs (unnormalised)
+  float* ws_ml;   // [batch][n_q][n_parts][2] running max (log2 units) and sum
+  int64_t num_blocks;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t group;        // n_q / n_kv
+  int32_t head_chunks;  // group / heads per workgroup
+  int32_t part_tokens;
+  int32_t n_parts;
+  int32_t out_bf16;
+  float scale_log2;     // softmax scale * log2(e)
+};
+
+// decode: kv_kind 0 f32 / 1 bf16 / 2 fp8; returns hipSuccess or the launch error
+int decode_heads_per_wg(int group);
+int decode_chunk_blocks(int heads_per_wg);
+bool decode_supported(int kv_kind, int d, int heads_per_wg);
+hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
+                               const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,
+                               hipStream_t stream);
+hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_blocks, const int64_t* slots, const void* k,
+                            const void* v, int32_t n, int32_t n_kv, int32_t row_bytes, int32_t block_size,
+                            hipStream_t stream);
+hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                         const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, const int64_t* cu,
+                         int64_t total_rows, int32_t batch, int32_t n_kv, int32_t row_bytes, int32_t block_size,
+                         hipStream_t stream);
+hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
+                               int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const int32_t* cu_q;
+  const int32_t* ctx_lens;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_table;
+  int64_t num_blocks;
+  int32_t num_seqs;
+  int32_t total_q;
+  int32_t max_q_len;
+  int32_t max_blocks;
+  int32_t n_q;
+  int32_t n_kv;
+  int32_t group;
+  int32_t causal;
+  int32_t out_bf16;
+  float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream);
+bool prefill_supported_group(int group);
+
+}  // namespace pkv

@@ -1,0 +1,269 @@
+// Chunked-prefill attention over a paged KV cache on gfx950 bf16 MFMA.
+//
+// Method ("KV cache, PagedAttention and FlashAttention", Problem 5: tiles of
+// Q, K, V in on-chip memory, online softmax with running max and sum, one
+// fused kernel; "Memory Management in LLM Serving Systems", FlashAttention:
+// masked positions are -inf and fully masked blocks are skipped, GQA lets the
+// query heads of a group share each K/V tile; FlashAttention-2: Q is split
+// across waves while every wave sees the whole K/V tile, and the division by
+// the row sum waits until the end).
+//
+// Work decomposition
+//   grid = (query tiles, KV heads, sequences), 256 threads = 4 waves.
+//   A workgroup owns 128 packed query rows of one sequence and one KV head:
+//   row r = (token r / G, head r % G), so the G heads that share the KV head
+//   reuse every K/V tile.  Each wave owns 32 rows (two 16-row MFMA tiles).
+//   Per 64-key tile (four 16-token cache blocks looked up in the table):
+//     K and V slabs -> LDS (16-byte loads, issued one tile ahead);
+//     S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K from LDS, Q in registers),
+//     so each lane holds four keys of one query row;
+//     causal mask only on tiles that cross the diagonal; online softmax per
+//     row (in-lane max over 16 keys + two cross-lane steps);
+//     P^T (bf16) is already in the B-operand layout of the next product, so
+//     O^T += V^T P^T uses V^T fragments read with ds_read_b64_tr_b16.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int BS = 16;          // tokens per cache block
+constexpr int KT = 64;          // keys per tile
+constexpr int ROWS = 128;       // packed query rows per workgroup
+constexpr int NT = 2;           // 16-row MFMA tiles per wave
+constexpr int KROW = D * 2 + 16;  // padded bf16 K row in LDS (A-operand reads)
+constexpr int VROW = D * 2 + 32;  // padded bf16 V row in LDS (transposing reads)
+constexpr int K_LDS = KT * KROW;
+constexpr int V_LDS = KT * VROW;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x2 ds_read_tr(const char* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  __shared__ __align__(16) char smem[K_LDS + V_LDS];
+  char* const k_lds = smem;
+  char* const v_lds = smem + K_LDS;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int s = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int G = a.group;
+  const int tq = ROWS / G;              // tokens per workgroup
+  const int q0 = blockIdx.x * tq;       // first chunk token of the tile
+  // a packed-query range outside [0, total_q) is clipped so no access leaves q or out
+  const int qs = min(max(a.cu_q[s], 0), a.total_q);
+  const int q_len = min(a.cu_q[s + 1], a.total_q) - qs;
+  if (q0 >= q_len) return;
+  const int ctx = min(max(a.ctx_lens[s], 0), a.max_blocks * BS);  // keeps every tile inside the table
+  const int total = ctx + q_len;        // keys that exist for this sequence
+  const int last_q = min(q0 + tq, q_len) - 1;
+  const int kv_end = a.causal ? ctx + last_q + 1 : total;  // keys any row of the tile sees
+  const int n_tiles = (kv_end + KT - 1) / KT;
+  const int diag0 = ctx + q0;           // keys >= diag0 are masked for some row
+
+  const int n = lane & 15;   // column (query row within a 16-row tile)
+  const int g = lane >> 4;   // lane group
+
+  // ---- Q^T fragments (B operand): row = (w*NT + nt)*16 + n, d = 32*ds + 8g + e
+  u32x4 qf[NT][4];
+  int row_tok[NT], row_head[NT], row_lim[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = (w * NT + nt) * 16 + n;
+    const int tok = q0 + r / G;
+    row_tok[nt] = tok;
+    row_head[nt] = kvh * G + r % G;
+    row_lim[nt] = a.causal ? ctx + tok : total - 1;  // last visible key
+    const bool ok = tok < q_len;
+    const char* qrow = reinterpret_cast<const char*>(a.q) +
+                       ((int64_t)(qs + (ok ? tok : 0)) * a.n_q + row_head[nt]) * D * 2;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      const u32x4 v = ld16(qrow + (32 * ds + 8 * g) * 2);
+      qf[nt][ds] = ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  f32x4 o[8][NT];  // O^T[16*dt + 4g + j][row n]
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[dt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NT], l_run[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
+
+  // ---- tile loads: 256 threads x 4 pieces of 16 B for each of K and V
+  const char* const kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* const vc = reinterpret_cast<const char*>(a.v_cache);
+  const int32_t* trow = a.block_table + (int64_t)s * a.max_blocks;
+  u32x4 kreg[4], vreg[4];
+  auto issue = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + 256 * i;         // piece index in the tile
+      const int b = p >> 8;                // block within the tile
+      const int lb = kt * (KT / BS) + b;   // logical block
+      int id = 0;
+      if (lb < a.max_blocks) id = trow[lb];
+      id = min(max(id, 0), (int)(a.num_blocks - 1));
+      const int64_t off = ((int64_t)id * a.n_kv + kvh) * (BS * D * 2) + (p & 255) * 16;
+      kreg[i] = ld16(kc + off);
+      vreg[i] = ld16(vc + off);
+    }
+  };
+  if (n_tiles > 0) issue(0);
+
+  const float sl = a.scale_log2;
+  for (int kt = 0; kt < n_tiles; ++kt) {
+    __syncthreads();  // the previous tile's LDS reads are done
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + 256 * i;
+      const int row = p >> 4;              // key row within the tile
+      const int col = (p & 15) * 16;       // byte column
+      u32x4 kv = kreg[i], vv = vreg[i];
+      if (kt * KT + row >= total) {        // slots past the sequence may hold anything
+        kv = u32x4{0, 0, 0, 0};
+        vv = u32x4{0, 0, 0, 0};
+      }
+      st16(k_lds + row * KROW + col, kv);
+      st16(v_lds + row * VROW + col, vv);
+    }
+    __syncthreads();
+    if (kt + 1 < n_tiles) issue(kt + 1);
+
+    // ---- S^T = K Q^T : four 16-key tiles x NT row tiles
+    f32x4 st_[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st_[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const u32x4 kf = ld16(k_lds + (16 * t + n) * KROW + (32 * ds + 8 * g) * 2);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf, qf[nt][ds], st_[t][nt]);
+      }
+    }
+
+    // ---- mask, online softmax, P^T fragments
+    const bool need_mask = (a.causal && kt * KT + KT - 1 > diag0) || (kt * KT + KT > total);
+    u32x4 pf[2][NT];  // B operand per 32-key step
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = st_[t][nt][j] * sl;
+          if (need_mask) {
+            const int key = kt * KT + 16 * t + 4 * g + j;
+            v = (key <= row_lim[nt]) ? v : -INFINITY;
+          }
+          st_[t][nt][j] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[nt], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2_fast(m_run[nt] - m_use);
+      m_run[nt] = m_new;
+      float ls = 0.f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float p4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          p4[j] = round_bf16(exp2_fast(st_[t][nt][j] - m_use));
+          ls += p4[j];
+        }
+        pk[t][0] = pack_bf16(p4[0], p4[1]);
+        pk[t][1] = pack_bf16(p4[2], p4[3]);
+      }
+      l_run[nt] = l_run[nt] * alpha + ls;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) pf[ks][nt] = u32x4{pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int jj = (lane >> 2) & 3;  // which of the four keys this lane's read supplies
+      const int qq = lane & 3;         // which 4-column group
+      const int key_a = 32 * ks + 4 * g + jj;
+      const int key_b = key_a + 16;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const u32x2 lo = ds_read_tr(v_lds + key_a * VROW + (16 * dt + 4 * qq) * 2);
+        const u32x2 hi = ds_read_tr(v_lds + key_b * VROW + (16 * dt + 4 * qq) * 2);
+        const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma_bf16(vf, pf[ks][nt], o[dt][nt]);
+      }
+    }
+  }
+
+  // ---- normalise and store: lane (n, g) holds d = 16*dt + 4g + j of row n
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    float l = l_run[nt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (row_tok[nt] >= q_len) continue;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t obase = ((int64_t)(qs + row_tok[nt]) * a.n_q + row_head[nt]) * D;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d0 = 16 * dt + 4 * g;
+      const f32x4 v = o[dt][nt] * inv;
+      if (a.out_bf16) {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<__bf16*>(a.out) + obase + d0) =
+            u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+      } else {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + obase + d0) = v;
+      }
+    }
+  }
+}
+
+bool prefill_supported_group(int group) {
+  return group >= 1 && group <= ROWS && (ROWS % group) == 0;
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream) {
+  (void)d;
+  const int tq = ROWS / a.group;
+  dim3 grid((a.max_q_len + tq - 1) / tq, a.n_kv, a.num_seqs);
+  if (grid.x == 0) return hipSuccess;
+  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

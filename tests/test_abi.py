@@ -1,0 +1,121 @@
+"""The C-ABI library: it loads, exports every symbol include/pkv.h declares,
+and rejects bad arguments on the host before any launch.  No GPU needed: every
+call here fails validation (or is host-only arithmetic)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_blocks_amd", "libpkv.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libpkv.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_blocks_amd as p
+    return p
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_binding_signatures_cover_the_header(pkv):
+    assert set(pkv._SIGS) == set(_declared())
+
+
+def test_version_and_status_strings(pkv):
+    hdr = open(HEADER).read()
+    assert pkv.abi_version() == int(re.search(r"#define PKV_ABI_VERSION (\d+)", hdr).group(1))
+    lib = pkv.load()
+    names = [lib.pkv_status_string(i).decode() for i in range(5)]
+    assert names == ["PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP"]
+
+
+def test_bytes_per_token_formula(pkv):
+    # 128 KiB (Llama3-8B shape, fp16) and 320 KiB (70B shape, bf16) per token
+    assert pkv.kv_bytes_per_token(32, 8, 128, 2) == 128 * 1024
+    assert pkv.kv_bytes_per_token(80, 8, 128, 2) == 320 * 1024
+    assert pkv.kv_bytes_per_token(80, 8, 128, 1) == 160 * 1024
+    assert pkv.kv_bytes_per_token(-1, 8, 128, 2) == -1
+
+
+def _decode(lib, **kw):
+    a = dict(out=0x1000, out_dtype=0, q=0x1000, q_dtype=1, k=0x1000, v=0x1000, kv_dtype=1, ks=None, vs=None,
+             table=0x1000, max_blocks=8, seq_lens=0x1000, batch=2, num_blocks=16, n_q=8, n_kv=2, d=128, bs=16,
+             scale=0.088, part=0, ws=None, ws_n=0, stream=None)
+    a.update(kw)
+    return lib.pkv_paged_attn_decode_partitioned(a["out"], a["out_dtype"], a["q"], a["q_dtype"], a["k"], a["v"],
+                                                 a["kv_dtype"], a["ks"], a["vs"], a["table"], a["max_blocks"],
+                                                 a["seq_lens"], a["batch"], a["num_blocks"], a["n_q"], a["n_kv"],
+                                                 a["d"], a["bs"], a["scale"], a["part"], a["ws"], a["ws_n"],
+                                                 a["stream"])
+
+
+def test_decode_validation_before_launch(pkv):
+    lib = pkv.load()
+    # the head ratio is checked first ("validate before mutate")
+    assert _decode(lib, n_q=6, n_kv=4, out=None) == pkv.ERR_INVALID_ARG
+    assert b"multiple of KV heads" in lib.pkv_last_error()
+    assert _decode(lib, n_kv=0) == pkv.ERR_INVALID_ARG
+    assert _decode(lib, q=None) == pkv.ERR_INVALID_ARG
+    assert _decode(lib, d=96) == pkv.ERR_UNSUPPORTED
+    assert _decode(lib, bs=32) == pkv.ERR_UNSUPPORTED
+    assert _decode(lib, q_dtype=0) == pkv.ERR_UNSUPPORTED          # f32 q with bf16 KV
+    assert _decode(lib, kv_dtype=2) == pkv.ERR_INVALID_ARG         # fp8 without scales
+    assert _decode(lib, kv_dtype=0, q_dtype=0, n_q=2, n_kv=2) == pkv.ERR_UNSUPPORTED  # f32, d128, one head per KV head
+    assert _decode(lib, scale=0.0) == pkv.ERR_INVALID_ARG
+    assert _decode(lib, part=100) == pkv.ERR_INVALID_ARG
+    # 8 blocks * 16 = 128 tokens -> a single partition, no workspace; 4096-token tables need one
+    need = pkv.paged_attn_decode_workspace(2, 8, 2, 128, 256, 16, 256)
+    assert need > 0
+    assert _decode(lib, max_blocks=256, part=256, ws=0x1000, ws_n=need - 1) == pkv.ERR_WORKSPACE
+    assert _decode(lib, max_blocks=256, part=256, ws=0x1001, ws_n=need) == pkv.ERR_INVALID_ARG  # misaligned
+
+
+def test_decode_workspace_sizes(pkv):
+    # one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
+    assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 7, 16, 0) == 0
+    n = 64 * 32 * 8
+    assert pkv.paged_attn_decode_workspace(64, 32, 8, 128, 128, 16, 256) == ((n * 128 * 4 + 255) // 256) * 256 + n * 8
+    assert pkv.paged_attn_decode_workspace(2, 6, 4, 64, 7, 16, 0) == 0  # invalid -> 0
+
+
+def test_other_entry_points_validate(pkv):
+    lib = pkv.load()
+    assert lib.pkv_slot_mapping(None, 1, 1, None, None, 0, 16, None, None) == pkv.OK  # empty is a no-op
+    assert lib.pkv_slot_mapping(None, 1, 1, 0x1000, 0x1000, 4, 16, 0x1000, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_kv_append(None, None, 1, 1, None, None, None, 0, 8, 128, 16, None) == pkv.OK
+    assert lib.pkv_kv_append(0x1000, 0x1000, 7, 1, 0x1000, 0x1000, 0x1000, 1, 8, 128, 16, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_kv_append(0x1000, 0x1000, 2, 1, 0x1000, 0x1000, 0x1000, 1, 8, 8, 16, None) == pkv.ERR_UNSUPPORTED
+    assert lib.pkv_paged_gather(0x1000, 0x1000, 0x1000, 0x1000, 1, 4, 0x1000, 2, 0x1000, 0x1000, 0, 1, 2, 64, 16,
+                                None) == pkv.OK
+    assert lib.pkv_check_tables(None, 1, None, 1, 1, 16, None, None) == pkv.ERR_INVALID_ARG
+    pf = lib.pkv_paged_attn_prefill_chunk
+    base = [0x1000, 0, 0x1000, 1, 0x1000, 0x1000, 2, 64, 32, 0x1000, 0x1000, 1, None, None, 0x1000, 8, 32, 32, 8, 128,
+            16, 0.088, 1, None, 0, None]
+    args = list(base); args[18] = 5
+    assert pf(*args) == pkv.ERR_INVALID_ARG          # 32 / 5
+    args = list(base); args[19] = 64
+    assert pf(*args) == pkv.ERR_UNSUPPORTED          # d 64
+    args = list(base); args[11] = 2
+    assert pf(*args) == pkv.ERR_UNSUPPORTED          # fp8 KV
+    args = list(base); args[22] = 3
+    assert pf(*args) == pkv.ERR_INVALID_ARG          # causal flag
+    args = list(base); args[7] = 0
+    assert pf(*args) == pkv.OK                       # no queries: no-op
+    assert pkv.load().pkv_paged_attn_prefill_workspace(16, 512, 32, 128) == 0

@@ -1,0 +1,88 @@
+"""GPU parity of chunked prefill (MFMA path) and append-then-attend."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import dev, err_report, host_bits, note
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_blocks_amd as p
+    assert torch.cuda.is_available()
+    return p
+
+
+def _run(pkv, p, causal=True, k_cache=None, v_cache=None, out_dtype=torch.float32):
+    kc = dev(p.k_cache, "bf16") if k_cache is None else k_cache
+    vc = dev(p.v_cache, "bf16") if v_cache is None else v_cache
+    q_lens = np.diff(p.cu_q_lens)
+    out = pkv.paged_attn_prefill_chunk(dev(p.q, "bf16"), dev(p.cu_q_lens), dev(p.context_lens), int(q_lens.max()),
+                                       kc, vc, dev(p.block_table), p.n_q, p.n_kv, p.d, 16, p.scale, causal=causal,
+                                       out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+def _oracle(p, causal=True):
+    return oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, p.k_cache, p.v_cache, "bf16", None, None,
+                                p.block_table, p.n_q, p.n_kv, p.scale, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 2), (8, 1)])
+def test_prefill_ragged(pkv, causal, n_q, n_kv):
+    ctx = [0, 5, 16, 37, 300, 1000]
+    ql = [7, 1, 33, 128, 200, 65]
+    p = synth.make_prefill_case(config=400, layer=n_q + n_kv, n_q=n_q, n_kv=n_kv, d=128, context_lens=ctx, q_len=ql)
+    note(f"prefill n_q={n_q} n_kv={n_kv} causal={causal}")
+    got = _run(pkv, p, causal)
+    want = _oracle(p, causal)
+    rep = err_report(got, want)
+    note("  " + rep)
+    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= 1e-2, rep
+
+
+def test_prefill_chunk_of_one_matches_decode(pkv):
+    p = synth.make_prefill_case(config=401, layer=0, n_q=32, n_kv=8, d=128, context_lens=[37, 500, 0], q_len=1)
+    got = _run(pkv, p)
+    dec = pkv.paged_attn_decode(dev(p.q, "bf16"), dev(p.k_cache, "bf16"), dev(p.v_cache, "bf16"), dev(p.block_table),
+                                dev(p.context_lens + 1), p.n_q, p.n_kv, p.d, 16, p.scale)
+    torch.cuda.synchronize()
+    want = _oracle(p)
+    d = dec.float().cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - want)) <= 1e-2 and np.max(np.abs(d - want)) <= 1e-2
+    assert np.max(np.abs(got - d)) <= 1e-2
+
+
+def test_append_then_attend(pkv):
+    """kv_append writes the chunk's rows (bit-exact), then prefill attends them."""
+    p = synth.make_prefill_case(config=402, layer=0, n_q=32, n_kv=8, d=128, context_lens=[0, 100, 1234],
+                                q_len=[64, 100, 512], chunk_in_cache=False)
+    full = synth.make_prefill_case(config=402, layer=0, n_q=32, n_kv=8, d=128, context_lens=[0, 100, 1234],
+                                   q_len=[64, 100, 512], chunk_in_cache=True)
+    kc, vc = dev(p.k_cache, "bf16"), dev(p.v_cache, "bf16")
+    tb = dev(p.block_table)
+    note("append then attend")
+    slots = pkv.slot_mapping(tb, dev(p.seq_ids), dev(p.positions), 16)
+    pkv.kv_append(kc, vc, slots, dev(p.k_new, "bf16"), dev(p.v_new, "bf16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(kc), full.k_cache) and np.array_equal(host_bits(vc), full.v_cache)
+    got = _run(pkv, p, k_cache=kc, v_cache=vc)
+    want = _oracle(full)
+    rep = err_report(got, want)
+    note("  " + rep)
+    assert np.max(np.abs(got - want)) <= 1e-2, rep
+
+
+def test_prefill_bf16_output(pkv):
+    p = synth.make_prefill_case(config=403, layer=0, n_q=32, n_kv=8, d=128, context_lens=[10, 70], q_len=[50, 3])
+    want = _oracle(p)
+    got = _run(pkv, p, out_dtype=torch.bfloat16)
+    assert np.max(np.abs(got - want)) <= 1e-2 + 2 ** -8 * np.max(np.abs(want))
