@@ -1,0 +1,420 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c1|c5]
+
+A step is one pass of the whole hot path over one batch, on inputs already
+resident in HBM:
+  * decode workloads (c1-c4): slot indexing for the batch's current token,
+    then for every layer kv_append of that token's K/V rows followed by paged
+    decode attention (split-K partitions + combine);
+  * prefill workload (c5): slot indexing of the chunk, kv_append of its 8,192
+    new rows, chunked-prefill attention.
+The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
+8 KV heads, d 128, lengths uniform in [1024, 2048], 32 layers, bf16 KV).
+
+Prints one JSON line.  `value` is achieved GB/s (algorithmic bytes / wall
+time of the K timed steps); `roofline` describes the decode call (split-K
+kernel + combine) timed with HIP events on the launch stream; `cpu_baseline`
+times the float64 CPU oracle on a bounded sample of the same workload on the
+host cores and checks the sampled GPU outputs against it.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) and tokens/s per layer"
+
+WORKLOADS = {
+    "c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5,
+}
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes / flops
+# ---------------------------------------------------------------------------
+
+def decode_layer_bytes(seq_lens, n_q, n_kv, d, kv_bytes, q_bytes, out_bytes, fp8):
+    """Every cached K/V byte read once, plus q, output, scales, table and lengths."""
+    L = np.asarray(seq_lens, dtype=np.int64)
+    blocks = (L + 15) // 16
+    b = int((L * n_kv * 2 * d * kv_bytes).sum())
+    if fp8:
+        b += int((blocks * n_kv * 2 * 4).sum())
+    b += len(L) * n_q * d * (q_bytes + out_bytes)
+    b += int(blocks.sum()) * 4 + 4 * len(L)
+    return b
+
+
+def append_bytes(tokens, n_kv, d, kv_bytes):
+    """Read the new K/V rows and their slots, write them into the pool."""
+    return tokens * (n_kv * d * kv_bytes * 2 * 2 + 8)
+
+
+def slot_bytes(tokens, max_blocks):
+    return tokens * (4 + 4 + 4 + 8)
+
+
+def prefill_flops(ctx_lens, q_len, n_q, d):
+    """4 d n_q per unmasked (query, key) pair; query i of a chunk sees ctx + i + 1 keys."""
+    tot = 0
+    for c in ctx_lens:
+        tot += sum(int(c) + i + 1 for i in range(q_len))
+    return 4 * d * n_q * tot
+
+
+# ---------------------------------------------------------------------------
+# workloads on the device
+# ---------------------------------------------------------------------------
+
+class DecodeWorkload:
+    def __init__(self, cfg_id: int, layers: int = None):
+        import torch
+        import paged_kv_cache_blocks_amd as pkv
+        self.pkv, self.torch = pkv, torch
+        c = synth.CONFIGS[cfg_id]
+        self.cfg_id = cfg_id
+        self.name = c["name"]
+        self.n_q, self.n_kv, self.d, self.kind = c["n_q"], c["n_kv"], c["d"], c["kv_dtype"]
+        self.layers = layers or c["layers"]
+        self.seq_lens = synth.config_seq_lens(cfg_id)
+        self.batch = len(self.seq_lens)
+        dev = torch.device("cuda")
+        need = sum(synth.blocks_for(L) for L in self.seq_lens)
+        self.num_blocks = 64 if cfg_id == 1 else need
+        perm = synth.rng(cfg_id, 0, synth.T_PERM).permutation(self.num_blocks).astype(np.int32)
+        table, filled = synth.build_tables(self.seq_lens, self.num_blocks, perm)
+        self.block_table_np = table
+        self.block_table = torch.from_numpy(table).to(dev)
+        self.seq_lens_t = torch.from_numpy(self.seq_lens).to(dev)
+        self.max_blocks = table.shape[1]
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[self.kind]
+        qdt = torch.float32 if self.kind == "f32" else torch.bfloat16
+        shape = (self.num_blocks, self.n_kv, 16, self.d)
+        filled_t = torch.from_numpy(filled).to(dev)[:, None, :, None]
+        self.k, self.v, self.ks, self.vs, self.q, self.k_new, self.v_new = [], [], [], [], [], [], []
+        for layer in range(self.layers):
+            seed = (cfg_id * 1000 + layer) * 8
+            kv = []
+            sc = []
+            for j in range(2):
+                x = torch.empty(shape, dtype=torch.float32, device=dev)
+                synth.device_normal_(x, seed + 1 + j)
+                if self.kind == "fp8":
+                    amax = torch.where(filled_t, x.abs(), torch.zeros((), device=dev)).amax(dim=(2, 3))
+                    s = torch.where(amax > 0, amax / 448.0, torch.ones((), device=dev)).float()
+                    codes = (x / s[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+                    codes = torch.where(filled_t, codes, torch.full((), 0x7F, dtype=torch.uint8, device=dev))
+                    kv.append(codes.contiguous())
+                    sc.append(s.contiguous())
+                else:
+                    y = x.to(tdt)
+                    nan = torch.full((), float("nan"), dtype=tdt, device=dev)
+                    kv.append(torch.where(filled_t, y, nan).contiguous())
+                del x
+            self.k.append(kv[0])
+            self.v.append(kv[1])
+            self.ks.append(sc[0] if sc else None)
+            self.vs.append(sc[1] if sc else None)
+            qf = torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
+            synth.device_normal_(qf, seed + 3)
+            self.q.append(qf.to(qdt).contiguous())
+            # the step's new token rows: the rows already at each sequence's last slot
+            last = torch.from_numpy(self.seq_lens - 1).to(dev).long()
+            blk = self.block_table[torch.arange(self.batch, device=dev), last // 16].long()
+            self.k_new.append(kv[0][blk, :, last % 16, :].contiguous())
+            self.v_new.append(kv[1][blk, :, last % 16, :].contiguous())
+        self.seq_ids = torch.arange(self.batch, dtype=torch.int32, device=dev)
+        self.positions = (self.seq_lens_t - 1).to(torch.int32)
+        self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
+        self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
+                    for _ in range(self.layers)]
+        ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.scale = synth.softmax_scale(self.d)
+        torch.cuda.synchronize()
+        kvb = synth.ELEM_BYTES[self.kind]
+        qb = 4 if self.kind == "f32" else 2
+        self.layer_bytes = decode_layer_bytes(self.seq_lens, self.n_q, self.n_kv, self.d, kvb, qb, 4,
+                                              self.kind == "fp8")
+        self.step_bytes = (slot_bytes(self.batch, self.max_blocks) +
+                           self.layers * (self.layer_bytes + append_bytes(self.batch, self.n_kv, self.d, kvb)))
+
+    def decode_call(self, layer):
+        self.pkv.paged_attn_decode(self.q[layer], self.k[layer], self.v[layer], self.block_table, self.seq_lens_t,
+                                   self.n_q, self.n_kv, self.d, 16, self.scale, k_scale=self.ks[layer],
+                                   v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws)
+
+    def step(self, events=None):
+        pkv = self.pkv
+        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
+        for layer in range(self.layers):
+            pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
+            if events is not None:
+                events[layer][0].record()
+            self.decode_call(layer)
+            if events is not None:
+                events[layer][1].record()
+
+    def describe(self):
+        return {"workload": self.name, "batch": self.batch, "n_q_heads": self.n_q, "n_kv_heads": self.n_kv,
+                "d_head": self.d, "block_size": 16, "layers": self.layers, "kv_dtype": self.kind,
+                "mean_seq_len": float(np.mean(self.seq_lens)), "max_blocks_per_seq": int(self.max_blocks),
+                "num_blocks_per_layer": int(self.num_blocks)}
+
+
+class PrefillWorkload:
+    def __init__(self, cfg_id: int = 5):
+        import torch
+        import paged_kv_cache_blocks_amd as pkv
+        self.pkv, self.torch = pkv, torch
+        c = synth.CONFIGS[cfg_id]
+        self.name = c["name"]
+        self.n_q, self.n_kv, self.d = c["n_q"], c["n_kv"], c["d"]
+        self.layers = 1
+        self.ctx = synth.config_seq_lens(cfg_id)
+        self.q_len = 512
+        dev = torch.device("cuda")
+        total = self.ctx + self.q_len
+        self.num_blocks = sum(synth.blocks_for(L) for L in total)
+        perm = synth.rng(cfg_id, 0, synth.T_PERM).permutation(self.num_blocks).astype(np.int32)
+        table, _ = synth.build_tables(total, self.num_blocks, perm)
+        self.block_table = torch.from_numpy(table).to(dev)
+        shape = (self.num_blocks, self.n_kv, 16, self.d)
+        self.k = synth.device_normal_(torch.empty(shape, device=dev), 5001).to(torch.bfloat16)
+        self.v = synth.device_normal_(torch.empty(shape, device=dev), 5002).to(torch.bfloat16)
+        nq = len(self.ctx) * self.q_len
+        self.q = synth.device_normal_(torch.empty((nq, self.n_q, self.d), device=dev), 5003).to(torch.bfloat16)
+        self.seq_ids = torch.repeat_interleave(torch.arange(len(self.ctx), dtype=torch.int32), self.q_len).to(dev)
+        self.positions = torch.cat([torch.arange(int(cx), int(cx) + self.q_len, dtype=torch.int32)
+                                    for cx in self.ctx]).to(dev)
+        self.k_new = synth.device_normal_(torch.empty((nq, self.n_kv, self.d), device=dev), 5004).to(torch.bfloat16)
+        self.v_new = synth.device_normal_(torch.empty((nq, self.n_kv, self.d), device=dev), 5005).to(torch.bfloat16)
+        self.cu = torch.arange(0, nq + 1, self.q_len, dtype=torch.int32, device=dev)
+        self.ctx_t = torch.from_numpy(self.ctx).to(dev)
+        self.slots = torch.empty(nq, dtype=torch.int64, device=dev)
+        self.out = torch.empty((nq, self.n_q, self.d), dtype=torch.float32, device=dev)
+        self.scale = synth.softmax_scale(self.d)
+        self.flops = prefill_flops(self.ctx, self.q_len, self.n_q, self.d)
+        torch.cuda.synchronize()
+
+    def attn_call(self):
+        self.pkv.paged_attn_prefill_chunk(self.q, self.cu, self.ctx_t, self.q_len, self.k, self.v, self.block_table,
+                                          self.n_q, self.n_kv, self.d, 16, self.scale, out=self.out)
+
+    def step(self, events=None):
+        pkv = self.pkv
+        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
+        pkv.kv_append(self.k, self.v, self.slots, self.k_new, self.v_new)
+        if events is not None:
+            events[0][0].record()
+        self.attn_call()
+        if events is not None:
+            events[0][1].record()
+
+    def describe(self):
+        return {"workload": self.name, "num_seqs": len(self.ctx), "q_len": self.q_len, "n_q_heads": self.n_q,
+                "n_kv_heads": self.n_kv, "d_head": self.d, "block_size": 16, "mean_ctx": float(np.mean(self.ctx))}
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample of the same workload)
+# ---------------------------------------------------------------------------
+
+_CPU = {}
+
+
+def _oracle_task(args):
+    layer, s = args
+    import oracle
+    from threadpoolctl import threadpool_limits
+    w = _CPU
+    with threadpool_limits(limits=1):
+        o = oracle.decode_one(w["q"][layer], w["q_dtype"], w["k"][layer], w["v"][layer], w["kind"],
+                              w["ks"][layer], w["vs"][layer], w["table"], w["lens"], w["n_q"], w["n_kv"],
+                              w["scale"], s)
+    return layer, s, o
+
+
+def cpu_baseline(w: DecodeWorkload, sample_layers: int):
+    """Time the oracle over `sample_layers` layers x all sequences on a process
+    pool; return the baseline record and the max-abs error of the GPU outputs
+    on that sample."""
+    import multiprocessing as mp
+    import torch
+
+    def host(t):
+        if t is None:
+            return None
+        t = t.cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    n = min(sample_layers, w.layers)
+    _CPU.clear()
+    _CPU.update(dict(q=[host(w.q[i]) for i in range(n)], k=[host(w.k[i]) for i in range(n)],
+                     v=[host(w.v[i]) for i in range(n)], ks=[host(w.ks[i]) for i in range(n)],
+                     vs=[host(w.vs[i]) for i in range(n)], table=w.block_table_np, lens=w.seq_lens,
+                     n_q=w.n_q, n_kv=w.n_kv, scale=w.scale, kind=w.kind,
+                     q_dtype="f32" if w.kind == "f32" else "bf16"))
+    gpu = [w.out[i].cpu().numpy().astype(np.float64) for i in range(n)]
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    tasks = [(i, s) for i in range(n) for s in range(w.batch)]
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(_oracle_task, tasks, chunksize=max(1, len(tasks) // (workers * 4)))
+        dt = time.perf_counter() - t0
+    err = 0.0
+    for layer, s, o in res:
+        err = max(err, float(np.max(np.abs(gpu[layer][s] - o))))
+    nbytes = n * w.layer_bytes
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    rec = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
+           "sample": f"{n} layer(s) x {w.batch} sequences of the same workload (all query heads), float64 NumPy "
+                     f"oracle on a {workers}-process pool, {dt:.2f} s wall; {cpu_model}",
+           "seconds": round(dt, 3), "tokens_per_s_per_layer": round(w.batch * n / dt, 2)}
+    return rec, err
+
+
+# ---------------------------------------------------------------------------
+# counters from committed rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("decode.hip", "pkv_device.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_blocks_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload_key):
+    """HBM bytes per decode call from the committed counter summary, or None if
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload_key}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel source hash:\s*([0-9a-f]+)", text)
+    t = re.search(r"HBM bytes per decode call:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_hash():
+        return None
+    return float(t.group(1))
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling only)")
+    ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="run only a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 (no multi-GPU path)"}))
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb * 2 ** 20 // 4
+        src = torch.randn(n, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
+        return
+
+    cfg = WORKLOADS[args.workload]
+    prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
+    t_build = time.perf_counter()
+    w = PrefillWorkload(cfg) if prefill else DecodeWorkload(cfg, args.layers)
+    print(f"[bench] built {args.workload} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+
+    n_ev = w.layers
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n_ev)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        w.step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [e0.elapsed_time(e1) for ev in events for e0, e1 in ev]
+    avg_call_s = float(np.mean(call_ms)) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    if prefill:
+        tflops = w.flops / (wall / args.steps) / 1e12
+        achieved = w.flops / avg_call_s / 1e12
+        rec = {"metric": "chunked prefill over a paged cache: achieved TFLOP/s (bf16 MFMA)", "value": round(tflops, 3),
+               "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+               "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), config-5 shapes)",
+               "config": w.describe(),
+               "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                            "kernel": "prefill_kernel", "avg_call_us": round(avg_call_s * 1e6, 2)},
+               "new_tokens_per_s": round(len(w.ctx) * w.q_len / (wall / args.steps), 1)}
+        print(json.dumps(rec))
+        return
+
+    gbs = w.step_bytes / (wall / args.steps) / 1e9
+    achieved = w.layer_bytes / avg_call_s / 1e9
+    traffic = traffic_from_profile(args.workload)
+    rec = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.kind,
+           "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
+           "config": w.describe(),
+           "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+           "tokens_per_s_per_layer": round(w.batch / (wall / args.steps / w.layers), 1),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "kernel": "decode_kernel + combine_kernel (one decode call)",
+                        "avg_call_us": round(avg_call_s * 1e6, 3), "bytes_per_call": w.layer_bytes}}
+    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        base, err = cpu_baseline(w, args.cpu_sample_layers)
+        rec["cpu_baseline"] = base
+        rec["sampled_parity_max_abs_err"] = err
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
