@@ -142,7 +142,8 @@ class DecodeWorkload:
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
         self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
                     for _ in range(self.layers)]
-        ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks)
+        ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
+                                             pkv.dtype_code(self.k[0]))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
         self.scale = synth.softmax_scale(self.d)
         torch.cuda.synchronize()

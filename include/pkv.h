@@ -118,9 +118,14 @@ pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_s
  * with K_s/V_s the rows of KV head h / (n_q_heads / n_kv_heads) gathered
  * through block_table ([MEM] "MHA, MQA, and GQA"; [FP] "Grouped-query
  * attention").  Computed FlashAttention-style ([KVP] Problem 5, "Tiling",
- * "Online softmax"; [MEM] "FlashAttention-2"): the sequence is split into
- * partitions processed by separate workgroups, each with a running max and
- * sum, then merged; scores never reach memory.
+ * "Online softmax"; [MEM] "FlashAttention-2"): the sequence is split across
+ * workgroups, each keeping a running max and sum, and the pieces are merged;
+ * scores never reach memory.  The split is the library's choice: fixed
+ * partitions per (sequence, KV head) when equal partitions of at most 4096
+ * tokens give one resident workgroup each, otherwise the balanced split, in
+ * which every workgroup receives an equal share of all blocks of the batch
+ * (any length mix, batch <= 4096); pkv_paged_attn_decode_partitioned picks
+ * either one explicitly.
  *   q: (device) [batch][n_q_heads][d_head]; out: (device) same shape.
  *   k_cache, v_cache: (device) [num_blocks][n_kv_heads][block_size][d_head].
  *   k_scale, v_scale: (device) fp32 [num_blocks][n_kv_heads] for FP8, else NULL.
@@ -129,7 +134,10 @@ pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_s
  * Supported: d_head in {64, 128}; block_size 16; (q, kv) in {(F32, F32),
  * (BF16, BF16), (BF16, FP8_E4M3FN)}; out F32 or BF16; n_q_heads a multiple of
  * n_kv_heads.  workspace: (device) at least
- * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned.
+ * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned; its contents
+ * need no initialisation and are scratch for the call.  Calls that share one
+ * workspace must be ordered (same stream).  The result is deterministic:
+ * the same inputs and launch give the same bits.
  * Accumulation is fp32; with bf16/fp8 KV the softmax weights are rounded to
  * bf16 before the value product and the normaliser sums the same rounded
  * weights. */
@@ -141,9 +149,11 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, 
                                  int32_t block_size, float scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
-/* Same as pkv_paged_attn_decode with an explicit partition size in tokens
- * (0 = the library's choice).  partition_tokens must be a positive multiple of
- * 256 (of 64 * the library's chunk for the head group).  Used to test that
+/* Same as pkv_paged_attn_decode with an explicit split: partition_tokens > 0
+ * gives fixed partitions of that many tokens per (sequence, KV head), one
+ * workgroup each, and must be a multiple of 256 (of 64 * the chunk of the
+ * head group) up to 4096; -1 asks for the balanced split (batch <= 4096,
+ * else PKV_ERR_UNSUPPORTED); 0 is the library's choice.  Used to test that
  * results do not depend on the split and to tune it. */
 pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
                                              const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
@@ -154,10 +164,12 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
                                              int32_t block_size, float scale, int32_t partition_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes the decode call needs (partition_tokens as above, 0 = the
- * library's choice).  Returns 0 for invalid arguments. */
+/* Workspace bytes the decode call needs on the current device (partition_tokens
+ * as above, 0 = the library's choice).  Returns 0 for invalid arguments, or
+ * when the split depends on the device and no device is present. */
 size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
-                                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens);
+                                       int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
+                                       int32_t partition_tokens);
 
 /* Chunked prefill attention: each sequence s brings q_len = cu_q_lens[s+1] -
  * cu_q_lens[s] new query tokens at absolute positions context_lens[s] + i.

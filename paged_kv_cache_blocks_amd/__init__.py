@@ -40,7 +40,7 @@ _SIGS = {
     "pkv_paged_attn_decode_partitioned": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                            _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp],
                                           ctypes.c_int),
-    "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _sz),
+    "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32], _sz),
     "pkv_paged_attn_prefill_chunk": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                                       ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                       _sz, _vp], ctypes.c_int),
@@ -172,9 +172,9 @@ def check_tables(block_table, seq_lens, num_blocks: int, block_size: int = 16, s
 
 
 def paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
-                                partition_tokens=0) -> int:
+                                kv_dtype: int = BF16, partition_tokens=0) -> int:
     return load().pkv_paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq,
-                                               block_size, partition_tokens)
+                                                  block_size, kv_dtype, partition_tokens)
 
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_kv_heads, d_head, block_size, scale,
@@ -188,7 +188,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
     if out is None:
         out = torch.empty((batch, n_q_heads, d_head), dtype=out_dtype, device=q.device)
     ws_bytes = paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, block_table.shape[1], block_size,
-                                           partition_tokens)
+                                           dtype_code(k_cache), partition_tokens)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None

@@ -1,5 +1,6 @@
-// Paged decode attention for gfx950: split-K over the sequence, FlashAttention
-// style online softmax inside each partition, and a partition-combine pass.
+// Paged decode attention for gfx950: split-K over the sequence with a
+// FlashAttention-style online softmax per wave, merged per workgroup, and a
+// merge pass for sequences that several workgroups share.
 //
 // Method ("KV cache, PagedAttention and FlashAttention", Problem 5: tiling,
 // online softmax with a running max m and sum l rescaled by e^(m - m_new),
@@ -9,26 +10,31 @@
 // the very end, parallelise over the sequence as well as batch and head; GQA:
 // the query heads of a group are processed against the same K/V block).
 //
-// Work decomposition
-//   grid = (partitions, KV heads x head chunks, sequences), 256 threads.
-//   A workgroup owns one partition of one sequence for GW query heads that
-//   share one KV head.  Its 4 waves take the partition's blocks round-robin in
-//   chunks of CB blocks and run independent online softmaxes; the 4 states are
-//   merged once at the end through LDS.
-//   Per chunk a wave:
-//     1. reads the chunk's K and V slabs from HBM with coalesced 16-byte loads
-//        (issued one chunk ahead; block ids come from the table once per wave)
-//     2. stages K into LDS as bf16 rows (fp8 converted here, once per element)
-//        and V as bf16 token *pairs* interleaved per column, so the value
-//        product runs on v_dot2c_f32_bf16;
-//     3. scores: lane (head h, token t) holds q[h] in registers and reads the
-//        whole K row from LDS -- every K element is fetched from HBM once and
-//        serves all GW heads of the group;
-//     4. online softmax over the chunk with DPP lane-group reductions;
-//        weights go to LDS as bf16 pairs;
-//     5. values: lane c owns output columns (2c, 2c+1) for all GW heads and
-//        accumulates dot2(p pair, v pair) in f32.
-//   f32 caches take the same path with f32 rows and fma in place of dot2.
+// A workgroup (4 waves) serves GW query heads that share one KV head.  Its
+// waves take the blocks of a range round-robin in chunks of CB blocks; per
+// chunk a wave
+//   1. has the chunk's K and V slabs in registers (coalesced 16-byte loads,
+//      issued while the previous chunk computed; block ids come from the
+//      table once per range, one id per lane);
+//   2. stages K into LDS as bf16 rows (fp8 converted here, once per element)
+//      and V as bf16 token *pairs* interleaved per column, so the value
+//      product runs on v_dot2c_f32_bf16;
+//   3. scores: lane (head h, token t, d-half) holds half of q[h] in registers
+//      and reads half of the K row from LDS; a DPP add joins the halves.
+//      Every K element is fetched from HBM once and serves all GW heads;
+//   4. online softmax over the chunk with DPP lane-group reductions; the
+//      weights go to LDS as bf16 pairs;
+//   5. values: lane c owns output columns (2c, 2c+1) for all GW heads and
+//      accumulates dot2(weight pair, value pair) in f32.
+// f32 caches take the same path with f32 rows and fma in place of dot2.
+//
+// Work split.  Balanced mode (the default): the flattened space of
+// (KV head, sequence, block) is cut into one equal contiguous range per
+// workgroup, so every CU gets the same number of blocks whatever the length
+// mix.  A workgroup writes the final output of every sequence it covers
+// whole, and partial (m, l, o) states for at most two cut sequences, which a
+// small merge kernel combines.  Partition mode: fixed-size token partitions
+// per (sequence, KV head) on a 1-D grid, then the same style of merge.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -36,6 +42,7 @@ namespace pkv {
 
 constexpr int kBlock = 16;  // tokens per cache block
 constexpr int kWaves = 4;   // waves per workgroup
+constexpr int kSegBlocks = kWaves * kWave;  // blocks one id load covers (one id per lane per wave)
 
 constexpr int align16(int x) { return (x + 15) & ~15; }
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
@@ -57,119 +64,140 @@ template <int LW> struct LoadVec;
 template <> struct LoadVec<16> { typedef u32x4 T; };
 template <> struct LoadVec<8> { typedef u32x2 T; };
 
+// Compile-time layout of one (element kind, head dim, heads per workgroup).
 template <int KIND, int D, int GW>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+struct Lay {
   using Gm = Geo<KIND, D>;
   using LV = typename LoadVec<Gm::LW>::T;
-  constexpr bool F32P = (KIND == KIND_F32);
-  constexpr int T = kWave / GW;                      // token slots per head group (score layout)
-  constexpr int CB = T > kBlock ? T / kBlock : 1;    // blocks per chunk
-  constexpr int R = T < kBlock ? kBlock / T : 1;     // score rounds per chunk
-  constexpr int CT = CB * kBlock;                    // tokens per chunk
-  constexpr int ES = F32P ? 4 : 2;                   // bytes per element in LDS
-  constexpr int KROW = D * ES + 16;                  // padded K row in LDS
-  constexpr int VROW = D * 4 + 16;                   // f32 V row, or one bf16-pair row
-  constexpr int NPAIR = kBlock / 2;                  // token pairs per block
-  constexpr int K_BYTES = CT * KROW;
-  constexpr int V_BYTES = F32P ? CT * VROW : CB * NPAIR * VROW;
-  constexpr int P_BYTES = F32P ? CT * GW * 4 : CB * NPAIR * GW * 4;
-  constexpr int A_BYTES = align16(GW * 4);
-  constexpr int WAVE_BYTES = align16(K_BYTES + V_BYTES + P_BYTES + A_BYTES);
-  constexpr int MERGE_BYTES = kWaves * GW * D * 4 + kWaves * GW * 2 * 4;
-  constexpr int SMEM = cmax(kWaves * WAVE_BYTES, MERGE_BYTES);
-  // value-product layout: columns per lane and lane groups per pair row
-  constexpr int PVL = F32P ? kWave : D / 2;          // lanes covering one row
-  constexpr int PVG = kWave / PVL;                   // row groups (bf16 path, d = 64)
-  constexpr int COLS = F32P ? D / kWave : 2;         // output columns per lane
-  static_assert(COLS >= 1 && PVG >= 1, "value layout");
+  static constexpr bool F32P = (KIND == KIND_F32);
+  // score layout: each (token, head) score is split over QS adjacent lanes
+  // that each hold 1/QS of q[head] (fewer registers, more waves per SIMD)
+  static constexpr int QS = 2;
+  static constexpr int TG = kWave / GW;                 // lanes per head group
+  static constexpr int T = TG / QS;                     // tokens per score round
+  // blocks per chunk: a round must fit in a chunk, and fp8 takes two blocks
+  // so a chunk still moves 8 KiB of K+V per wave
+  static constexpr int CB = (T > kBlock ? T / kBlock : 1) * (KIND == KIND_FP8 ? 2 : 1);
+  static constexpr int CT = CB * kBlock;                // tokens per chunk
+  static constexpr int R = CT / T;                      // score rounds per chunk
+  static constexpr int ES = F32P ? 4 : 2;               // bytes per element in LDS
+  static constexpr int KROW = D * ES + 16;              // padded K row in LDS
+  static constexpr int VROW = D * 4 + 16;               // f32 V row, or one bf16-pair row
+  static constexpr int NPAIR = kBlock / 2;              // token pairs per block
+  static constexpr int K_BYTES = CT * KROW;
+  static constexpr int V_BYTES = F32P ? CT * VROW : CB * NPAIR * VROW;
+  static constexpr int P_BYTES = F32P ? CT * GW * 4 : CB * NPAIR * GW * 4;
+  static constexpr int A_BYTES = align16(GW * 4);
+  static constexpr int WAVE_BYTES = align16(K_BYTES + V_BYTES + P_BYTES + A_BYTES);
+  static constexpr int MERGE_BYTES = kWaves * GW * D * 4 + kWaves * GW * 2 * 4;
+  static constexpr int SMEM = cmax(kWaves * WAVE_BYTES, MERGE_BYTES);
+  // value-product layout
+  static constexpr int PVL = F32P ? kWave : D / 2;      // lanes covering one row
+  static constexpr int PVG = kWave / PVL;               // row groups (bf16 path, d = 64)
+  static constexpr int COLS = F32P ? D / kWave : 2;     // output columns per lane
+  static constexpr int QV = (F32P ? D / 4 : D / 8) / QS;  // 16-byte pieces of q per lane
+  static_assert(COLS >= 1 && PVG >= 1 && R >= 1 && CT % T == 0, "layout");
+};
 
-  __shared__ __align__(16) char smem[SMEM];
+// Per-wave running state: q slice, running max (log2 units), this lane's share
+// of the running sum, and the output accumulators.
+template <int KIND, int D, int GW>
+struct WaveState {
+  using Ly = Lay<KIND, D, GW>;
+  u32x4 qv[Ly::QV];
+  float m_run, l_run;
+  float o[GW][Ly::COLS];
+};
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = threadIdx.x / kWave;
-  const int part = blockIdx.x;
-  const int s = blockIdx.z;
-  const int kvh = blockIdx.y / a.head_chunks;
-  const int h0 = kvh * a.group + (blockIdx.y % a.head_chunks) * GW;
-
-  int L = a.seq_lens[s];
-  L = min(max(L, 0), a.max_blocks * kBlock);
-  const int p0 = part * a.part_tokens;
-  if (a.n_parts > 1 && p0 >= L) return;
-  const int plen = max(0, min(a.part_tokens, L - p0));
-  const int nb_part = (plen + kBlock - 1) / kBlock;
-  const int n_chunks = (nb_part + CB - 1) / CB;
-  const int n_my = n_chunks > w ? (n_chunks - w + kWaves - 1) / kWaves : 0;
-
-  // this wave's block ids, one per lane: lane i <-> block (i % CB) of the
-  // wave's chunk i / CB (= partition chunk w + 4 * (i / CB))
-  int my_id = 0;
-  {
-    const int pb = (w + kWaves * (lane / CB)) * CB + lane % CB;
-    if (pb < nb_part) {
-      const int id = a.block_table[(int64_t)s * a.max_blocks + p0 / kBlock + pb];
-      my_id = min(max(id, 0), (int)(a.num_blocks - 1));
-    }
-  }
-
-  char* const wbase = smem + w * WAVE_BYTES;
-  char* const k_lds = wbase;
-  char* const v_lds = wbase + K_BYTES;
-  char* const p_lds = v_lds + V_BYTES;
-  float* const a_lds = reinterpret_cast<float*>(p_lds + P_BYTES);
-
-  // score layout: lane = sh * T + st  (head sh of the group, token slot st)
-  const int sh = lane / T;
-  const int st = lane % T;
-
-  // q row of head h0 + sh, kept in registers for the whole partition
-  constexpr int QV = F32P ? D / 4 : D / 8;
-  u32x4 qv[QV];
-  {
-    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.n_q + h0 + sh) * D * (F32P ? 4 : 2);
+template <int KIND, int D, int GW>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, int s, int h0, int lane, WaveState<KIND, D, GW>& ws) {
+  using Ly = Lay<KIND, D, GW>;
+  const int sh = lane / Ly::TG, qh = lane % Ly::QS;
+  const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.n_q + h0 + sh) * D * Ly::ES;
 #pragma unroll
-    for (int j = 0; j < QV; ++j) qv[j] = ld16(qrow + j * 16);
-  }
+  for (int j = 0; j < Ly::QV; ++j) ws.qv[j] = ld16(qrow + (qh * Ly::QV + j) * 16);
+}
 
-  float m_run = -INFINITY;  // running max of this lane's head (log2 units)
-  float l_run = 0.f;        // this lane's share of the running sum
-  float o[GW][COLS];
+template <int KIND, int D, int GW>
+__device__ __forceinline__ void reset_state(WaveState<KIND, D, GW>& ws) {
+  ws.m_run = -INFINITY;
+  ws.l_run = 0.f;
 #pragma unroll
   for (int h = 0; h < GW; ++h)
 #pragma unroll
-    for (int k = 0; k < COLS; ++k) o[h][k] = 0.f;
+    for (int k = 0; k < Lay<KIND, D, GW>::COLS; ++k) ws.o[h][k] = 0.f;
+}
 
+// Blocks [blk_begin, blk_begin + nblk) (nblk <= kSegBlocks) of sequence s,
+// KV head kvh; the four waves interleave chunks.  Tokens at or past L, or past
+// the range, are masked.  Accumulates into this wave's state.
+template <int KIND, int D, int GW>
+__device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int L,
+                                           int w, int lane, char* wbase, WaveState<KIND, D, GW>& ws) {
+  using Ly = Lay<KIND, D, GW>;
+  using Gm = typename Ly::Gm;
+  using LV = typename Ly::LV;
+  constexpr bool F32P = Ly::F32P;
+  constexpr int T = Ly::T, TG = Ly::TG, QS = Ly::QS, CB = Ly::CB, CT = Ly::CT, R = Ly::R, ES = Ly::ES;
+  constexpr int KROW = Ly::KROW, VROW = Ly::VROW, NPAIR = Ly::NPAIR, PVL = Ly::PVL, PVG = Ly::PVG;
+  constexpr int COLS = Ly::COLS, QV = Ly::QV;
+
+  const int n_chunks = (nblk + CB - 1) / CB;
+  const int n_my = n_chunks > w ? (n_chunks - w + kWaves - 1) / kWaves : 0;
+  if (n_my == 0) return;
+  // a chunk may extend past the range (nblk not a multiple of CB): tokens
+  // there belong to another range even when the sequence goes on
+  L = min(L, (blk_begin + nblk) * kBlock);
+  const int sh = lane / TG, st = (lane % TG) / QS, qh = lane % QS;
+
+  // this wave's block ids, one per lane: lane i <-> block (i % CB) of the
+  // wave's chunk i / CB (= range chunk w + 4 * (i / CB))
+  const int pb_lane = (w + kWaves * (lane / CB)) * CB + lane % CB;
+  int my_id = 0;
+  float my_ks = 1.f, my_vs = 1.f;
+  if (pb_lane < nblk) {
+    const int id = a.block_table[(int64_t)s * a.max_blocks + blk_begin + pb_lane];
+    my_id = min(max(id, 0), (int)(a.num_blocks - 1));
+    if constexpr (KIND == KIND_FP8) {
+      my_ks = a.k_scale[(int64_t)my_id * a.n_kv + kvh];
+      my_vs = a.v_scale[(int64_t)my_id * a.n_kv + kvh];
+    }
+  }
+  const int tok0 = blk_begin * kBlock;  // sequence position of the range's first token
+
+  char* const k_lds = wbase;
+  char* const v_lds = wbase + Ly::K_BYTES;
+  char* const p_lds = v_lds + Ly::V_BYTES;
+  float* const a_lds = reinterpret_cast<float*>(p_lds + Ly::P_BYTES);
   const char* const kc = reinterpret_cast<const char*>(a.k_cache);
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
-  LV kreg[CB][Gm::NLK], vreg[CB][Gm::NLK];
 
+  LV bk[CB][Gm::NLK], bv[CB][Gm::NLK];
   auto issue_loads = [&](int c) {
 #pragma unroll
     for (int b = 0; b < CB; ++b) {
-      const int id = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(my_id, c * CB + b));
+      const int id = __builtin_amdgcn_readlane(my_id, c * CB + b);
       const int64_t slab = ((int64_t)id * a.n_kv + kvh) * Gm::slab_bytes;
 #pragma unroll
       for (int i = 0; i < Gm::NLK; ++i) {
         const int64_t off = slab + (int64_t)(i * kWave + lane) * Gm::LW;
-        kreg[b][i] = *reinterpret_cast<const LV*>(kc + off);
-        vreg[b][i] = *reinterpret_cast<const LV*>(vc + off);
+        bk[b][i] = *reinterpret_cast<const LV*>(kc + off);
+        bv[b][i] = *reinterpret_cast<const LV*>(vc + off);
       }
     }
   };
 
-  if (n_my > 0) issue_loads(0);
-
+  issue_loads(0);
   for (int c = 0; c < n_my; ++c) {
-    const int ct0 = (w + kWaves * c) * CT;  // first token of the chunk (partition-relative)
-    const int nvalid = plen - ct0;         // tokens of the chunk that exist (may exceed CT)
+    const int ct0 = (w + kWaves * c) * CT;      // first token of the chunk (range-relative)
+    const int nvalid = L - (tok0 + ct0);        // tokens of the chunk that exist (may exceed CT)
     float kscale[CB], vscale[CB];
 #pragma unroll
     for (int b = 0; b < CB; ++b) {
       kscale[b] = vscale[b] = 1.f;
       if constexpr (KIND == KIND_FP8) {
-        const int id = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(my_id, c * CB + b));
-        kscale[b] = a.k_scale[(int64_t)id * a.n_kv + kvh];
-        vscale[b] = a.v_scale[(int64_t)id * a.n_kv + kvh];
+        kscale[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), c * CB + b));
+        vscale[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), c * CB + b));
       }
     }
 
@@ -185,14 +213,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         if constexpr (KIND == KIND_FP8) {
           constexpr int NW = Gm::LW / 4;
           uint32_t wv[NW];
-          __builtin_memcpy(wv, &kreg[b][i], Gm::LW);
+          __builtin_memcpy(wv, &bk[b][i], Gm::LW);
           uint32_t bw[2 * NW];
 #pragma unroll
           for (int e = 0; e < NW; ++e) fp8x4_to_bf16x4(wv[e], bw[2 * e], bw[2 * e + 1]);
 #pragma unroll
           for (int e = 0; e < NW / 2; ++e) st16(dst + e * 16, u32x4{bw[4 * e], bw[4 * e + 1], bw[4 * e + 2], bw[4 * e + 3]});
         } else {
-          st16(dst, kreg[b][i]);
+          st16(dst, bk[b][i]);
         }
       }
       const bool tail = nvalid < (b + 1) * kBlock;  // some rows of this block are past the end
@@ -201,7 +229,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int i = 0; i < Gm::NLK; ++i) {
           const int r = lane / Gm::LPR + Gm::RPI * i;
           const int c0 = (lane % Gm::LPR) * Gm::EPL;
-          u32x4 v = vreg[b][i];
+          u32x4 v = bv[b][i];
           if (tail && b * kBlock + r >= nvalid) v = u32x4{0, 0, 0, 0};
           st16(v_lds + (b * kBlock + r) * VROW + c0 * 4, v);
         }
@@ -217,32 +245,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
           if constexpr (KIND == KIND_FP8) {
             constexpr int NW = Gm::LW / 4;
             uint32_t wa[NW], wb[NW];
-            __builtin_memcpy(wa, &vreg[b][i], Gm::LW);
-            __builtin_memcpy(wb, &vreg[b][i + 1], Gm::LW);
+            __builtin_memcpy(wa, &bv[b][i], Gm::LW);
+            __builtin_memcpy(wb, &bv[b][i + 1], Gm::LW);
 #pragma unroll
             for (int e = 0; e < NW; ++e) {
               fp8x4_to_bf16x4(wa[e], A[2 * e], A[2 * e + 1]);
               fp8x4_to_bf16x4(wb[e], Bv[2 * e], Bv[2 * e + 1]);
             }
           } else {
-            __builtin_memcpy(A, &vreg[b][i], Gm::LW);
-            __builtin_memcpy(Bv, &vreg[b][i + 1], Gm::LW);
-          }
-          if (tail) {
-            if (b * kBlock + r0 >= nvalid) {
-#pragma unroll
-              for (int e = 0; e < NB; ++e) A[e] = 0;
-            }
-            if (b * kBlock + r1 >= nvalid) {
-#pragma unroll
-              for (int e = 0; e < NB; ++e) Bv[e] = 0;
-            }
+            __builtin_memcpy(A, &bv[b][i], Gm::LW);
+            __builtin_memcpy(Bv, &bv[b][i + 1], Gm::LW);
           }
           uint32_t pr[2 * NB];
 #pragma unroll
           for (int e = 0; e < NB; ++e) {
             pr[2 * e] = pair_lo(A[e], Bv[e]);
             pr[2 * e + 1] = pair_hi(A[e], Bv[e]);
+          }
+          if (tail) {
+            // rows past the end may hold NaN: clear their half of every pair
+            const uint32_t keep = (b * kBlock + r0 < nvalid ? 0x0000ffffu : 0u) |
+                                  (b * kBlock + r1 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int e = 0; e < 2 * NB; ++e) pr[e] &= keep;
           }
           char* dst = v_lds + (b * NPAIR + pq) * VROW + c0 * 4;
 #pragma unroll
@@ -260,70 +285,81 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int tau = r * T + st;  // token within the chunk
-      const char* krow = k_lds + tau * KROW;
-      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+      const char* krow = k_lds + tau * KROW + qh * QV * 16;
+      float acc0, acc1, acc2, acc3;
       if constexpr (F32P) {
+        acc0 = acc1 = acc2 = acc3 = 0.f;
 #pragma unroll
         for (int j = 0; j < QV; ++j) {
           const u32x4 kp = ld16(krow + j * 16);
-          acc0 = fmaf(__uint_as_float(qv[j][0]), __uint_as_float(kp[0]), acc0);
-          acc1 = fmaf(__uint_as_float(qv[j][1]), __uint_as_float(kp[1]), acc1);
-          acc2 = fmaf(__uint_as_float(qv[j][2]), __uint_as_float(kp[2]), acc2);
-          acc3 = fmaf(__uint_as_float(qv[j][3]), __uint_as_float(kp[3]), acc3);
+          acc0 = fmaf(__uint_as_float(ws.qv[j][0]), __uint_as_float(kp[0]), acc0);
+          acc1 = fmaf(__uint_as_float(ws.qv[j][1]), __uint_as_float(kp[1]), acc1);
+          acc2 = fmaf(__uint_as_float(ws.qv[j][2]), __uint_as_float(kp[2]), acc2);
+          acc3 = fmaf(__uint_as_float(ws.qv[j][3]), __uint_as_float(kp[3]), acc3);
         }
       } else {
+        const u32x4 k0 = ld16(krow);
+        acc0 = dot2_bf16(ws.qv[0][0], k0[0], 0.f);
+        acc1 = dot2_bf16(ws.qv[0][1], k0[1], 0.f);
+        acc2 = dot2_bf16(ws.qv[0][2], k0[2], 0.f);
+        acc3 = dot2_bf16(ws.qv[0][3], k0[3], 0.f);
 #pragma unroll
-        for (int j = 0; j < QV; ++j) {
+        for (int j = 1; j < QV; ++j) {
           const u32x4 kp = ld16(krow + j * 16);
-          acc0 = dot2_bf16(qv[j][0], kp[0], acc0);
-          acc1 = dot2_bf16(qv[j][1], kp[1], acc1);
-          acc2 = dot2_bf16(qv[j][2], kp[2], acc2);
-          acc3 = dot2_bf16(qv[j][3], kp[3], acc3);
+          acc0 = dot2_bf16(ws.qv[j][0], kp[0], acc0);
+          acc1 = dot2_bf16(ws.qv[j][1], kp[1], acc1);
+          acc2 = dot2_bf16(ws.qv[j][2], kp[2], acc2);
+          acc3 = dot2_bf16(ws.qv[j][3], kp[3], acc3);
         }
       }
+      float dot = (acc0 + acc1) + (acc2 + acc3);
+      dot += dpp_f<DPP_QUAD_XOR1>(dot);  // the other d-half of this (token, head)
       float ksc = kscale[0];
       if constexpr (CB > 1) {
 #pragma unroll
         for (int b = 1; b < CB; ++b) ksc = (tau / kBlock == b) ? kscale[b] : ksc;
       }
-      const float sv = ((acc0 + acc1) + (acc2 + acc3)) * (a.scale_log2 * ksc);
+      const float sv = dot * (a.scale_log2 * ksc);
       sc[r] = (tau < nvalid) ? sv : -INFINITY;
       cmax_ = fmaxf(cmax_, sc[r]);
     }
-    cmax_ = group_max<T>(cmax_);
-    const float m_new = fmaxf(m_run, cmax_);
+    cmax_ = group_max<TG>(cmax_);
+    const float m_new = fmaxf(ws.m_run, cmax_);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m_run - m_use);
-    m_run = m_new;
+    const float alpha = exp2_fast(ws.m_run - m_use);
+    ws.m_run = m_new;
     float lsum = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int tau = r * T + st;
       float p = exp2_fast(sc[r] - m_use);
       if constexpr (F32P) {
-        reinterpret_cast<float*>(p_lds)[tau * GW + sh] = p;
+        if (qh == 0) reinterpret_cast<float*>(p_lds)[tau * GW + sh] = p;
       } else {
         p = round_bf16(p);
         const int b = tau / kBlock, t = tau % kBlock;
         const int i = t / Gm::RPI, g = t % Gm::RPI;
         const int pq = g + Gm::RPI * (i / 2);
-        reinterpret_cast<__bf16*>(p_lds)[((b * NPAIR + pq) * GW + sh) * 2 + (i & 1)] = (__bf16)p;
+        if (qh == 0) reinterpret_cast<__bf16*>(p_lds)[((b * NPAIR + pq) * GW + sh) * 2 + (i & 1)] = (__bf16)p;
       }
-      lsum += p;
+      lsum += (qh == 0) ? p : 0.f;
     }
-    l_run = l_run * alpha + lsum;
-    if (st == 0) a_lds[sh] = alpha;
+    ws.l_run = ws.l_run * alpha + lsum;
+    // alpha is exactly 1 for a head whose running max did not move
+    const bool rescale = __builtin_amdgcn_ballot_w64(alpha != 1.f) != 0;
+    if (rescale && st == 0 && qh == 0) a_lds[sh] = alpha;
     wave_lds_sync();
 
     // ---- rescale and accumulate P V ----
-    float al[GW];
+    if (rescale) {
+      float al[GW];
 #pragma unroll
-    for (int h = 0; h < GW; ++h) al[h] = a_lds[h];
+      for (int h = 0; h < GW; ++h) al[h] = a_lds[h];
 #pragma unroll
-    for (int h = 0; h < GW; ++h)
+      for (int h = 0; h < GW; ++h)
 #pragma unroll
-      for (int k = 0; k < COLS; ++k) o[h][k] *= al[h];
-
+        for (int k = 0; k < COLS; ++k) ws.o[h][k] *= al[h];
+    }
     if constexpr (F32P) {
       const int col = lane * COLS;
 #pragma unroll 4
@@ -338,16 +374,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int h = 0; h < GW; ++h)
 #pragma unroll
-          for (int k = 0; k < COLS; ++k) o[h][k] = fmaf(pp[h], vv[k], o[h][k]);
+          for (int k = 0; k < COLS; ++k) ws.o[h][k] = fmaf(pp[h], vv[k], ws.o[h][k]);
       }
     } else {
       const int pg = lane / PVL;
       const int dcol = (lane % PVL) * 2;
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
+        // bf16 accumulates into o directly; fp8 gathers the block's product
+        // first and multiplies it by the block's V scale once
         float t[GW][2];
 #pragma unroll
-        for (int h = 0; h < GW; ++h) t[h][0] = t[h][1] = 0.f;
+        for (int h = 0; h < GW; ++h) {
+          t[h][0] = (KIND == KIND_FP8) ? 0.f : ws.o[h][0];
+          t[h][1] = (KIND == KIND_FP8) ? 0.f : ws.o[h][1];
+        }
 #pragma unroll
         for (int qq = 0; qq < NPAIR / PVG; ++qq) {
           const int pq = qq * PVG + pg;
@@ -364,34 +405,47 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
-          o[h][0] = fmaf(vscale[b], t[h][0], o[h][0]);
-          o[h][1] = fmaf(vscale[b], t[h][1], o[h][1]);
+          if constexpr (KIND == KIND_FP8) {
+            ws.o[h][0] = fmaf(vscale[b], t[h][0], ws.o[h][0]);
+            ws.o[h][1] = fmaf(vscale[b], t[h][1], ws.o[h][1]);
+          } else {
+            ws.o[h][0] = t[h][0];
+            ws.o[h][1] = t[h][1];
+          }
         }
       }
     }
   }
+}
 
-  // ---- merge the four waves' states ----
-  const float l_head = group_sum<T>(l_run);
-  if constexpr (!F32P && PVG > 1) {
+// Merge the four waves' states in LDS.  emit(h, col, M, l, o) is called once
+// per (head, column) of the workgroup, spread over the 256 threads; M is in
+// log2 units and (l, o) are unnormalised.  All threads must call it.
+template <int KIND, int D, int GW, class Emit>
+__device__ __forceinline__ void merge_waves(char* smem, int w, int lane, WaveState<KIND, D, GW>& ws, Emit emit) {
+  using Ly = Lay<KIND, D, GW>;
+  constexpr int COLS = Ly::COLS, PVL = Ly::PVL, PVG = Ly::PVG, TG = Ly::TG, QS = Ly::QS;
+  const int sh = lane / TG, st = (lane % TG) / QS, qh = lane % QS;
+  const float l_head = group_sum<TG>(ws.l_run);
+  if constexpr (!Ly::F32P && PVG > 1) {
 #pragma unroll
     for (int h = 0; h < GW; ++h)
 #pragma unroll
-      for (int k = 0; k < COLS; ++k) o[h][k] += __shfl_xor(o[h][k], 32);
+      for (int k = 0; k < COLS; ++k) ws.o[h][k] += __shfl_xor(ws.o[h][k], 32);
   }
   __syncthreads();
   float* mo = reinterpret_cast<float*>(smem);  // [wave][head][d]
   float* mml = mo + kWaves * GW * D;            // [wave][head][2]
-  if (st == 0) {
-    mml[(w * GW + sh) * 2 + 0] = m_run;
+  if (st == 0 && qh == 0) {
+    mml[(w * GW + sh) * 2 + 0] = ws.m_run;
     mml[(w * GW + sh) * 2 + 1] = l_head;
   }
   if (lane < PVL) {
-    const int col = F32P ? lane * COLS : (lane % PVL) * 2;
+    const int col = Ly::F32P ? lane * COLS : (lane % PVL) * 2;
 #pragma unroll
     for (int h = 0; h < GW; ++h)
 #pragma unroll
-      for (int k = 0; k < COLS; ++k) mo[(w * GW + h) * D + col + k] = o[h][k];
+      for (int k = 0; k < COLS; ++k) mo[(w * GW + h) * D + col + k] = ws.o[h][k];
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < GW * D; idx += 256) {
@@ -409,59 +463,283 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         osum = fmaf(e, mo[(ww * GW + h) * D + col], osum);
       }
     }
+    emit(h, col, M, lsum, osum);
+  }
+  __syncthreads();  // the LDS is reused by whatever runs next
+}
+
+__device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, float v) {
+  if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[idx] = (__bf16)v;
+  else reinterpret_cast<float*>(a.out)[idx] = v;
+}
+
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
+  return min(max(a.seq_lens[s], 0), a.max_blocks * kBlock);
+}
+
+// ---------------------------------------------------------------------------
+// Partition mode: 1-D grid, KV head (x head chunk) fastest, then sequence, then
+// partition, so consecutive workgroups go to different XCDs and every XCD
+// sees the same mix of heads, sequences and partitions.
+// ---------------------------------------------------------------------------
+template <int KIND, int D, int GW>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+  using Ly = Lay<KIND, D, GW>;
+  __shared__ __align__(16) char smem[Ly::SMEM];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int hk = a.n_kv * a.head_chunks;
+  const int kvc = blockIdx.x % hk;
+  const int s = (blockIdx.x / hk) % a.batch;
+  const int part = blockIdx.x / (hk * a.batch);
+  const int kvh = kvc / a.head_chunks;
+  const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
+  const int p0 = part * a.part_tokens;
+
+  const int L = clamp_len(a, s);
+  if (a.n_parts > 1 && p0 >= L) return;
+  WaveState<KIND, D, GW> ws;
+  load_q(a, s, h0, lane, ws);
+  const int plen = max(0, min(a.part_tokens, L - p0));
+  const int nb_part = (plen + kBlock - 1) / kBlock;
+  reset_state(ws);
+  run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws);
+  merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
     const int hq = h0 + h;
     if (a.n_parts == 1) {
-      const float val = lsum > 0.f ? osum / lsum : 0.f;
-      const int64_t oi = ((int64_t)s * a.n_q + hq) * D + col;
-      if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[oi] = (__bf16)val;
-      else reinterpret_cast<float*>(a.out)[oi] = val;
+      store_out(a, ((int64_t)s * a.n_q + hq) * D + col, l > 0.f ? o / l : 0.f);
     } else {
       const int64_t pi = ((int64_t)s * a.n_q + hq) * a.n_parts + part;
-      a.ws_o[pi * D + col] = osum;
+      a.ws_o[pi * D + col] = o;
       if (col == 0) {
         a.ws_ml[pi * 2 + 0] = M;
-        a.ws_ml[pi * 2 + 1] = lsum;
+        a.ws_ml[pi * 2 + 1] = l;
       }
     }
-  }
+  });
 }
 
 // Merge the partitions of one (sequence, query head): the rescale rule of the
-// online softmax applied to whole partitions.
+// online softmax applied to whole partitions.  One wave per (sequence, head):
+// lane j takes partition j of each group of 64 for the max and the weights,
+// and every lane accumulates its output columns over the partitions with each
+// weight broadcast from its lane.
 template <int D>
 __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   constexpr int COLS = D / kWave;
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
-  int L = a.seq_lens[s];
-  L = min(max(L, 0), a.max_blocks * kBlock);
+  const int L = clamp_len(a, s);
   const int nv = (L + a.part_tokens - 1) / a.part_tokens;
   const int64_t base = ((int64_t)s * a.n_q + hq) * a.n_parts;
   const float* ml = a.ws_ml + base * 2;
   const float* op = a.ws_o + base * D;
   float M = -INFINITY;
-  for (int j = 0; j < nv; ++j) M = fmaxf(M, ml[2 * j]);
+  for (int j0 = 0; j0 < nv; j0 += kWave)
+    if (j0 + lane < nv) M = fmaxf(M, ml[2 * (j0 + lane)]);
+  M = group_max<kWave>(M);
   float den = 0.f, num[COLS];
 #pragma unroll
   for (int k = 0; k < COLS; ++k) num[k] = 0.f;
   if (M != -INFINITY) {
-    for (int j = 0; j < nv; ++j) {
-      const float m = ml[2 * j];
-      if (m == -INFINITY) continue;
-      const float e = exp2_fast(m - M);
-      den = fmaf(e, ml[2 * j + 1], den);
+    for (int j0 = 0; j0 < nv; j0 += kWave) {
+      float wj = 0.f, lj = 0.f;
+      if (j0 + lane < nv) {
+        const float m = ml[2 * (j0 + lane)];
+        lj = ml[2 * (j0 + lane) + 1];
+        wj = (m == -INFINITY) ? 0.f : exp2_fast(m - M);
+      }
+      den += group_sum<kWave>(wj * lj);
+      const int cnt = min(kWave, nv - j0);
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        float x[4][COLS], e[4];
 #pragma unroll
-      for (int k = 0; k < COLS; ++k) num[k] = fmaf(e, op[(int64_t)j * D + lane + k * kWave], num[k]);
+        for (int u = 0; u < 4; ++u) {
+          e[u] = __shfl(wj, j + u);
+#pragma unroll
+          for (int k = 0; k < COLS; ++k) x[u][k] = op[(int64_t)(j0 + j + u) * D + lane + k * kWave];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int k = 0; k < COLS; ++k) num[k] = fmaf(e[u], x[u][k], num[k]);
+      }
+      for (; j < cnt; ++j) {
+        const float e = __shfl(wj, j);
+#pragma unroll
+        for (int k = 0; k < COLS; ++k) num[k] = fmaf(e, op[(int64_t)(j0 + j) * D + lane + k * kWave], num[k]);
+      }
     }
   }
 #pragma unroll
-  for (int k = 0; k < COLS; ++k) {
-    const float val = den > 0.f ? num[k] / den : 0.f;
-    const int64_t oi = ((int64_t)s * a.n_q + hq) * D + lane + k * kWave;
-    if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[oi] = (__bf16)val;
-    else reinterpret_cast<float*>(a.out)[oi] = val;
+  for (int k = 0; k < COLS; ++k)
+    store_out(a, ((int64_t)s * a.n_q + hq) * D + lane + k * kWave, den > 0.f ? num[k] / den : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced mode.  Flattened block index f = kvc * NB + pre[s] + j, where kvc
+// is the (KV head, head chunk) index, pre[s] the number of blocks of the
+// sequences before s, and j the block within sequence s.  Workgroup g takes
+// [g * per, (g + 1) * per) with per = ceil(F / n_wg).  Partial states go to
+// slot (g, 0) for the range's first sequence and (g, 1) for its last one;
+// split_info[s * HK + kvc] = {first workgroup, last workgroup, slot used by
+// the first} is written by the workgroup holding the pair's first block, for
+// every non-empty pair.
+// ---------------------------------------------------------------------------
+template <int KIND, int D, int GW>
+__global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeArgs a) {
+  using Ly = Lay<KIND, D, GW>;
+  __shared__ __align__(16) char smem[Ly::SMEM];
+  extern __shared__ __align__(16) int pre[];  // [batch + 1] block prefix sums (dynamic LDS)
+  __shared__ int wave_tot[kWaves];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int hk = a.n_kv * a.head_chunks;
+
+  // exclusive prefix sums of the blocks per sequence, 256 sequences per pass
+  {
+    int carry = 0;
+    for (int base = 0; base <= a.batch; base += 256) {
+      const int s = base + threadIdx.x;
+      const int nb = s < a.batch ? (clamp_len(a, s) + kBlock - 1) / kBlock : 0;
+      int incl = nb;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+      }
+      if (lane == kWave - 1) wave_tot[w] = incl;
+      __syncthreads();
+      int run = carry + incl - nb;
+      int tot = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        if (ww < w) run += wave_tot[ww];
+        tot += wave_tot[ww];
+      }
+      if (s <= a.batch) pre[s] = run;
+      carry += tot;
+      __syncthreads();  // wave_tot is rewritten by the next pass
+    }
+  }
+  const int NB = pre[a.batch];
+  const int64_t F = (int64_t)hk * NB;
+  const int64_t per = (F + a.n_wg - 1) / a.n_wg;
+  // where a flattened block sits: (kvc, s, j)
+  auto locate = [&](int64_t f, int& kvc, int& s, int& j) {
+    kvc = (int)(f / NB);
+    const int rem = (int)(f % NB);
+    int lo = 0, hi = a.batch - 1;  // largest s with pre[s] <= rem
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= rem) lo = mid;
+      else hi = mid - 1;
+    }
+    s = lo;
+    j = rem - pre[s];
+  };
+
+  WaveState<KIND, D, GW> ws;
+  {
+    const int r = blockIdx.x;
+    const int64_t f0 = min((int64_t)r * per, F);
+    const int64_t f1 = min(f0 + per, F);
+    int kvc = 0, s = 0, j = 0;
+    if (f0 < f1) locate(f0, kvc, s, j);
+    bool first_seg = true;
+    for (int64_t f = f0; f < f1;) {
+      const int L = clamp_len(a, s);
+      const int nb = (L + kBlock - 1) / kBlock;
+      const int seg = (int)min((int64_t)(nb - j), f1 - f);
+      if (seg > 0) {
+        const int kvh = kvc / a.head_chunks;
+        const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
+        load_q(a, s, h0, lane, ws);
+        reset_state(ws);
+        __syncthreads();  // the previous merge used the staging area
+        for (int b0 = 0; b0 < seg; b0 += kSegBlocks)
+          run_blocks<KIND, D, GW>(a, s, kvh, j + b0, min(kSegBlocks, seg - b0), L, w, lane,
+                                  smem + w * Ly::WAVE_BYTES, ws);
+        const bool whole = (j == 0 && seg == nb);
+        const int slot = first_seg ? 0 : 1;
+        const int rr = r;
+        merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
+          if (whole) {
+            store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, l > 0.f ? o / l : 0.f);
+          } else {
+            const int64_t pi = ((int64_t)rr * 2 + slot) * GW + h;
+            a.ws_o[pi * D + col] = o;
+            if (col == 0) {
+              a.ws_ml[pi * 2 + 0] = M;
+              a.ws_ml[pi * 2 + 1] = l;
+            }
+          }
+        });
+        if (j == 0 && threadIdx.x == 0) {
+          // this range holds the pair's first block (flattened index f)
+          int4 info;
+          info.x = r;
+          info.y = (int)((f + nb - 1) / per);
+          info.z = (f == f0) ? 0 : 1;
+          info.w = 0;
+          reinterpret_cast<int4*>(a.split_info)[(int64_t)s * hk + kvc] = info;
+        }
+        f += seg;
+        first_seg = false;
+      }
+      j = 0;
+      if (++s == a.batch) {
+        s = 0;
+        ++kvc;
+      }
+    }
   }
 }
 
+// Merge the partial states of the pairs that several workgroups share.  One
+// workgroup per (sequence, KV head chunk); pairs one workgroup covered need
+// nothing, and empty pairs get zeros here.
+template <int D, int GW>
+__global__ __launch_bounds__(256) void combine_balanced_kernel(DecodeArgs a) {
+  const int hk = a.n_kv * a.head_chunks;
+  const int kvc = blockIdx.x % hk;
+  const int s = blockIdx.x / hk;
+  const int kvh = kvc / a.head_chunks;
+  const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
+  const int L = clamp_len(a, s);
+  if (L == 0) {
+    for (int idx = threadIdx.x; idx < GW * D; idx += 256)
+      store_out(a, ((int64_t)s * a.n_q + h0 + idx / D) * D + idx % D, 0.f);
+    return;
+  }
+  const int4 info = reinterpret_cast<const int4*>(a.split_info)[(int64_t)s * hk + kvc];
+  if (info.y == info.x) return;
+  const int n = info.y - info.x + 1;
+  for (int idx = threadIdx.x; idx < GW * D; idx += 256) {
+    const int h = idx / D, col = idx % D;
+    float M = -INFINITY;
+    for (int k = 0; k < n; ++k) {
+      const int64_t pi = ((int64_t)(info.x + k) * 2 + (k == 0 ? info.z : 0)) * GW + h;
+      M = fmaxf(M, a.ws_ml[pi * 2]);
+    }
+    float den = 0.f, num = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < n; ++k) {
+        const int64_t pi = ((int64_t)(info.x + k) * 2 + (k == 0 ? info.z : 0)) * GW + h;
+        const float m = a.ws_ml[pi * 2];
+        if (m == -INFINITY) continue;
+        const float e = exp2_fast(m - M);
+        den = fmaf(e, a.ws_ml[pi * 2 + 1], den);
+        num = fmaf(e, a.ws_o[pi * D + col], num);
+      }
+    }
+    store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, den > 0.f ? num / den : 0.f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
 int decode_heads_per_wg(int group) {
   for (int g : {8, 4, 2, 1})
     if (group % g == 0) return g;
@@ -469,14 +747,81 @@ int decode_heads_per_wg(int group) {
 }
 
 int decode_chunk_blocks(int heads_per_wg) {
-  const int t = kWave / heads_per_wg;
+  const int t = kWave / heads_per_wg / 2;  // tokens per score round (d split over two lanes)
   return t > kBlock ? t / kBlock : 1;
 }
 
 template <int KIND, int D, int GW>
+static int balanced_wgs_per_cu(int batch) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_balanced_kernel<KIND, D, GW>, 256,
+                                                   decode_balanced_lds_bytes(batch)) != hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int KIND, int D>
+static int balanced_wgs_gw(int gw, int batch) {
+  switch (gw) {
+    case 8: return balanced_wgs_per_cu<KIND, D, 8>(batch);
+    case 4: return balanced_wgs_per_cu<KIND, D, 4>(batch);
+    case 2: return balanced_wgs_per_cu<KIND, D, 2>(batch);
+    default: return balanced_wgs_per_cu<KIND, D, 1>(batch);
+  }
+}
+
+template <int KIND, int D, int GW>
+static int partition_wgs_per_cu() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<KIND, D, GW>, 256, 0) != hipSuccess) return 1;
+  return n > 0 ? n : 1;
+}
+
+template <int KIND, int D>
+static int partition_wgs_gw(int gw) {
+  switch (gw) {
+    case 8: return partition_wgs_per_cu<KIND, D, 8>();
+    case 4: return partition_wgs_per_cu<KIND, D, 4>();
+    case 2: return partition_wgs_per_cu<KIND, D, 2>();
+    default: return partition_wgs_per_cu<KIND, D, 1>();
+  }
+}
+
+int decode_partition_wgs_per_cu(int kv_kind, int d, int heads_per_wg) {
+  if (kv_kind == KIND_F32)
+    return d == 64 ? partition_wgs_gw<KIND_F32, 64>(heads_per_wg) : partition_wgs_gw<KIND_F32, 128>(heads_per_wg);
+  if (kv_kind == KIND_BF16)
+    return d == 64 ? partition_wgs_gw<KIND_BF16, 64>(heads_per_wg) : partition_wgs_gw<KIND_BF16, 128>(heads_per_wg);
+  return d == 64 ? partition_wgs_gw<KIND_FP8, 64>(heads_per_wg) : partition_wgs_gw<KIND_FP8, 128>(heads_per_wg);
+}
+
+int decode_balanced_lds_bytes(int batch) { return ((batch + 1) * 4 + 255) / 256 * 256; }
+
+int decode_balanced_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch) {
+  if (kv_kind == KIND_F32)
+    return d == 64 ? balanced_wgs_gw<KIND_F32, 64>(heads_per_wg, batch)
+                   : balanced_wgs_gw<KIND_F32, 128>(heads_per_wg, batch);
+  if (kv_kind == KIND_BF16)
+    return d == 64 ? balanced_wgs_gw<KIND_BF16, 64>(heads_per_wg, batch)
+                   : balanced_wgs_gw<KIND_BF16, 128>(heads_per_wg, batch);
+  return d == 64 ? balanced_wgs_gw<KIND_FP8, 64>(heads_per_wg, batch)
+                 : balanced_wgs_gw<KIND_FP8, 128>(heads_per_wg, batch);
+}
+
+template <int KIND, int D, int GW>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_parts, a.n_kv * a.head_chunks, a.batch);
-  hipLaunchKernelGGL((decode_kernel<KIND, D, GW>), grid, dim3(256), 0, stream, a);
+  if (a.n_wg > 0) {
+    hipLaunchKernelGGL((decode_balanced_kernel<KIND, D, GW>), dim3(a.n_wg), dim3(256),
+                       decode_balanced_lds_bytes(a.batch), stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t pairs = (int64_t)a.batch * a.n_kv * a.head_chunks;
+    hipLaunchKernelGGL((combine_balanced_kernel<D, GW>), dim3((unsigned)pairs), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t wgs = (int64_t)a.n_parts * a.n_kv * a.head_chunks * a.batch;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_kernel<KIND, D, GW>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_parts == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.n_q, a.batch), dim3(64), 0, stream, a);
@@ -489,15 +834,8 @@ static hipError_t launch_gw(const DecodeArgs& a, hipStream_t stream) {
     case 8: return launch_one<KIND, D, 8>(a, stream);
     case 4: return launch_one<KIND, D, 4>(a, stream);
     case 2: return launch_one<KIND, D, 2>(a, stream);
-    default:
-      // one query head per KV head with f32 rows of 128 would need more LDS than a CU has
-      if constexpr (KIND == KIND_F32 && D == 128) return hipErrorInvalidValue;
-      else return launch_one<KIND, D, 1>(a, stream);
+    default: return launch_one<KIND, D, 1>(a, stream);
   }
-}
-
-bool decode_supported(int kv_kind, int d, int heads_per_wg) {
-  return !(kv_kind == KIND_F32 && d == 128 && heads_per_wg == 1);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream) {

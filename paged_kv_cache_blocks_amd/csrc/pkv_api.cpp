@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
@@ -45,6 +46,7 @@ bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E
 
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;
+constexpr int kBalancedSplit = -1;  // partition_tokens value that asks for the balanced split
 
 // heads ratio check, shared by the attention calls
 pkv_status check_heads(int32_t n_q, int32_t n_kv) {
@@ -53,32 +55,58 @@ pkv_status check_heads(int32_t n_q, int32_t n_kv) {
   return PKV_OK;
 }
 
-// The library's partition size: split each sequence so that the grid holds
-// several thousand workgroups, never fewer tokens than one pass of the four
-// waves, never more than 1024 tokens (long sequences keep many partitions so
-// no single workgroup dominates the tail).
-int32_t choose_partition(int32_t batch, int32_t n_kv, int32_t head_chunks, int32_t max_tokens, int32_t quantum) {
-  const int64_t pairs = (int64_t)batch * n_kv * head_chunks;
-  int64_t want = ((int64_t)max_tokens * pairs + 8191) / 8192;
-  int64_t p = ((want + 255) / 256) * 256;
-  if (p < 256) p = 256;
-  if (p > 1024) p = 1024;
-  if (p % quantum) p = ((p + quantum - 1) / quantum) * quantum;
-  return (int32_t)p;
-}
-
 struct DecodePlan {
   int32_t head_chunks;
-  int32_t part_tokens;
-  int32_t n_parts;
-  size_t ws_o_bytes;
+  int32_t part_tokens;  // partition mode
+  int32_t n_parts;      // partition mode
+  int32_t n_wg;         // balanced mode: workgroups (0 = partition mode)
+  size_t ws_o_off, ws_ml_off, split_off;
   size_t ws_bytes;
 };
 
+// Compute units of the current device and workgroups of the balanced decode
+// kernel per CU: fixed properties of the device and the code object, looked
+// up once per (device, kernel variant).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+int partition_wgs_per_cu(int kind, int d, int gw) {
+  static int cache[64][3][2][9] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int& c = cache[dev][kind][d == 128][gw];
+  if (c == 0) c = pkv::decode_partition_wgs_per_cu(kind, d, gw);
+  return c;
+}
+
+int balanced_wgs_per_cu(int kind, int d, int gw, int batch) {
+  // keyed by the batch rounded up to 256 sequences (1 KiB of prefix sums)
+  constexpr int kBuckets = pkv::kDecodeMaxBalancedBatch / 256;
+  static int cache[64][3][2][9][kBuckets] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int bucket = (batch + 255) / 256 - 1;
+  int& c = cache[dev][kind][d == 128][gw][bucket];
+  if (c == 0) c = pkv::decode_balanced_wgs_per_cu(kind, d, gw, (bucket + 1) * 256);
+  return c;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
 pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int32_t max_blocks, int32_t block_size,
-                       int32_t partition_tokens, DecodePlan* plan) {
+                       int kv_dtype, int32_t partition_tokens, DecodePlan* plan) {
   pkv_status st = check_heads(n_q, n_kv);
   if (st != PKV_OK) return st;
+  if (!valid_dtype(kv_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
   if (batch < 1 || max_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be positive");
   if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
   if (d != 64 && d != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d unsupported (64 or 128)", d);
@@ -87,23 +115,62 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
   const int quantum = 64 * pkv::decode_chunk_blocks(gw);
   const int64_t max_tokens = (int64_t)max_blocks * block_size;
   if (max_tokens > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
+  plan->head_chunks = group / gw;
+  const int64_t hk = (int64_t)n_kv * plan->head_chunks;
   int32_t part = partition_tokens;
   if (part == 0) {
-    part = choose_partition(batch, n_kv, group / gw, (int32_t)max_tokens, quantum);
+    // Library's choice.  Cut each (sequence, KV head chunk) into the fewest
+    // equal partitions of at most kMaxPartition tokens; if all of those
+    // workgroups are resident at once, use them (long per-wave streams, no
+    // cross-sequence bookkeeping).  Otherwise the balanced split, which gives
+    // every workgroup the same number of blocks whatever the length mix.
+    const int cus = device_cus();
+    if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
+    const int64_t resident = (int64_t)cus * partition_wgs_per_cu(kv_dtype, d, gw);
+    const int64_t step = quantum > 256 ? quantum : 256;
+    const int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
+    if ((int64_t)batch * hk * n_parts <= resident)
+      part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + step - 1) / step * step);
+    if (part == 0 && batch > pkv::kDecodeMaxBalancedBatch) part = kMaxPartition;
+  } else if (part == kBalancedSplit) {
+    if (batch > pkv::kDecodeMaxBalancedBatch)
+      return fail(PKV_ERR_UNSUPPORTED, "the balanced split takes at most %d sequences", pkv::kDecodeMaxBalancedBatch);
+    part = 0;
   } else if (part < 0 || part % 256 != 0 || part % quantum != 0 || part > kMaxPartition) {
-    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d must be a multiple of %d in (0, %d]", part,
+    return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d must be -1, 0 or a multiple of %d in (0, %d]", part,
                 quantum > 256 ? quantum : 256, kMaxPartition);
   }
-  plan->head_chunks = group / gw;
+  if (part == 0) {
+    // balanced mode: one equal share of all blocks per workgroup, at most as
+    // many workgroups as the device keeps resident, and at least 8 blocks each
+    const int cus = device_cus();
+    if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
+    const int64_t resident = (int64_t)cus * balanced_wgs_per_cu(kv_dtype, d, gw, batch);
+    const int64_t max_blocks_total = (int64_t)batch * hk * max_blocks;
+    int64_t n_wg = std::min(resident, (max_blocks_total + 7) / 8);
+    if (n_wg < 1) n_wg = 1;
+    plan->n_wg = (int32_t)n_wg;
+    plan->part_tokens = 0;
+    plan->n_parts = 0;
+    const size_t slots = (size_t)n_wg * 2 * gw;
+    plan->ws_o_off = 0;
+    plan->ws_ml_off = align256(slots * d * sizeof(float));
+    plan->split_off = plan->ws_ml_off + align256(slots * 2 * sizeof(float));
+    plan->ws_bytes = plan->split_off + (size_t)batch * hk * 16;
+    return PKV_OK;
+  }
+  plan->n_wg = 0;
   plan->part_tokens = part;
   plan->n_parts = (int32_t)((max_tokens + part - 1) / part);
+  plan->ws_o_off = 0;
+  plan->split_off = 0;
   if (plan->n_parts == 1) {
-    plan->ws_o_bytes = 0;
+    plan->ws_ml_off = 0;
     plan->ws_bytes = 0;
   } else {
     const size_t n = (size_t)batch * n_q * plan->n_parts;
-    plan->ws_o_bytes = ((n * d * sizeof(float)) + 255) & ~size_t(255);
-    plan->ws_bytes = plan->ws_o_bytes + n * 2 * sizeof(float);
+    plan->ws_ml_off = align256(n * d * sizeof(float));
+    plan->ws_bytes = plan->ws_ml_off + n * 2 * sizeof(float);
   }
   return PKV_OK;
 }
@@ -196,10 +263,11 @@ pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_s
 }
 
 size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
-                                       int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens) {
+                                       int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
+                                       int32_t partition_tokens) {
   DecodePlan plan;
-  if (plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, partition_tokens, &plan) !=
-      PKV_OK)
+  if (plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype,
+                  partition_tokens, &plan) != PKV_OK)
     return 0;
   return plan.ws_bytes;
 }
@@ -221,9 +289,9 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
     return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
   if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
   if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
-  DecodePlan plan;
-  st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, partition_tokens, &plan);
-  if (st != PKV_OK) return st;
+  if (batch < 1 || max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be positive");
+  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (d_head != 64 && d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d unsupported (64 or 128)", d_head);
   const bool combo_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) || (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
                         (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3FN);
   if (!combo_ok) return fail(PKV_ERR_UNSUPPORTED, "(q, kv) dtype combination (%d, %d) unsupported", q_dtype, kv_dtype);
@@ -231,11 +299,13 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   if (kv_dtype == PKV_FP8_E4M3FN && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID_ARG, "fp8 caches need k_scale and v_scale");
   const int group = n_q_heads / n_kv_heads;
-  const int gw = pkv::decode_heads_per_wg(group);
-  if (!pkv::decode_supported((int)kv_dtype, d_head, gw))
-    return fail(PKV_ERR_UNSUPPORTED, "f32 caches with d_head 128 need at least two query heads per KV head");
   if (!(scale > 0.f) || !(scale < 1e30f)) return fail(PKV_ERR_INVALID_ARG, "scale must be positive and finite");
-  if (batch > 65535 || n_kv_heads * plan.head_chunks > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  DecodePlan plan;
+  st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype,
+                   partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  if (batch > 65535 || (int64_t)batch * n_kv_heads * plan.head_chunks > 0x7fffffff)
+    return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
@@ -251,8 +321,11 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.v_scale = v_scale;
   a.block_table = block_table;
   a.seq_lens = seq_lens;
-  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(workspace) : nullptr;
-  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + plan.ws_o_bytes) : nullptr;
+  char* wsp = reinterpret_cast<char*>(workspace);
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(wsp + plan.ws_o_off) : nullptr;
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(wsp + plan.ws_ml_off) : nullptr;
+  a.split_info = plan.n_wg ? reinterpret_cast<int*>(wsp + plan.split_off) : nullptr;
+  a.n_wg = plan.n_wg;
   a.num_blocks = num_blocks;
   a.batch = batch;
   a.max_blocks = max_blocks_per_seq;

@@ -6,6 +6,9 @@
 
 namespace pkv {
 
+// the balanced decode mode keeps per-sequence block prefix sums in LDS (4 bytes each)
+constexpr int kDecodeMaxBalancedBatch = 4096;
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -17,6 +20,9 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_o;    // [batch][n_q][n_parts][d] partial outputs (unnormalised)
   float* ws_ml;   // [batch][n_q][n_parts][2] running max (log2 units) and sum
+                  // (balanced mode: [n_wg][2 slots][heads per workgroup][d] and [...][2])
+  int* split_info;  // balanced mode: int4 per (sequence, KV head chunk)
+  int32_t n_wg;     // balanced mode: workgroups (0 = partition mode)
   int64_t num_blocks;
   int32_t batch;
   int32_t max_blocks;
@@ -33,7 +39,9 @@ struct DecodeArgs {
 // decode: kv_kind 0 f32 / 1 bf16 / 2 fp8; returns hipSuccess or the launch error
 int decode_heads_per_wg(int group);
 int decode_chunk_blocks(int heads_per_wg);
-bool decode_supported(int kv_kind, int d, int heads_per_wg);
+int decode_partition_wgs_per_cu(int kv_kind, int d, int heads_per_wg);
+int decode_balanced_lds_bytes(int batch);  // dynamic LDS of the balanced kernel
+int decode_balanced_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch);
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,

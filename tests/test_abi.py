@@ -77,22 +77,22 @@ def test_decode_validation_before_launch(pkv):
     assert _decode(lib, bs=32) == pkv.ERR_UNSUPPORTED
     assert _decode(lib, q_dtype=0) == pkv.ERR_UNSUPPORTED          # f32 q with bf16 KV
     assert _decode(lib, kv_dtype=2) == pkv.ERR_INVALID_ARG         # fp8 without scales
-    assert _decode(lib, kv_dtype=0, q_dtype=0, n_q=2, n_kv=2) == pkv.ERR_UNSUPPORTED  # f32, d128, one head per KV head
     assert _decode(lib, scale=0.0) == pkv.ERR_INVALID_ARG
     assert _decode(lib, part=100) == pkv.ERR_INVALID_ARG
     # 8 blocks * 16 = 128 tokens -> a single partition, no workspace; 4096-token tables need one
-    need = pkv.paged_attn_decode_workspace(2, 8, 2, 128, 256, 16, 256)
+    need = pkv.paged_attn_decode_workspace(2, 8, 2, 128, 256, 16, pkv.BF16, 256)
     assert need > 0
     assert _decode(lib, max_blocks=256, part=256, ws=0x1000, ws_n=need - 1) == pkv.ERR_WORKSPACE
     assert _decode(lib, max_blocks=256, part=256, ws=0x1001, ws_n=need) == pkv.ERR_INVALID_ARG  # misaligned
 
 
 def test_decode_workspace_sizes(pkv):
-    # one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
-    assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 7, 16, 0) == 0
+    # partition mode: one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
+    assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 4, 16, pkv.BF16, 256) == 0
     n = 64 * 32 * 8
-    assert pkv.paged_attn_decode_workspace(64, 32, 8, 128, 128, 16, 256) == ((n * 128 * 4 + 255) // 256) * 256 + n * 8
-    assert pkv.paged_attn_decode_workspace(2, 6, 4, 64, 7, 16, 0) == 0  # invalid -> 0
+    assert pkv.paged_attn_decode_workspace(64, 32, 8, 128, 128, 16, pkv.BF16, 256) == \
+        ((n * 128 * 4 + 255) // 256) * 256 + n * 8
+    assert pkv.paged_attn_decode_workspace(2, 6, 4, 64, 7, 16, pkv.BF16, 256) == 0  # invalid -> 0
 
 
 def test_other_entry_points_validate(pkv):

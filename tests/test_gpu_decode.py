@@ -39,15 +39,17 @@ def test_config1_tiny_fp32(pkv):
 RAGGED = [1, 2, 15, 16, 17, 31, 33, 64, 65, 255, 256, 257, 700, 1031]
 
 
+BALANCED = -1  # partition_tokens value that asks for the balanced split
+
+
+@pytest.mark.parametrize("split", [0, BALANCED])
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "f32"])
 @pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8), (16, 16), (8, 1), (12, 6), (32, 2)])
 @pytest.mark.parametrize("d", [64, 128])
-def test_ragged_shapes(pkv, kind, n_q, n_kv, d):
-    if kind == "f32" and d == 128 and n_q == n_kv:
-        pytest.skip("f32 rows of 128 with one query head per KV head are not supported (LDS)")
+def test_ragged_shapes(pkv, kind, n_q, n_kv, d, split):
     c = synth.make_decode_case(config=300, layer=n_q * 7 + n_kv + d, n_q=n_q, n_kv=n_kv, d=d, seq_lens=RAGGED,
                                kv_dtype=kind, num_blocks=sum(synth.blocks_for(L) for L in RAGGED) + 7)
-    _check(pkv, c)
+    _check(pkv, c, partition_tokens=split)
 
 
 @pytest.mark.parametrize("part", [256, 512, 1024, 4096])
@@ -126,3 +128,29 @@ def test_max_length_sequence(pkv):
     c = synth.make_decode_case(config=305, layer=0, n_q=16, n_kv=2, d=128, seq_lens=[8192, 8191], kv_dtype="bf16")
     assert c.block_table.shape[1] * 16 == 8192
     _check(pkv, c)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_balanced_split_deterministic_and_edges(pkv, kind):
+    """The balanced split on a length mix with empty, one-token and long
+    sequences: matches the oracle, repeats bit for bit, and agrees with a
+    fixed-partition run and the library's choice within tolerance."""
+    lens = [0, 1, 3000, 16, 0, 17, 9000, 5, 2048, 1, 700]
+    c = synth.make_decode_case(config=306, layer=0, n_q=64, n_kv=8, d=128, seq_lens=lens, kv_dtype=kind)
+    t = upload_decode(c)
+    got, want = _check(pkv, c, partition_tokens=BALANCED)
+    assert np.array_equal(got, run_decode(pkv, c, t=t, partition_tokens=BALANCED))
+    assert np.max(np.abs(run_decode(pkv, c, t=t) - want)) <= TOL[kind]
+    fixed = run_decode(pkv, c, t=t, partition_tokens=1024)
+    assert np.max(np.abs(fixed - want)) <= TOL[kind]
+
+
+@pytest.mark.parametrize("kind", ["fp8", "bf16"])
+@pytest.mark.parametrize("n_q,n_kv", [(8, 8), (32, 8), (16, 1)])
+def test_ranges_ending_mid_sequence(pkv, kind, n_q, n_kv):
+    """Single short sequences whose blocks are cut across workgroups at odd
+    block offsets (the balanced split gives each workgroup 8 blocks)."""
+    for lens in ([37], [33], [300], [49, 3, 81]):
+        c = synth.make_decode_case(config=307, layer=len(lens), n_q=n_q, n_kv=n_kv, d=128, seq_lens=lens,
+                                   kv_dtype=kind)
+        _check(pkv, c, partition_tokens=BALANCED)
