@@ -1,13 +1,13 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2|c3|c4|c1|c5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole hot path over one batch, on inputs already
 resident in HBM:
-  * decode workloads (c1-c4): slot indexing for the batch's current token,
+  * decode workloads: slot indexing for the batch's current token,
     then for every layer kv_append of that token's K/V rows followed by paged
     decode attention (split-K partitions + combine);
-  * prefill workload (c5): slot indexing of the chunk, kv_append of its 8,192
+  * prefill workload: slot indexing of the chunk, kv_append of its 8,192
     new rows, chunked-prefill attention.
 The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
 8 KV heads, d 128, lengths uniform in [1024, 2048], 32 layers, bf16 KV).
@@ -38,8 +38,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) and tokens/s per layer"
 
+# workload name -> synth workload id (the id also namespaces the seeds)
 WORKLOADS = {
-    "c1": 1, "c2": 2, "c3": 3, "c4": 4, "c5": 5,
+    "tiny-f32": 1,            # batch 2, 8q/2kv, d 64, lengths {37, 100}, f32, 1 layer
+    "llama8b-bf16": 2,        # batch 64, 32q/8kv, d 128, lengths U[1024, 2048], bf16, 32 layers
+    "llama70b-32k-bf16": 3,   # batch 8, 64q/8kv, d 128, lengths 32768, bf16, 80 layers
+    "llama70b-fp8-mix": 4,    # batch 256, 64q/8kv, d 128, log-normal lengths, fp8 E4M3, 16 layers
+    "prefill-chunk-bf16": 5,  # 16 x 512 new tokens over contexts U[0, 8192], 32q/8kv, d 128, bf16
 }
 
 
@@ -145,6 +150,8 @@ class DecodeWorkload:
         ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
                                              pkv.dtype_code(self.k[0]))
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.plan = pkv.paged_attn_decode_plan(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
+                                               pkv.dtype_code(self.k[0]))
         self.scale = synth.softmax_scale(self.d)
         torch.cuda.synchronize()
         kvb = synth.ELEM_BYTES[self.kind]
@@ -169,6 +176,17 @@ class DecodeWorkload:
             self.decode_call(layer)
             if events is not None:
                 events[layer][1].record()
+
+    def kernel_desc(self):
+        p = self.plan
+        if p["split"] == "balanced":
+            k = f"decode_balanced_kernel ({p['workgroups']} workgroups, equal block shares) + combine_balanced_kernel"
+        else:
+            k = (f"decode_kernel ({p['n_parts']} partition(s) of {p['partition_tokens']} tokens per (sequence, KV "
+                 f"head), {p['workgroups']} workgroups)")
+            if p["merge_pass"]:
+                k += " + combine_kernel"
+        return k + "; timed per decode call"
 
     def describe(self):
         return {"workload": self.name, "batch": self.batch, "n_q_heads": self.n_q, "n_kv_heads": self.n_kv,
@@ -280,6 +298,8 @@ def cpu_baseline(w: DecodeWorkload, sample_layers: int):
         t0 = time.perf_counter()
         res = pool.map(_oracle_task, tasks, chunksize=max(1, len(tasks) // (workers * 4)))
         dt = time.perf_counter() - t0
+        pool.close()  # let the workers exit on their own rather than be terminated
+        pool.join()
     err = 0.0
     for layer, s, o in res:
         err = max(err, float(np.max(np.abs(gpu[layer][s] - o))))
@@ -331,7 +351,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="llama8b-bf16", choices=list(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling only)")
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -407,7 +427,7 @@ def main():
            "tokens_per_s_per_layer": round(w.batch / (wall / args.steps / w.layers), 1),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                        "kernel": "decode_kernel + combine_kernel (one decode call)",
+                        "kernel": w.kernel_desc(),
                         "avg_call_us": round(avg_call_s * 1e6, 3), "bytes_per_call": w.layer_bytes}}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:

@@ -171,6 +171,18 @@ size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t
                                        int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
                                        int32_t partition_tokens);
 
+/* How the decode call with these arguments splits its work on the current
+ * device (partition_tokens as for pkv_paged_attn_decode_partitioned).  info:
+ * (host) int32[6], filled with {split: 0 fixed partitions / 1 balanced,
+ * partition tokens (0 when balanced), partitions per (sequence, KV head)
+ * (0 when balanced), workgroups of the split kernel, 1 if a merge pass
+ * follows else 0, query heads per workgroup}.  Errors as for the decode
+ * call's argument checks; PKV_ERR_HIP when the split needs a device and none
+ * is present. */
+pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                      int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
+                                      int32_t partition_tokens, int32_t* info);
+
 /* Chunked prefill attention: each sequence s brings q_len = cu_q_lens[s+1] -
  * cu_q_lens[s] new query tokens at absolute positions context_lens[s] + i.
  * With causal = 1, query i attends keys 0 .. context_lens[s] + i; with

@@ -41,6 +41,7 @@ _SIGS = {
                                            _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp],
                                           ctypes.c_int),
     "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32], _sz),
+    "pkv_paged_attn_decode_plan": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_chunk": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                                       ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                       _sz, _vp], ctypes.c_int),
@@ -169,6 +170,16 @@ def check_tables(block_table, seq_lens, num_blocks: int, block_size: int = 16, s
     _check(load().pkv_check_tables(_ptr(block_table), block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
                                 num_blocks, block_size, _ptr(err), _stream(stream)))
     return int(err.item())
+
+
+def paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
+                           kv_dtype: int = BF16, partition_tokens=0) -> dict:
+    """How the decode call splits its work on the current device."""
+    info = (ctypes.c_int32 * 6)()
+    _check(load().pkv_paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size,
+                                             kv_dtype, partition_tokens, ctypes.cast(info, ctypes.c_void_p)))
+    return {"split": "balanced" if info[0] else "partitions", "partition_tokens": info[1], "n_parts": info[2],
+            "workgroups": info[3], "merge_pass": bool(info[4]), "heads_per_workgroup": info[5]}
 
 
 def paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,

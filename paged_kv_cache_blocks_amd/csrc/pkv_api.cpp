@@ -272,6 +272,24 @@ size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t
   return plan.ws_bytes;
 }
 
+pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                      int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
+                                      int32_t partition_tokens, int32_t* info) {
+  if (!info) return fail(PKV_ERR_INVALID_ARG, "info is NULL");
+  DecodePlan plan;
+  pkv_status st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype,
+                              partition_tokens, &plan);
+  if (st != PKV_OK) return st;
+  const int64_t pairs = (int64_t)batch * n_kv_heads * plan.head_chunks;
+  info[0] = plan.n_wg ? 1 : 0;
+  info[1] = plan.part_tokens;
+  info[2] = plan.n_parts;
+  info[3] = plan.n_wg ? plan.n_wg : (int32_t)std::min<int64_t>(pairs * plan.n_parts, 0x7fffffff);
+  info[4] = (plan.n_wg || plan.n_parts > 1) ? 1 : 0;
+  info[5] = (n_q_heads / n_kv_heads) / plan.head_chunks;
+  return ok();
+}
+
 pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
                                              const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
                                              const float* k_scale, const float* v_scale,

@@ -119,3 +119,17 @@ def test_other_entry_points_validate(pkv):
     args = list(base); args[7] = 0
     assert pf(*args) == pkv.OK                       # no queries: no-op
     assert pkv.load().pkv_paged_attn_prefill_workspace(16, 512, 32, 128) == 0
+
+
+def test_decode_plan_argument_checks(pkv):
+    """The plan query validates like the decode call; explicit partitions are
+    planned without a device."""
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_attn_decode_plan(2, 6, 4, 64, 7, 16, pkv.BF16, 256)  # heads not a multiple
+    with pytest.raises(pkv.PkvError):
+        pkv.paged_attn_decode_plan(2, 8, 2, 64, 7, 16, pkv.BF16, 300)  # partition not a multiple of 256
+    p = pkv.paged_attn_decode_plan(3, 32, 8, 128, 256, 16, pkv.BF16, 1024)
+    assert p == {"split": "partitions", "partition_tokens": 1024, "n_parts": 4, "workgroups": 3 * 8 * 4,
+                 "merge_pass": True, "heads_per_workgroup": 4}
+    p = pkv.paged_attn_decode_plan(3, 64, 8, 128, 64, 16, pkv.FP8_E4M3FN, 1024)
+    assert p["n_parts"] == 1 and not p["merge_pass"] and p["heads_per_workgroup"] == 8

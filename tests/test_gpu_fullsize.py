@@ -22,8 +22,9 @@ def _host(t):
     return None if t is None else host_bits(t)
 
 
-@pytest.mark.parametrize("workload,layers,seqs", [("c1", 1, [0, 1]), ("c2", 2, [0, 17, 63]), ("c3", 1, [0, 5]),
-                                                  ("c4", 1, None)])
+@pytest.mark.parametrize("workload,layers,seqs", [("tiny-f32", 1, [0, 1]), ("llama8b-bf16", 2, [0, 17, 63]),
+                                                  ("llama70b-32k-bf16", 1, [0, 5]),
+                                                  ("llama70b-fp8-mix", 1, None)])
 def test_decode_fullsize_sampled(bench, workload, layers, seqs):
     note(f"full-size decode {workload}: building {layers} layer(s)")
     w = bench.DecodeWorkload(bench.WORKLOADS[workload], layers=layers)
@@ -46,7 +47,7 @@ def test_decode_fullsize_sampled(bench, workload, layers, seqs):
 
 
 def test_prefill_fullsize_sampled(bench):
-    note("full-size prefill c5")
+    note("full-size chunked prefill, 16 x 512 new tokens")
     w = bench.PrefillWorkload(5)
     w.step()
     torch.cuda.synchronize()
