@@ -149,7 +149,7 @@ class DecodeWorkload:
                     for _ in range(self.layers)]
         ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
                                              pkv.dtype_code(self.k[0]))
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
         self.plan = pkv.paged_attn_decode_plan(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
                                                pkv.dtype_code(self.k[0]))
         self.scale = synth.softmax_scale(self.d)
@@ -179,8 +179,8 @@ class DecodeWorkload:
 
     def kernel_desc(self):
         p = self.plan
-        if p["split"] == "balanced":
-            k = f"decode_balanced_kernel ({p['workgroups']} workgroups, equal block shares) + combine_balanced_kernel"
+        if p["split"] == "queue":
+            k = f"decode_queue_kernel ({p['workgroups']} workgroups claiming items) + combine_queue_kernel"
         else:
             k = (f"decode_kernel ({p['n_parts']} partition(s) of {p['partition_tokens']} tokens per (sequence, KV "
                  f"head), {p['workgroups']} workgroups)")

@@ -122,10 +122,12 @@ pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_s
  * workgroups, each keeping a running max and sum, and the pieces are merged;
  * scores never reach memory.  The split is the library's choice: fixed
  * partitions per (sequence, KV head) when equal partitions of at most 4096
- * tokens give one resident workgroup each, otherwise the balanced split, in
- * which every workgroup receives an equal share of all blocks of the batch
- * (any length mix, batch <= 4096); pkv_paged_attn_decode_partitioned picks
- * either one explicitly.
+ * tokens give one resident workgroup each, otherwise the work-queue split:
+ * each (sequence, KV head) is cut into items of equal block counts, a
+ * resident set of workgroups claims items from a counter in the workspace,
+ * and a merge pass combines the items of each sequence (any length mix,
+ * batch <= 4096).  pkv_paged_attn_decode_partitioned picks either one
+ * explicitly.
  *   q: (device) [batch][n_q_heads][d_head]; out: (device) same shape.
  *   k_cache, v_cache: (device) [num_blocks][n_kv_heads][block_size][d_head].
  *   k_scale, v_scale: (device) fp32 [num_blocks][n_kv_heads] for FP8, else NULL.
@@ -134,10 +136,14 @@ pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_s
  * Supported: d_head in {64, 128}; block_size 16; (q, kv) in {(F32, F32),
  * (BF16, BF16), (BF16, FP8_E4M3FN)}; out F32 or BF16; n_q_heads a multiple of
  * n_kv_heads.  workspace: (device) at least
- * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned; its contents
- * need no initialisation and are scratch for the call.  Calls that share one
- * workspace must be ordered (same stream).  The result is deterministic:
- * the same inputs and launch give the same bits.
+ * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned.  It must be
+ * zero-filled before its first use: the work-queue split keeps its item
+ * counter there, and every call leaves the counter at zero again, so a
+ * workspace reused call after call (graph replays included) needs no further
+ * clearing.  The rest is scratch for the call.  Calls that share one
+ * workspace must be ordered (same stream).  The result is deterministic: the
+ * same inputs and launch give the same bits, whichever workgroup ran which
+ * item.
  * Accumulation is fp32; with bf16/fp8 KV the softmax weights are rounded to
  * bf16 before the value product and the normaliser sums the same rounded
  * weights. */
@@ -152,7 +158,7 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, 
 /* Same as pkv_paged_attn_decode with an explicit split: partition_tokens > 0
  * gives fixed partitions of that many tokens per (sequence, KV head), one
  * workgroup each, and must be a multiple of 256 (of 64 * the chunk of the
- * head group) up to 4096; -1 asks for the balanced split (batch <= 4096,
+ * head group) up to 4096; -1 asks for the work-queue split (batch <= 4096,
  * else PKV_ERR_UNSUPPORTED); 0 is the library's choice.  Used to test that
  * results do not depend on the split and to tune it. */
 pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
@@ -173,9 +179,9 @@ size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t
 
 /* How the decode call with these arguments splits its work on the current
  * device (partition_tokens as for pkv_paged_attn_decode_partitioned).  info:
- * (host) int32[6], filled with {split: 0 fixed partitions / 1 balanced,
- * partition tokens (0 when balanced), partitions per (sequence, KV head)
- * (0 when balanced), workgroups of the split kernel, 1 if a merge pass
+ * (host) int32[6], filled with {split: 0 fixed partitions / 1 work queue,
+ * partition tokens (0 for the queue), partitions per (sequence, KV head)
+ * (0 for the queue), workgroups of the split kernel, 1 if a merge pass
  * follows else 0, query heads per workgroup}.  Errors as for the decode
  * call's argument checks; PKV_ERR_HIP when the split needs a device and none
  * is present. */

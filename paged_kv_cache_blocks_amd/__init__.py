@@ -178,7 +178,7 @@ def paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_
     info = (ctypes.c_int32 * 6)()
     _check(load().pkv_paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size,
                                              kv_dtype, partition_tokens, ctypes.cast(info, ctypes.c_void_p)))
-    return {"split": "balanced" if info[0] else "partitions", "partition_tokens": info[1], "n_parts": info[2],
+    return {"split": "queue" if info[0] else "partitions", "partition_tokens": info[1], "n_parts": info[2],
             "workgroups": info[3], "merge_pass": bool(info[4]), "heads_per_workgroup": info[5]}
 
 
@@ -201,7 +201,7 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
     ws_bytes = paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, block_table.shape[1], block_size,
                                            dtype_code(k_cache), partition_tokens)
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)  # the item counter starts at 0
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().pkv_paged_attn_decode_partitioned(

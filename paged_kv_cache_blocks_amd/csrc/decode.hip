@@ -28,13 +28,12 @@
 //      accumulates dot2(weight pair, value pair) in f32.
 // f32 caches take the same path with f32 rows and fma in place of dot2.
 //
-// Work split.  Balanced mode (the default): the flattened space of
-// (KV head, sequence, block) is cut into one equal contiguous range per
-// workgroup, so every CU gets the same number of blocks whatever the length
-// mix.  A workgroup writes the final output of every sequence it covers
-// whole, and partial (m, l, o) states for at most two cut sequences, which a
-// small merge kernel combines.  Partition mode: fixed-size token partitions
-// per (sequence, KV head) on a 1-D grid, then the same style of merge.
+// Work split.  Partition mode: fixed-size token partitions per (sequence,
+// KV head) on a 1-D grid, then a merge of each sequence's partitions.
+// Work-queue mode: each (sequence, KV head) is cut into items of equal block
+// counts; a resident set of workgroups takes two items each and then claims
+// the rest from a counter, so faster XCDs take more; a merge kernel combines
+// each sequence's items.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -128,66 +127,105 @@ __device__ __forceinline__ void reset_state(WaveState<KIND, D, GW>& ws) {
     for (int k = 0; k < Lay<KIND, D, GW>::COLS; ++k) ws.o[h][k] = 0.f;
 }
 
-// Blocks [blk_begin, blk_begin + nblk) (nblk <= kSegBlocks) of sequence s,
-// KV head kvh; the four waves interleave chunks.  Tokens at or past L, or past
-// the range, are masked.  Accumulates into this wave's state.
+// This wave's block ids for blocks [blk_begin, blk_begin + nblk) (nblk <=
+// kSegBlocks) of sequence s, one per lane: lane i <-> block (i % CB) of the
+// wave's chunk i / CB (= range chunk w + 4 * (i / CB)); ids outside the pool
+// are clamped into it.  fp8: the block's K and V scales ride along.
+struct BlockIds {
+  int id;
+  float ks, vs;
+};
+
 template <int KIND, int D, int GW>
-__device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int L,
-                                           int w, int lane, char* wbase, WaveState<KIND, D, GW>& ws) {
+__device__ __forceinline__ BlockIds load_ids(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int w,
+                                             int lane) {
+  constexpr int CB = Lay<KIND, D, GW>::CB;
+  BlockIds r{0, 1.f, 1.f};
+  const int pb_lane = (w + kWaves * (lane / CB)) * CB + lane % CB;
+  if (pb_lane < nblk) {
+    const int id = a.block_table[(int64_t)s * a.max_blocks + blk_begin + pb_lane];
+    r.id = min(max(id, 0), (int)(a.num_blocks - 1));
+    if constexpr (KIND == KIND_FP8) {
+      r.ks = a.k_scale[(int64_t)r.id * a.n_kv + kvh];
+      r.vs = a.v_scale[(int64_t)r.id * a.n_kv + kvh];
+    }
+  }
+  return r;
+}
+
+// Chunks of a range this wave takes (chunks go round-robin over the waves).
+template <int KIND, int D, int GW>
+__device__ __forceinline__ int wave_chunks(int nblk, int w) {
+  constexpr int CB = Lay<KIND, D, GW>::CB;
+  const int n_chunks = (nblk + CB - 1) / CB;
+  return n_chunks > w ? (n_chunks - w + kWaves - 1) / kWaves : 0;
+}
+
+// The K and V slabs of one chunk in flight (registers).
+template <int KIND, int D, int GW>
+struct SlabRegs {
+  using Ly = Lay<KIND, D, GW>;
+  typename Ly::LV bk[Ly::CB][Ly::Gm::NLK], bv[Ly::CB][Ly::Gm::NLK];
+};
+
+// Issue the 16-byte loads of the wave's chunk c (ids from load_ids).
+template <int KIND, int D, int GW>
+__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int kvh, int my_id, int c, int lane,
+                                            SlabRegs<KIND, D, GW>& r) {
   using Ly = Lay<KIND, D, GW>;
   using Gm = typename Ly::Gm;
   using LV = typename Ly::LV;
+  const char* const kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* const vc = reinterpret_cast<const char*>(a.v_cache);
+#pragma unroll
+  for (int b = 0; b < Ly::CB; ++b) {
+    const int id = __builtin_amdgcn_readlane(my_id, c * Ly::CB + b);
+    const int64_t slab = ((int64_t)id * a.n_kv + kvh) * Gm::slab_bytes;
+#pragma unroll
+    for (int i = 0; i < Gm::NLK; ++i) {
+      const int64_t off = slab + (int64_t)(i * kWave + lane) * Gm::LW;
+      r.bk[b][i] = *reinterpret_cast<const LV*>(kc + off);
+      r.bv[b][i] = *reinterpret_cast<const LV*>(vc + off);
+    }
+  }
+}
+
+// Blocks [blk_begin, blk_begin + nblk) (nblk <= kSegBlocks) of sequence s,
+// KV head kvh; the four waves interleave chunks.  Tokens at or past L, or past
+// the range, are masked.  Accumulates into this wave's state.  On entry the
+// loads of the wave's first chunk are in flight in `slabs` (if it has one).
+// after_stage() runs once the wave's last chunk is staged and the registers
+// are free (the caller may start the next range's loads there);
+// after_scores() once the last chunk's scores are done and q is free.
+template <int KIND, int D, int GW, class AfterStage, class AfterScores>
+__device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int L,
+                                           int w, int lane, char* wbase, WaveState<KIND, D, GW>& ws,
+                                           SlabRegs<KIND, D, GW>& slabs, const BlockIds& ids,
+                                           AfterStage after_stage, AfterScores after_scores) {
+  using Ly = Lay<KIND, D, GW>;
+  using Gm = typename Ly::Gm;
   constexpr bool F32P = Ly::F32P;
   constexpr int T = Ly::T, TG = Ly::TG, QS = Ly::QS, CB = Ly::CB, CT = Ly::CT, R = Ly::R, ES = Ly::ES;
   constexpr int KROW = Ly::KROW, VROW = Ly::VROW, NPAIR = Ly::NPAIR, PVL = Ly::PVL, PVG = Ly::PVG;
   constexpr int COLS = Ly::COLS, QV = Ly::QV;
 
-  const int n_chunks = (nblk + CB - 1) / CB;
-  const int n_my = n_chunks > w ? (n_chunks - w + kWaves - 1) / kWaves : 0;
+  const int n_my = wave_chunks<KIND, D, GW>(nblk, w);
   if (n_my == 0) return;
   // a chunk may extend past the range (nblk not a multiple of CB): tokens
   // there belong to another range even when the sequence goes on
   L = min(L, (blk_begin + nblk) * kBlock);
   const int sh = lane / TG, st = (lane % TG) / QS, qh = lane % QS;
-
-  // this wave's block ids, one per lane: lane i <-> block (i % CB) of the
-  // wave's chunk i / CB (= range chunk w + 4 * (i / CB))
-  const int pb_lane = (w + kWaves * (lane / CB)) * CB + lane % CB;
-  int my_id = 0;
-  float my_ks = 1.f, my_vs = 1.f;
-  if (pb_lane < nblk) {
-    const int id = a.block_table[(int64_t)s * a.max_blocks + blk_begin + pb_lane];
-    my_id = min(max(id, 0), (int)(a.num_blocks - 1));
-    if constexpr (KIND == KIND_FP8) {
-      my_ks = a.k_scale[(int64_t)my_id * a.n_kv + kvh];
-      my_vs = a.v_scale[(int64_t)my_id * a.n_kv + kvh];
-    }
-  }
+  const int my_id = ids.id;
+  const float my_ks = ids.ks, my_vs = ids.vs;
   const int tok0 = blk_begin * kBlock;  // sequence position of the range's first token
 
   char* const k_lds = wbase;
   char* const v_lds = wbase + Ly::K_BYTES;
   char* const p_lds = v_lds + Ly::V_BYTES;
   float* const a_lds = reinterpret_cast<float*>(p_lds + Ly::P_BYTES);
-  const char* const kc = reinterpret_cast<const char*>(a.k_cache);
-  const char* const vc = reinterpret_cast<const char*>(a.v_cache);
+  auto& bk = slabs.bk;
+  auto& bv = slabs.bv;
 
-  LV bk[CB][Gm::NLK], bv[CB][Gm::NLK];
-  auto issue_loads = [&](int c) {
-#pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      const int id = __builtin_amdgcn_readlane(my_id, c * CB + b);
-      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * Gm::slab_bytes;
-#pragma unroll
-      for (int i = 0; i < Gm::NLK; ++i) {
-        const int64_t off = slab + (int64_t)(i * kWave + lane) * Gm::LW;
-        bk[b][i] = *reinterpret_cast<const LV*>(kc + off);
-        bv[b][i] = *reinterpret_cast<const LV*>(vc + off);
-      }
-    }
-  };
-
-  issue_loads(0);
   for (int c = 0; c < n_my; ++c) {
     const int ct0 = (w + kWaves * c) * CT;      // first token of the chunk (range-relative)
     const int nvalid = L - (tok0 + ct0);        // tokens of the chunk that exist (may exceed CT)
@@ -276,7 +314,8 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
       }
     }
     // the registers are free again: fetch the next chunk while this one computes
-    if (c + 1 < n_my) issue_loads(c + 1);
+    if (c + 1 < n_my) issue_chunk<KIND, D, GW>(a, kvh, my_id, c + 1, lane, slabs);
+    else after_stage();
     wave_lds_sync();
 
     // ---- scores and online softmax ----
@@ -323,6 +362,7 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
       sc[r] = (tau < nvalid) ? sv : -INFINITY;
       cmax_ = fmaxf(cmax_, sc[r]);
     }
+    if (c + 1 == n_my) after_scores();
     cmax_ = group_max<TG>(cmax_);
     const float m_new = fmaxf(ws.m_run, cmax_);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -503,7 +543,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int plen = max(0, min(a.part_tokens, L - p0));
   const int nb_part = (plen + kBlock - 1) / kBlock;
   reset_state(ws);
-  run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws);
+  const BlockIds ids = load_ids<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, w, lane);
+  SlabRegs<KIND, D, GW> slabs;
+  if (wave_chunks<KIND, D, GW>(nb_part, w) > 0) issue_chunk<KIND, D, GW>(a, kvh, ids.id, 0, lane, slabs);
+  run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids,
+                          [] {}, [] {});
   merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
     const int hq = h0 + h;
     if (a.n_parts == 1) {
@@ -577,163 +621,305 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Balanced mode.  Flattened block index f = kvc * NB + pre[s] + j, where kvc
-// is the (KV head, head chunk) index, pre[s] the number of blocks of the
-// sequences before s, and j the block within sequence s.  Workgroup g takes
-// [g * per, (g + 1) * per) with per = ceil(F / n_wg).  Partial states go to
-// slot (g, 0) for the range's first sequence and (g, 1) for its last one;
-// split_info[s * HK + kvc] = {first workgroup, last workgroup, slot used by
-// the first} is written by the workgroup holding the pair's first block, for
-// every non-empty pair.
+// Work-queue mode.  Every (sequence, KV head chunk) pair is cut into items of
+// U consecutive blocks (the last one shorter), with U chosen on the device so
+// that the batch makes about items_per_wg items per workgroup.  Items are
+// numbered pair by pair: item = kvc * NI + pre[s] + j, where pre[s] counts the
+// items of the sequences before s.  Workgroup g takes items g and g + n_wg,
+// then claims further items from a counter in the workspace until none is
+// left, so workgroups on faster XCDs simply take more items.  The claim for
+// the item after next is made one item ahead, and the next item's block ids,
+// q rows and first K/V chunk are fetched while the current item finishes, so
+// switching items does not drain the loads in flight.  An item that covers a
+// whole pair writes the output; otherwise it writes its partial (m, l, o) to
+// slot `item` and the merge kernel combines the pair's consecutive items.
+// Results depend only on the item boundaries, never on which workgroup ran an
+// item: the output is deterministic.
 // ---------------------------------------------------------------------------
+constexpr int kItemsPerWg = 8;  // items per workgroup the planner asks for
+constexpr int kMinItemBlocks = 8;
+
+struct Item {
+  int kvc, s, j0, nblk;  // pair, first block, blocks
+};
+
 template <int KIND, int D, int GW>
-__global__ __launch_bounds__(256) void decode_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
   using Ly = Lay<KIND, D, GW>;
   __shared__ __align__(16) char smem[Ly::SMEM];
-  extern __shared__ __align__(16) int pre[];  // [batch + 1] block prefix sums (dynamic LDS)
-  __shared__ int wave_tot[kWaves];
+  extern __shared__ __align__(16) int pre[];  // [batch + 1] item prefix sums (dynamic LDS)
+  __shared__ int red[kWaves];
+  __shared__ int next_item;
+  // q rows of the next item, fetched at the start of the current one and
+  // parked in LDS at its end (double buffered by item parity)
+  constexpr int QB = GW * D * Ly::ES;  // bytes of q for one item's heads
+  constexpr int QN = (QB / 8 + 255) / 256;
+  __shared__ __align__(16) char q_lds[2][QB];
+  u32x2 qn[QN];
+  WaveState<KIND, D, GW> ws;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   const int hk = a.n_kv * a.head_chunks;
 
-  // exclusive prefix sums of the blocks per sequence, 256 sequences per pass
+  // block-wide sum of v over the 256 threads
+  auto block_sum = [&](int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) t += red[ww];
+    __syncthreads();
+    return t;
+  };
+  // total blocks over the batch, then the item size
+  int nb_tot = 0;
+  for (int base = 0; base < a.batch; base += 256) {
+    const int s = base + threadIdx.x;
+    nb_tot += s < a.batch ? (clamp_len(a, s) + kBlock - 1) / kBlock : 0;
+  }
+  nb_tot = block_sum(nb_tot);
+  const int64_t F = (int64_t)hk * nb_tot;
+  const int64_t want = (F + (int64_t)a.n_wg * a.items_per_wg - 1) / ((int64_t)a.n_wg * a.items_per_wg);
+  const int U = (int)min<int64_t>(max<int64_t>(want, kMinItemBlocks), kSegBlocks);
+  // exclusive prefix sums of the items per sequence, 256 sequences per pass
   {
     int carry = 0;
     for (int base = 0; base <= a.batch; base += 256) {
       const int s = base + threadIdx.x;
-      const int nb = s < a.batch ? (clamp_len(a, s) + kBlock - 1) / kBlock : 0;
-      int incl = nb;
+      const int ni = s < a.batch ? ((clamp_len(a, s) + kBlock - 1) / kBlock + U - 1) / U : 0;
+      int incl = ni;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
         const int y = __shfl_up(incl, off);
         if (lane >= off) incl += y;
       }
-      if (lane == kWave - 1) wave_tot[w] = incl;
+      if (lane == kWave - 1) red[w] = incl;
       __syncthreads();
-      int run = carry + incl - nb;
+      int run = carry + incl - ni;
       int tot = 0;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) {
-        if (ww < w) run += wave_tot[ww];
-        tot += wave_tot[ww];
+        if (ww < w) run += red[ww];
+        tot += red[ww];
       }
       if (s <= a.batch) pre[s] = run;
       carry += tot;
-      __syncthreads();  // wave_tot is rewritten by the next pass
+      __syncthreads();
     }
   }
-  const int NB = pre[a.batch];
-  const int64_t F = (int64_t)hk * NB;
-  const int64_t per = (F + a.n_wg - 1) / a.n_wg;
-  // where a flattened block sits: (kvc, s, j)
-  auto locate = [&](int64_t f, int& kvc, int& s, int& j) {
-    kvc = (int)(f / NB);
-    const int rem = (int)(f % NB);
+  const int NI = pre[a.batch];
+  const int n_items = hk * NI;
+  if (n_items > a.n_slots) return;  // cannot happen with the planner's workspace; never write past it
+  const int n_static = min(n_items, 2 * a.n_wg);
+
+  auto locate = [&](int item) {
+    Item it;
+    it.kvc = item / NI;
+    const int rem = item - it.kvc * NI;
     int lo = 0, hi = a.batch - 1;  // largest s with pre[s] <= rem
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
       if (pre[mid] <= rem) lo = mid;
       else hi = mid - 1;
     }
-    s = lo;
-    j = rem - pre[s];
+    it.s = lo;
+    it.j0 = (rem - pre[lo]) * U;
+    const int nb = (clamp_len(a, lo) + kBlock - 1) / kBlock;
+    it.nblk = min(U, nb - it.j0);
+    return it;
+  };
+  auto head0 = [&](const Item& it) { return (it.kvc / a.head_chunks) * a.group + (it.kvc % a.head_chunks) * GW; };
+  auto q_fetch = [&](const Item& it) {  // the item's GW consecutive q rows are contiguous
+    const char* src = reinterpret_cast<const char*>(a.q) + ((int64_t)it.s * a.n_q + head0(it)) * D * Ly::ES;
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (idx < QB / 8) qn[i] = *reinterpret_cast<const u32x2*>(src + idx * 8);
+    }
+  };
+  auto q_park = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < QN; ++i) {
+      const int idx = threadIdx.x + 256 * i;
+      if (idx < QB / 8) *reinterpret_cast<u32x2*>(q_lds[buf] + idx * 8) = qn[i];
+    }
+  };
+  auto q_from_lds = [&](int buf) {
+    const int sh = lane / Ly::TG, qh = lane % Ly::QS;
+    const char* row = q_lds[buf] + sh * D * Ly::ES;
+#pragma unroll
+    for (int j = 0; j < Ly::QV; ++j) ws.qv[j] = ld16(row + (qh * Ly::QV + j) * 16);
   };
 
-  WaveState<KIND, D, GW> ws;
-  {
-    const int r = blockIdx.x;
-    const int64_t f0 = min((int64_t)r * per, F);
-    const int64_t f1 = min(f0 + per, F);
-    int kvc = 0, s = 0, j = 0;
-    if (f0 < f1) locate(f0, kvc, s, j);
-    bool first_seg = true;
-    for (int64_t f = f0; f < f1;) {
-      const int L = clamp_len(a, s);
-      const int nb = (L + kBlock - 1) / kBlock;
-      const int seg = (int)min((int64_t)(nb - j), f1 - f);
-      if (seg > 0) {
-        const int kvh = kvc / a.head_chunks;
-        const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
-        load_q(a, s, h0, lane, ws);
-        reset_state(ws);
-        __syncthreads();  // the previous merge used the staging area
-        for (int b0 = 0; b0 < seg; b0 += kSegBlocks)
-          run_blocks<KIND, D, GW>(a, s, kvh, j + b0, min(kSegBlocks, seg - b0), L, w, lane,
-                                  smem + w * Ly::WAVE_BYTES, ws);
-        const bool whole = (j == 0 && seg == nb);
-        const int slot = first_seg ? 0 : 1;
-        const int rr = r;
-        merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
-          if (whole) {
-            store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, l > 0.f ? o / l : 0.f);
-          } else {
-            const int64_t pi = ((int64_t)rr * 2 + slot) * GW + h;
-            a.ws_o[pi * D + col] = o;
-            if (col == 0) {
-              a.ws_ml[pi * 2 + 0] = M;
-              a.ws_ml[pi * 2 + 1] = l;
-            }
-          }
-        });
-        if (j == 0 && threadIdx.x == 0) {
-          // this range holds the pair's first block (flattened index f)
-          int4 info;
-          info.x = r;
-          info.y = (int)((f + nb - 1) / per);
-          info.z = (f == f0) ? 0 : 1;
-          info.w = 0;
-          reinterpret_cast<int4*>(a.split_info)[(int64_t)s * hk + kvc] = info;
+  int cur = blockIdx.x;
+  if (cur >= n_items) return;
+  int parity = 0;  // item count of this workgroup, mod 2
+  int nxt = cur + a.n_wg < n_static ? cur + a.n_wg : n_items;
+  unsigned claimed = 0;
+  const unsigned n_dyn = (unsigned)(n_items - n_static);
+  if (threadIdx.x == 0 && nxt < n_items && n_dyn > 0) claimed = atomicAdd(a.dyn_counter, 1u);
+
+  SlabRegs<KIND, D, GW> slabs;
+  Item ic = locate(cur);
+  BlockIds ids_c = load_ids<KIND, D, GW>(a, ic.s, ic.kvc / a.head_chunks, ic.j0, ic.nblk, w, lane);
+  load_q(a, ic.s, head0(ic), lane, ws);
+  if (wave_chunks<KIND, D, GW>(ic.nblk, w) > 0)
+    issue_chunk<KIND, D, GW>(a, ic.kvc / a.head_chunks, ids_c.id, 0, lane, slabs);
+  Item in_{0, 0, 0, 0};
+  BlockIds ids_n{0, 1.f, 1.f};
+  if (nxt < n_items) {
+    in_ = locate(nxt);
+    ids_n = load_ids<KIND, D, GW>(a, in_.s, in_.kvc / a.head_chunks, in_.j0, in_.nblk, w, lane);
+    q_fetch(in_);
+  }
+
+  while (true) {
+    const int kvh = ic.kvc / a.head_chunks;
+    const int h0 = head0(ic);
+    const int L = clamp_len(a, ic.s);
+    const int nb = (L + kBlock - 1) / kBlock;
+    const bool have_next = nxt < n_items;
+    const int nmy_next = have_next ? wave_chunks<KIND, D, GW>(in_.nblk, w) : 0;
+    const int kvh_n = in_.kvc / a.head_chunks;
+    reset_state(ws);
+    if (wave_chunks<KIND, D, GW>(ic.nblk, w) == 0) {
+      // nothing of this item for this wave: go straight to the next one
+      if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, kvh_n, ids_n.id, 0, lane, slabs);
+    } else {
+      run_blocks<KIND, D, GW>(
+          a, ic.s, kvh, ic.j0, ic.nblk, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids_c,
+          [&] {
+            if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, kvh_n, ids_n.id, 0, lane, slabs);
+          },
+          [] {});
+    }
+    if (have_next) q_park(parity ^ 1);  // read after the merge's barriers
+    // the merge below reads the states of all four waves
+    const bool whole = (ic.j0 == 0 && ic.nblk == nb);
+    const int item = cur;
+    merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
+      if (whole) {
+        store_out(a, ((int64_t)ic.s * a.n_q + h0 + h) * D + col, l > 0.f ? o / l : 0.f);
+      } else {
+        const int64_t pi = (int64_t)item * GW + h;
+        a.ws_o[pi * D + col] = o;
+        if (col == 0) {
+          a.ws_ml[pi * 2 + 0] = M;
+          a.ws_ml[pi * 2 + 1] = l;
         }
-        f += seg;
-        first_seg = false;
       }
-      j = 0;
-      if (++s == a.batch) {
-        s = 0;
-        ++kvc;
-      }
+    });
+    if (ic.j0 == 0 && threadIdx.x == 0) {
+      int4 info;
+      info.x = cur;
+      info.y = cur + (nb + U - 1) / U - 1;  // the pair's items are consecutive
+      info.z = 0;
+      info.w = 0;
+      reinterpret_cast<int4*>(a.split_info)[(int64_t)ic.s * hk + ic.kvc] = info;
+    }
+    if (!have_next) break;
+    // rotate: the claimed item becomes the one after next
+    if (threadIdx.x == 0) next_item = claimed < n_dyn ? n_static + (int)claimed : n_items;
+    __syncthreads();
+    cur = nxt;
+    ic = in_;
+    ids_c = ids_n;
+    nxt = next_item;
+    parity ^= 1;
+    q_from_lds(parity);
+    if (threadIdx.x == 0 && nxt < n_items) claimed = atomicAdd(a.dyn_counter, 1u);
+    if (nxt < n_items) {
+      in_ = locate(nxt);
+      ids_n = load_ids<KIND, D, GW>(a, in_.s, in_.kvc / a.head_chunks, in_.j0, in_.nblk, w, lane);
+      q_fetch(in_);
     }
   }
 }
 
-// Merge the partial states of the pairs that several workgroups share.  One
-// workgroup per (sequence, KV head chunk); pairs one workgroup covered need
-// nothing, and empty pairs get zeros here.
+// Merge the items of the pairs that several items cover: the rescale rule of
+// the online softmax applied to whole items.  grid = (pairs, GW / HPW): a
+// workgroup takes HPW heads of one pair; thread (k-slice, column) folds every
+// KS-th item of its column, eight items per batch of independent loads, and
+// the KS slices meet in LDS.  Empty pairs get zeros here.  Block (0, 0) also
+// rewinds the item counter for the next call (the decode kernel has finished
+// by now).
 template <int D, int GW>
-__global__ __launch_bounds__(256) void combine_balanced_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void combine_queue_kernel(DecodeArgs a, int hpw) {
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.dyn_counter = 0u;
+  constexpr int KS = 256 / D;  // threads per column
+  constexpr int NB = 8;        // items per batch of loads
+  __shared__ float red_m[KS][D], red_l[KS][D], red_o[KS][D];
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
   const int s = blockIdx.x / hk;
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int L = clamp_len(a, s);
+  const int hb = blockIdx.y * hpw;
   if (L == 0) {
-    for (int idx = threadIdx.x; idx < GW * D; idx += 256)
-      store_out(a, ((int64_t)s * a.n_q + h0 + idx / D) * D + idx % D, 0.f);
+    for (int idx = threadIdx.x; idx < hpw * D; idx += 256)
+      store_out(a, ((int64_t)s * a.n_q + h0 + hb + idx / D) * D + idx % D, 0.f);
     return;
   }
   const int4 info = reinterpret_cast<const int4*>(a.split_info)[(int64_t)s * hk + kvc];
-  if (info.y == info.x) return;
+  if (info.y <= info.x) return;
   const int n = info.y - info.x + 1;
-  for (int idx = threadIdx.x; idx < GW * D; idx += 256) {
-    const int h = idx / D, col = idx % D;
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) {
-      const int64_t pi = ((int64_t)(info.x + k) * 2 + (k == 0 ? info.z : 0)) * GW + h;
-      M = fmaxf(M, a.ws_ml[pi * 2]);
-    }
-    float den = 0.f, num = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < n; ++k) {
-        const int64_t pi = ((int64_t)(info.x + k) * 2 + (k == 0 ? info.z : 0)) * GW + h;
-        const float m = a.ws_ml[pi * 2];
-        if (m == -INFINITY) continue;
-        const float e = exp2_fast(m - M);
-        den = fmaf(e, a.ws_ml[pi * 2 + 1], den);
-        num = fmaf(e, a.ws_o[pi * D + col], num);
+  const int col = threadIdx.x % D, ks = threadIdx.x / D;
+  for (int hh = 0; hh < hpw; ++hh) {
+    const int h = hb + hh;
+    float M = -INFINITY, l = 0.f, o = 0.f;
+    for (int k0 = ks; k0 < n; k0 += KS * NB) {
+      float mk[NB], lk[NB], ok[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int k = k0 + j * KS;
+        mk[j] = -INFINITY;
+        lk[j] = ok[j] = 0.f;
+        if (k < n) {
+          const int64_t pi = (int64_t)(info.x + k) * GW + h;
+          mk[j] = a.ws_ml[pi * 2];
+          lk[j] = a.ws_ml[pi * 2 + 1];
+          ok[j] = a.ws_o[pi * D + col];
+        }
       }
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) Mb = fmaxf(Mb, mk[j]);
+      if (Mb == -INFINITY) continue;
+      const float e0 = exp2_fast(M - Mb);  // 0 while M is still -inf
+      l *= e0;
+      o *= e0;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const float e = (mk[j] == -INFINITY) ? 0.f : exp2_fast(mk[j] - Mb);
+        l = fmaf(e, lk[j], l);
+        o = fmaf(e, ok[j], o);
+      }
+      M = Mb;
     }
-    store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, den > 0.f ? num / den : 0.f);
+    red_m[ks][col] = M;
+    red_l[ks][col] = l;
+    red_o[ks][col] = o;
+    __syncthreads();
+    if (ks == 0) {
+      float Mt = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) Mt = fmaxf(Mt, red_m[j][col]);
+      float lt = 0.f, ot = 0.f;
+      if (Mt != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < KS; ++j) {
+          const float mj = red_m[j][col];
+          const float e = (mj == -INFINITY) ? 0.f : exp2_fast(mj - Mt);
+          lt = fmaf(e, red_l[j][col], lt);
+          ot = fmaf(e, red_o[j][col], ot);
+        }
+      }
+      store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, lt > 0.f ? ot / lt : 0.f);
+    }
+    __syncthreads();
   }
 }
 
@@ -752,21 +938,21 @@ int decode_chunk_blocks(int heads_per_wg) {
 }
 
 template <int KIND, int D, int GW>
-static int balanced_wgs_per_cu(int batch) {
+static int queue_wgs_per_cu(int batch) {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_balanced_kernel<KIND, D, GW>, 256,
-                                                   decode_balanced_lds_bytes(batch)) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_queue_kernel<KIND, D, GW>, 256,
+                                                   decode_queue_lds_bytes(batch)) != hipSuccess)
     return 1;
   return n > 0 ? n : 1;
 }
 
 template <int KIND, int D>
-static int balanced_wgs_gw(int gw, int batch) {
+static int queue_wgs_gw(int gw, int batch) {
   switch (gw) {
-    case 8: return balanced_wgs_per_cu<KIND, D, 8>(batch);
-    case 4: return balanced_wgs_per_cu<KIND, D, 4>(batch);
-    case 2: return balanced_wgs_per_cu<KIND, D, 2>(batch);
-    default: return balanced_wgs_per_cu<KIND, D, 1>(batch);
+    case 8: return queue_wgs_per_cu<KIND, D, 8>(batch);
+    case 4: return queue_wgs_per_cu<KIND, D, 4>(batch);
+    case 2: return queue_wgs_per_cu<KIND, D, 2>(batch);
+    default: return queue_wgs_per_cu<KIND, D, 1>(batch);
   }
 }
 
@@ -795,28 +981,32 @@ int decode_partition_wgs_per_cu(int kv_kind, int d, int heads_per_wg) {
   return d == 64 ? partition_wgs_gw<KIND_FP8, 64>(heads_per_wg) : partition_wgs_gw<KIND_FP8, 128>(heads_per_wg);
 }
 
-int decode_balanced_lds_bytes(int batch) { return ((batch + 1) * 4 + 255) / 256 * 256; }
+int decode_queue_lds_bytes(int batch) { return ((batch + 1) * 4 + 255) / 256 * 256; }
+int decode_queue_items_per_wg() { return kItemsPerWg; }
+int decode_queue_max_item_blocks() { return kSegBlocks; }
 
-int decode_balanced_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch) {
+int decode_queue_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch) {
   if (kv_kind == KIND_F32)
-    return d == 64 ? balanced_wgs_gw<KIND_F32, 64>(heads_per_wg, batch)
-                   : balanced_wgs_gw<KIND_F32, 128>(heads_per_wg, batch);
+    return d == 64 ? queue_wgs_gw<KIND_F32, 64>(heads_per_wg, batch)
+                   : queue_wgs_gw<KIND_F32, 128>(heads_per_wg, batch);
   if (kv_kind == KIND_BF16)
-    return d == 64 ? balanced_wgs_gw<KIND_BF16, 64>(heads_per_wg, batch)
-                   : balanced_wgs_gw<KIND_BF16, 128>(heads_per_wg, batch);
-  return d == 64 ? balanced_wgs_gw<KIND_FP8, 64>(heads_per_wg, batch)
-                 : balanced_wgs_gw<KIND_FP8, 128>(heads_per_wg, batch);
+    return d == 64 ? queue_wgs_gw<KIND_BF16, 64>(heads_per_wg, batch)
+                   : queue_wgs_gw<KIND_BF16, 128>(heads_per_wg, batch);
+  return d == 64 ? queue_wgs_gw<KIND_FP8, 64>(heads_per_wg, batch)
+                 : queue_wgs_gw<KIND_FP8, 128>(heads_per_wg, batch);
 }
 
 template <int KIND, int D, int GW>
 static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   if (a.n_wg > 0) {
-    hipLaunchKernelGGL((decode_balanced_kernel<KIND, D, GW>), dim3(a.n_wg), dim3(256),
-                       decode_balanced_lds_bytes(a.batch), stream, a);
+    hipLaunchKernelGGL((decode_queue_kernel<KIND, D, GW>), dim3(a.n_wg), dim3(256),
+                       decode_queue_lds_bytes(a.batch), stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t pairs = (int64_t)a.batch * a.n_kv * a.head_chunks;
-    hipLaunchKernelGGL((combine_balanced_kernel<D, GW>), dim3((unsigned)pairs), dim3(256), 0, stream, a);
+    const int hpw = GW / a.merge_splits;
+    hipLaunchKernelGGL((combine_queue_kernel<D, GW>), dim3((unsigned)pairs, (unsigned)a.merge_splits), dim3(256), 0,
+                       stream, a, hpw);
     return hipGetLastError();
   }
   const int64_t wgs = (int64_t)a.n_parts * a.n_kv * a.head_chunks * a.batch;

@@ -46,7 +46,8 @@ bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E
 
 constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;
-constexpr int kBalancedSplit = -1;  // partition_tokens value that asks for the balanced split
+constexpr int kQueueMaxWgsPerCu = 2;
+constexpr int kQueueSplit = -1;  // partition_tokens value that asks for the work-queue split
 
 // heads ratio check, shared by the attention calls
 pkv_status check_heads(int32_t n_q, int32_t n_kv) {
@@ -59,12 +60,15 @@ struct DecodePlan {
   int32_t head_chunks;
   int32_t part_tokens;  // partition mode
   int32_t n_parts;      // partition mode
-  int32_t n_wg;         // balanced mode: workgroups (0 = partition mode)
-  size_t ws_o_off, ws_ml_off, split_off;
+  int32_t n_wg;         // queue mode: workgroups (0 = partition mode)
+  int32_t merge_splits;  // queue mode: merge workgroups per pair
+  int32_t n_slots;       // queue mode: partial-state slots
+  int32_t items_per_wg;
+  size_t ws_o_off, ws_ml_off, split_off, counter_off;
   size_t ws_bytes;
 };
 
-// Compute units of the current device and workgroups of the balanced decode
+// Compute units of the current device and workgroups of the work-queue decode
 // kernel per CU: fixed properties of the device and the code object, looked
 // up once per (device, kernel variant).
 int device_cus() {
@@ -88,15 +92,15 @@ int partition_wgs_per_cu(int kind, int d, int gw) {
   return c;
 }
 
-int balanced_wgs_per_cu(int kind, int d, int gw, int batch) {
+int queue_wgs_per_cu(int kind, int d, int gw, int batch) {
   // keyed by the batch rounded up to 256 sequences (1 KiB of prefix sums)
-  constexpr int kBuckets = pkv::kDecodeMaxBalancedBatch / 256;
+  constexpr int kBuckets = pkv::kDecodeMaxQueueBatch / 256;
   static int cache[64][3][2][9][kBuckets] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int bucket = (batch + 255) / 256 - 1;
   int& c = cache[dev][kind][d == 128][gw][bucket];
-  if (c == 0) c = pkv::decode_balanced_wgs_per_cu(kind, d, gw, (bucket + 1) * 256);
+  if (c == 0) c = pkv::decode_queue_wgs_per_cu(kind, d, gw, (bucket + 1) * 256);
   return c;
 }
 
@@ -122,8 +126,9 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
     // Library's choice.  Cut each (sequence, KV head chunk) into the fewest
     // equal partitions of at most kMaxPartition tokens; if all of those
     // workgroups are resident at once, use them (long per-wave streams, no
-    // cross-sequence bookkeeping).  Otherwise the balanced split, which gives
-    // every workgroup the same number of blocks whatever the length mix.
+    // cross-sequence bookkeeping).  Otherwise the work-queue split, which
+    // keeps every workgroup busy until the batch is done whatever the length
+    // mix and however fast each XCD runs.
     const int cus = device_cus();
     if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
     const int64_t resident = (int64_t)cus * partition_wgs_per_cu(kv_dtype, d, gw);
@@ -131,35 +136,55 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
     const int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
     if ((int64_t)batch * hk * n_parts <= resident)
       part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + step - 1) / step * step);
-    if (part == 0 && batch > pkv::kDecodeMaxBalancedBatch) part = kMaxPartition;
-  } else if (part == kBalancedSplit) {
-    if (batch > pkv::kDecodeMaxBalancedBatch)
-      return fail(PKV_ERR_UNSUPPORTED, "the balanced split takes at most %d sequences", pkv::kDecodeMaxBalancedBatch);
+    if (part == 0 && batch > pkv::kDecodeMaxQueueBatch) part = kMaxPartition;
+  } else if (part == kQueueSplit) {
+    if (batch > pkv::kDecodeMaxQueueBatch)
+      return fail(PKV_ERR_UNSUPPORTED, "the work-queue split takes at most %d sequences", pkv::kDecodeMaxQueueBatch);
     part = 0;
   } else if (part < 0 || part % 256 != 0 || part % quantum != 0 || part > kMaxPartition) {
     return fail(PKV_ERR_INVALID_ARG, "partition_tokens %d must be -1, 0 or a multiple of %d in (0, %d]", part,
                 quantum > 256 ? quantum : 256, kMaxPartition);
   }
   if (part == 0) {
-    // balanced mode: one equal share of all blocks per workgroup, at most as
-    // many workgroups as the device keeps resident, and at least 8 blocks each
+    // work-queue mode: as many workgroups as the device keeps resident (at
+    // least 8 blocks each), items claimed dynamically
     const int cus = device_cus();
     if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
-    const int64_t resident = (int64_t)cus * balanced_wgs_per_cu(kv_dtype, d, gw, batch);
-    const int64_t max_blocks_total = (int64_t)batch * hk * max_blocks;
+    // at most two workgroups per CU: measured faster than three on both the
+    // 8B- and 70B-shaped decodes (more waves in flight only add contention)
+    const int occ = std::min(queue_wgs_per_cu(kv_dtype, d, gw, batch), kQueueMaxWgsPerCu);
+    const int64_t resident = (int64_t)cus * occ;
+    const int64_t pairs = (int64_t)batch * hk;
+    const int64_t max_blocks_total = pairs * max_blocks;
     int64_t n_wg = std::min(resident, (max_blocks_total + 7) / 8);
     if (n_wg < 1) n_wg = 1;
     plan->n_wg = (int32_t)n_wg;
     plan->part_tokens = 0;
     plan->n_parts = 0;
-    const size_t slots = (size_t)n_wg * 2 * gw;
+    // items <= F / U + pairs, and U >= F / (n_wg * items per wg) unless U hits
+    // its cap, so this many partial slots always suffice
+    const int64_t per_wg = pkv::decode_queue_items_per_wg();
+    plan->items_per_wg = (int32_t)per_wg;
+    const int64_t cap = pkv::decode_queue_max_item_blocks();
+    const int64_t slots = std::max(n_wg * per_wg, (max_blocks_total + cap - 1) / cap) + pairs;
+    // merge workgroups per pair: one per head when pairs hold many items
+    int splits = 1;
+    while (splits < gw && n_wg * per_wg / pairs / splits > 8) splits *= 2;
+    plan->merge_splits = splits;
+    if (slots > 0x7fffffff) return fail(PKV_ERR_UNSUPPORTED, "decode too large for the work-queue split");
+    plan->n_slots = (int32_t)slots;
     plan->ws_o_off = 0;
-    plan->ws_ml_off = align256(slots * d * sizeof(float));
-    plan->split_off = plan->ws_ml_off + align256(slots * 2 * sizeof(float));
-    plan->ws_bytes = plan->split_off + (size_t)batch * hk * 16;
+    plan->ws_ml_off = align256((size_t)slots * gw * d * sizeof(float));
+    plan->split_off = plan->ws_ml_off + align256((size_t)slots * gw * 2 * sizeof(float));
+    plan->counter_off = plan->split_off + align256((size_t)pairs * 16);
+    plan->ws_bytes = plan->counter_off + 256;
     return PKV_OK;
   }
   plan->n_wg = 0;
+  plan->merge_splits = 1;
+  plan->n_slots = 0;
+  plan->items_per_wg = 0;
+  plan->counter_off = 0;
   plan->part_tokens = part;
   plan->n_parts = (int32_t)((max_tokens + part - 1) / part);
   plan->ws_o_off = 0;
@@ -344,6 +369,10 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(wsp + plan.ws_ml_off) : nullptr;
   a.split_info = plan.n_wg ? reinterpret_cast<int*>(wsp + plan.split_off) : nullptr;
   a.n_wg = plan.n_wg;
+  a.merge_splits = plan.merge_splits;
+  a.n_slots = plan.n_slots;
+  a.items_per_wg = plan.items_per_wg;
+  a.dyn_counter = plan.n_wg ? reinterpret_cast<unsigned*>(wsp + plan.counter_off) : nullptr;
   a.num_blocks = num_blocks;
   a.batch = batch;
   a.max_blocks = max_blocks_per_seq;

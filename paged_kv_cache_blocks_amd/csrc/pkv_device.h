@@ -58,10 +58,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // four OCP E4M3FN bytes -> two packed bf16 dwords (exact: every E4M3FN value
 // is a bf16 value).  gfx950 converts the OCP encoding in hardware.
 __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-  lo = pack_bf16(a[0], a[1]);
-  hi = pack_bf16(b[0], b[1]);
+  // v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16 value,
+  // so the conversion is exact (NaN stays NaN)
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -6,8 +6,8 @@
 
 namespace pkv {
 
-// the balanced decode mode keeps per-sequence block prefix sums in LDS (4 bytes each)
-constexpr int kDecodeMaxBalancedBatch = 4096;
+// the queue decode mode keeps per-sequence item prefix sums in LDS (4 bytes each)
+constexpr int kDecodeMaxQueueBatch = 4096;
 
 struct DecodeArgs {
   void* out;
@@ -20,9 +20,13 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_o;    // [batch][n_q][n_parts][d] partial outputs (unnormalised)
   float* ws_ml;   // [batch][n_q][n_parts][2] running max (log2 units) and sum
-                  // (balanced mode: [n_wg][2 slots][heads per workgroup][d] and [...][2])
-  int* split_info;  // balanced mode: int4 per (sequence, KV head chunk)
-  int32_t n_wg;     // balanced mode: workgroups (0 = partition mode)
+                  // (queue mode: [item][heads per workgroup][d] and [...][2])
+  int* split_info;  // queue mode: int4 per (sequence, KV head chunk): first and last item
+  unsigned* dyn_counter;  // queue mode: item counter, zero before the call and rewound to zero by it
+  int32_t n_wg;     // queue mode: workgroups (0 = partition mode)
+  int32_t merge_splits;  // queue mode: merge workgroups per pair (divides the heads per workgroup)
+  int32_t n_slots;       // queue mode: partial-state slots in the workspace
+  int32_t items_per_wg;  // queue mode: items the batch is cut into per workgroup
   int64_t num_blocks;
   int32_t batch;
   int32_t max_blocks;
@@ -40,8 +44,10 @@ struct DecodeArgs {
 int decode_heads_per_wg(int group);
 int decode_chunk_blocks(int heads_per_wg);
 int decode_partition_wgs_per_cu(int kv_kind, int d, int heads_per_wg);
-int decode_balanced_lds_bytes(int batch);  // dynamic LDS of the balanced kernel
-int decode_balanced_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch);
+int decode_queue_lds_bytes(int batch);  // dynamic LDS of the queue kernel
+int decode_queue_items_per_wg();           // items the queue kernel aims for per workgroup
+int decode_queue_max_item_blocks();      // largest item the queue kernel makes
+int decode_queue_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch);
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,

@@ -39,10 +39,10 @@ def test_config1_tiny_fp32(pkv):
 RAGGED = [1, 2, 15, 16, 17, 31, 33, 64, 65, 255, 256, 257, 700, 1031]
 
 
-BALANCED = -1  # partition_tokens value that asks for the balanced split
+QUEUE = -1  # partition_tokens value that asks for the work-queue split
 
 
-@pytest.mark.parametrize("split", [0, BALANCED])
+@pytest.mark.parametrize("split", [0, QUEUE])
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "f32"])
 @pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8), (16, 16), (8, 1), (12, 6), (32, 2)])
 @pytest.mark.parametrize("d", [64, 128])
@@ -131,15 +131,16 @@ def test_max_length_sequence(pkv):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
-def test_balanced_split_deterministic_and_edges(pkv, kind):
-    """The balanced split on a length mix with empty, one-token and long
-    sequences: matches the oracle, repeats bit for bit, and agrees with a
-    fixed-partition run and the library's choice within tolerance."""
+def test_queue_split_deterministic_and_edges(pkv, kind):
+    """The work-queue split on a length mix with empty, one-token and long
+    sequences: matches the oracle, repeats bit for bit (whichever workgroup
+    claims which item), and agrees with a fixed-partition run and the
+    library's choice within tolerance."""
     lens = [0, 1, 3000, 16, 0, 17, 9000, 5, 2048, 1, 700]
     c = synth.make_decode_case(config=306, layer=0, n_q=64, n_kv=8, d=128, seq_lens=lens, kv_dtype=kind)
     t = upload_decode(c)
-    got, want = _check(pkv, c, partition_tokens=BALANCED)
-    assert np.array_equal(got, run_decode(pkv, c, t=t, partition_tokens=BALANCED))
+    got, want = _check(pkv, c, partition_tokens=QUEUE)
+    assert np.array_equal(got, run_decode(pkv, c, t=t, partition_tokens=QUEUE))
     assert np.max(np.abs(run_decode(pkv, c, t=t) - want)) <= TOL[kind]
     fixed = run_decode(pkv, c, t=t, partition_tokens=1024)
     assert np.max(np.abs(fixed - want)) <= TOL[kind]
@@ -148,9 +149,9 @@ def test_balanced_split_deterministic_and_edges(pkv, kind):
 @pytest.mark.parametrize("kind", ["fp8", "bf16"])
 @pytest.mark.parametrize("n_q,n_kv", [(8, 8), (32, 8), (16, 1)])
 def test_ranges_ending_mid_sequence(pkv, kind, n_q, n_kv):
-    """Single short sequences whose blocks are cut across workgroups at odd
-    block offsets (the balanced split gives each workgroup 8 blocks)."""
+    """Single short sequences cut into items at odd block offsets (the work
+    queue makes items of at least 8 blocks)."""
     for lens in ([37], [33], [300], [49, 3, 81]):
         c = synth.make_decode_case(config=307, layer=len(lens), n_q=n_q, n_kv=n_kv, d=128, seq_lens=lens,
                                    kv_dtype=kind)
-        _check(pkv, c, partition_tokens=BALANCED)
+        _check(pkv, c, partition_tokens=QUEUE)
