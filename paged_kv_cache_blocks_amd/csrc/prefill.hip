@@ -40,6 +40,8 @@ constexpr int V_LDS = KT * VROW;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
+
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
@@ -117,21 +119,32 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* trow = a.block_table + (int64_t)s * a.max_blocks;
   u32x4 kreg[4], vreg[4];
-  auto issue = [&](int kt) {
+  // thread piece i of a tile lies in block i of the tile (256 pieces of 16 B
+  // per block); the tile's four block ids are fetched one tile ahead of the
+  // K/V loads that use them, so no load waits on a table lookup
+  int ids[4];
+  auto fetch_ids = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = tid + 256 * i;         // piece index in the tile
-      const int b = p >> 8;                // block within the tile
-      const int lb = kt * (KT / BS) + b;   // logical block
+      const int lb = kt * (KT / BS) + i;   // logical block
       int id = 0;
       if (lb < a.max_blocks) id = trow[lb];
-      id = min(max(id, 0), (int)(a.num_blocks - 1));
-      const int64_t off = ((int64_t)id * a.n_kv + kvh) * (BS * D * 2) + (p & 255) * 16;
+      ids[i] = min(max(id, 0), (int)(a.num_blocks - 1));
+    }
+  };
+  auto issue = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t off = ((int64_t)ids[i] * a.n_kv + kvh) * (BS * D * 2) + tid * 16;
       kreg[i] = ld16(kc + off);
       vreg[i] = ld16(vc + off);
     }
   };
-  if (n_tiles > 0) issue(0);
+  if (n_tiles > 0) {
+    fetch_ids(0);
+    issue();
+    if (n_tiles > 1) fetch_ids(1);
+  }
 
   const float sl = a.scale_log2;
   for (int kt = 0; kt < n_tiles; ++kt) {
@@ -150,7 +163,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       st16(v_lds + row * VROW + col, vv);
     }
     __syncthreads();
-    if (kt + 1 < n_tiles) issue(kt + 1);
+    if (kt + 1 < n_tiles) {
+      issue();
+      if (kt + 2 < n_tiles) fetch_ids(kt + 2);
+    }
 
     // ---- S^T = K Q^T : four 16-key tiles x NT row tiles
     f32x4 st_[4][NT];
@@ -168,7 +184,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- mask, online softmax, P^T fragments
+    // ---- mask, online softmax, P^T fragments.  The running max is kept in
+    // log2 units (scale * log2 e folded in), so each weight is one FMA and one
+    // exp2; rows whose max did not move skip the rescale of their outputs.
     const bool need_mask = (a.causal && kt * KT + KT - 1 > diag0) || (kt * KT + KT > total);
     u32x4 pf[2][NT];  // B operand per 32-key step
 #pragma unroll
@@ -178,38 +196,40 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = st_[t][nt][j] * sl;
+          float v = st_[t][nt][j];
           if (need_mask) {
             const int key = kt * KT + 16 * t + 4 * g + j;
             v = (key <= row_lim[nt]) ? v : -INFINITY;
+            st_[t][nt][j] = v;
           }
-          st_[t][nt][j] = v;
           mx = fmaxf(mx, v);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx);
+      const float m_new = fmaxf(m_run[nt], mx * sl);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_fast(m_run[nt] - m_use);
       m_run[nt] = m_new;
-      float ls = 0.f;
       uint32_t pk[4][2];
+      float ls = 0.f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float p4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p4[j] = round_bf16(exp2_fast(st_[t][nt][j] - m_use));
-          ls += p4[j];
-        }
+        for (int j = 0; j < 4; ++j) p4[j] = exp2_fast(fmaf(st_[t][nt][j], sl, -m_use));
         pk[t][0] = pack_bf16(p4[0], p4[1]);
         pk[t][1] = pack_bf16(p4[2], p4[3]);
+        // the row sum takes the same bf16-rounded weights the product uses
+        ls = dot2_bf16(pk[t][0], kOnesBf16x2, ls);
+        ls = dot2_bf16(pk[t][1], kOnesBf16x2, ls);
       }
       l_run[nt] = l_run[nt] * alpha + ls;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pf[ks][nt] = u32x4{pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
+        for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
+      }
     }
 
     // ---- O^T += V^T P^T
