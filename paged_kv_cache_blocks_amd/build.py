@@ -20,6 +20,10 @@ ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 # Packed FP32 instructions are kept out of the generated code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
+# The prefill kernel keeps its MFMA accumulators in ordinary VGPRs: it needs
+# fewer than 256 registers that way, which leaves room for two waves per SIMD,
+# and the softmax reads the score tiles without accumulator-register copies.
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():
@@ -31,7 +35,7 @@ def _hipcc():
 def _compile(src):
     obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [_hipcc()] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc()] + FLAGS + EXTRA.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if noise not in l)

@@ -41,6 +41,7 @@ constexpr int V_LDS = KT * VROW;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
+constexpr float kRescaleSlack = 8.f;           // log2 units: weights stay <= 256
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -149,18 +150,23 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const float sl = a.scale_log2;
   for (int kt = 0; kt < n_tiles; ++kt) {
     __syncthreads();  // the previous tile's LDS reads are done
+    if (kt * KT + KT > total) {
+      // the sequence ends inside this tile: slots past it may hold anything
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (kt * KT + ((tid + 256 * i) >> 4) >= total) {
+          kreg[i] = u32x4{0, 0, 0, 0};
+          vreg[i] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + 256 * i;
       const int row = p >> 4;              // key row within the tile
       const int col = (p & 15) * 16;       // byte column
-      u32x4 kv = kreg[i], vv = vreg[i];
-      if (kt * KT + row >= total) {        // slots past the sequence may hold anything
-        kv = u32x4{0, 0, 0, 0};
-        vv = u32x4{0, 0, 0, 0};
-      }
-      st16(k_lds + row * KROW + col, kv);
-      st16(v_lds + row * VROW + col, vv);
+      st16(k_lds + row * KROW + col, kreg[i]);
+      st16(v_lds + row * VROW + col, vreg[i]);
     }
     __syncthreads();
     if (kt + 1 < n_tiles) {
@@ -184,9 +190,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    // ---- mask, online softmax, P^T fragments.  The running max is kept in
-    // log2 units (scale * log2 e folded in), so each weight is one FMA and one
-    // exp2; rows whose max did not move skip the rescale of their outputs.
+    // ---- mask, online softmax, P^T fragments.  The reference max m is kept
+    // in log2 units (scale * log2 e folded in), so each weight is one FMA and
+    // one exp2.  m moves only when a row's max exceeds it by more than
+    // kRescaleSlack: weights up to 2^kRescaleSlack are exact in the same way
+    // (the final division by l cancels any common reference), and the output
+    // accumulators are rescaled only on those rare moves.
     const bool need_mask = (a.causal && kt * KT + KT - 1 > diag0) || (kt * KT + KT > total);
     u32x4 pf[2][NT];  // B operand per 32-key step
 #pragma unroll
@@ -206,7 +215,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[nt], mx * sl);
+      const float mt = mx * sl;
+      const float m_new = (mt > m_run[nt] + kRescaleSlack) ? mt : m_run[nt];  // m_run = -inf takes mt
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_fast(m_run[nt] - m_use);
       m_run[nt] = m_new;
