@@ -9,7 +9,8 @@
 // the row sum waits until the end).
 //
 // Work decomposition
-//   grid = (query tiles, KV heads, sequences), 256 threads = 4 waves.
+//   1-D grid over (query tile, KV head, sequence) work items, placed so the
+//   query tiles of one (sequence, KV head) share an XCD; 256 threads = 4 waves.
 //   A workgroup owns 128 packed query rows of one sequence and one KV head:
 //   row r = (token r / G, head r % G), so the G heads that share the KV head
 //   reuse every K/V tile.  Each wave owns 32 rows (two 16-row MFMA tiles).
@@ -37,11 +38,16 @@ constexpr int KROW = D * 2 + 16;  // padded bf16 K row in LDS (A-operand reads)
 constexpr int VROW = D * 2 + 32;  // padded bf16 V row in LDS (transposing reads)
 constexpr int K_LDS = KT * KROW;
 constexpr int V_LDS = KT * VROW;
+constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 constexpr float kRescaleSlack = 8.f;           // log2 units: weights stay <= 256
+
+// Keeps a rarely taken branch a branch: without it the compiler may turn the
+// body into selects executed on every tile.
+__device__ __forceinline__ void no_if_conversion() { asm volatile("" ::: "memory"); }
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -64,11 +70,30 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int s = blockIdx.z;
-  const int kvh = blockIdx.y;
   const int G = a.group;
   const int tq = ROWS / G;              // tokens per workgroup
-  const int q0 = blockIdx.x * tq;       // first chunk token of the tile
+  // Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Id
+  // i runs on XCD i % 8; it is given query tile (i / 8) % q_tiles of pair
+  // p = ((i / 8) / q_tiles) * 8 + i % 8, pair p = (sequence p / n_kv, KV head
+  // p % n_kv).  So every query tile of a pair, all reading the same K/V
+  // tiles, runs on one XCD and shares its L2, while the pairs of a sequence
+  // spread over the XCDs and keep their loads even.  (Pair counts that are
+  // not a multiple of 8 keep the plain order.)
+  const int q_tiles = (a.max_q_len + tq - 1) / tq;
+  const int n_pairs = a.n_kv * a.num_seqs;
+  const int id = blockIdx.x;
+  int qt, pair;
+  if (n_pairs % kXcds == 0) {
+    const int j = id / kXcds;
+    qt = j % q_tiles;
+    pair = (j / q_tiles) * kXcds + id % kXcds;
+  } else {
+    qt = id % q_tiles;
+    pair = id / q_tiles;
+  }
+  const int kvh = pair % a.n_kv;
+  const int s = pair / a.n_kv;
+  const int q0 = qt * tq;               // first chunk token of the tile
   // a packed-query range outside [0, total_q) is clipped so no access leaves q or out
   const int qs = min(max(a.cu_q[s], 0), a.total_q);
   const int q_len = min(a.cu_q[s + 1], a.total_q) - qs;
@@ -150,16 +175,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const float sl = a.scale_log2;
   for (int kt = 0; kt < n_tiles; ++kt) {
     __syncthreads();  // the previous tile's LDS reads are done
-    if (kt * KT + KT > total) {
-      // the sequence ends inside this tile: slots past it may hold anything
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kt * KT + ((tid + 256 * i) >> 4) >= total) {
-          kreg[i] = u32x4{0, 0, 0, 0};
-          vreg[i] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + 256 * i;
@@ -167,6 +182,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int col = (p & 15) * 16;       // byte column
       st16(k_lds + row * KROW + col, kreg[i]);
       st16(v_lds + row * VROW + col, vreg[i]);
+    }
+    if (kt * KT + KT > total) {
+      // the sequence ends inside this tile: V rows past it may hold anything,
+      // NaN included, and their zero weights must not meet a NaN (K rows need
+      // no clearing: their scores are masked)
+      no_if_conversion();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = tid + 256 * i;
+        if (kt * KT + (p >> 4) >= total) st16(v_lds + (p >> 4) * VROW + (p & 15) * 16, u32x4{0, 0, 0, 0});
+      }
     }
     __syncthreads();
     if (kt + 1 < n_tiles) {
@@ -198,6 +224,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     // accumulators are rescaled only on those rare moves.
     const bool need_mask = (a.causal && kt * KT + KT - 1 > diag0) || (kt * KT + KT > total);
     u32x4 pf[2][NT];  // B operand per 32-key step
+    if (need_mask) {
+      no_if_conversion();
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int key = kt * KT + 16 * t + 4 * g + j;
+            st_[t][nt][j] = (key <= row_lim[nt]) ? st_[t][nt][j] : -INFINITY;
+          }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = -INFINITY;
@@ -205,13 +243,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float v = st_[t][nt][j];
-          if (need_mask) {
-            const int key = kt * KT + 16 * t + 4 * g + j;
-            v = (key <= row_lim[nt]) ? v : -INFINITY;
-            st_[t][nt][j] = v;
-          }
-          mx = fmaxf(mx, v);
+          mx = fmaxf(mx, st_[t][nt][j]);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -237,6 +269,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) pf[ks][nt] = u32x4{pk[2 * ks][0], pk[2 * ks][1], pk[2 * ks + 1][0], pk[2 * ks + 1][1]};
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+        no_if_conversion();
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) o[dt][nt] *= alpha;
       }
@@ -290,9 +323,10 @@ bool prefill_supported_group(int group) {
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream) {
   (void)d;
   const int tq = ROWS / a.group;
-  dim3 grid((a.max_q_len + tq - 1) / tq, a.n_kv, a.num_seqs);
-  if (grid.x == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, stream, a);
+  const int64_t n_work = (int64_t)((a.max_q_len + tq - 1) / tq) * a.n_kv * a.num_seqs;
+  if (n_work == 0) return hipSuccess;
+  if (n_work > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)n_work), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
