@@ -34,11 +34,20 @@ constexpr int BS = 16;          // tokens per cache block
 constexpr int KT = 64;          // keys per tile
 constexpr int ROWS = 128;       // packed query rows per workgroup
 constexpr int NT = 2;           // 16-row MFMA tiles per wave
-constexpr int KROW = D * 2 + 16;  // padded bf16 K row in LDS (A-operand reads)
-constexpr int VROW = D * 2 + 32;  // padded bf16 V row in LDS (transposing reads)
-constexpr int K_LDS = KT * KROW;
-constexpr int V_LDS = KT * VROW;
+constexpr int ROWB = D * 2;      // bytes of one bf16 K or V row
+constexpr int TILE_B = KT * ROWB;  // one K (or V) tile in LDS
+constexpr int STAGE_B = 2 * TILE_B;  // K tile then V tile
+constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
+
+// LDS layout of a tile: row r (key) holds its 16 pieces of 16 bytes with
+// piece c stored in slot c ^ (r % 16), so the 16 rows a column read touches
+// fall in 16 different slots (no bank conflicts) although rows are unpadded
+// (the direct global->LDS loads write 1 KiB of consecutive LDS each).
+__device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ (row & 15)) << 4); }
+
+typedef __attribute__((address_space(1))) const void gmem_t;
+typedef __attribute__((address_space(3))) void lmem_t;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -63,9 +72,7 @@ __device__ __forceinline__ u32x2 ds_read_tr(const char* p) {
 }  // namespace
 
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
-  __shared__ __align__(16) char smem[K_LDS + V_LDS];
-  char* const k_lds = smem;
-  char* const v_lds = smem + K_LDS;
+  __shared__ __align__(16) char smem[kStages * STAGE_B];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,64 +147,58 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     l_run[nt] = 0.f;
   }
 
-  // ---- tile loads: 256 threads x 4 pieces of 16 B for each of K and V
+  // ---- tile loads: wave w brings block w of the tile (16 keys) straight into
+  // LDS, 4 KiB of K and 4 KiB of V in four 1-KiB instructions each; its block
+  // id is fetched one tile ahead of the loads that use it
   const char* const kc = reinterpret_cast<const char*>(a.k_cache);
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* trow = a.block_table + (int64_t)s * a.max_blocks;
-  u32x4 kreg[4], vreg[4];
-  // thread piece i of a tile lies in block i of the tile (256 pieces of 16 B
-  // per block); the tile's four block ids are fetched one tile ahead of the
-  // K/V loads that use them, so no load waits on a table lookup
-  int ids[4];
-  auto fetch_ids = [&](int kt) {
+  const int n_lblocks = (kv_end + BS - 1) / BS;  // logical blocks any row of the tile sees
+  auto fetch_id = [&](int kt) {
+    const int lb = kt * (KT / BS) + w;
+    int id = -1;
+    if (lb < n_lblocks && lb < a.max_blocks) id = min(max(trow[lb], 0), (int)(a.num_blocks - 1));
+    return id;  // -1: nothing to load for this wave
+  };
+  auto issue = [&](int kt, int id) {
+    if (id < 0) return;
+    char* const stage = smem + (kt % kStages) * STAGE_B;
+    const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int lb = kt * (KT / BS) + i;   // logical block
-      int id = 0;
-      if (lb < a.max_blocks) id = trow[lb];
-      ids[i] = min(max(id, 0), (int)(a.num_blocks - 1));
+    for (int k = 0; k < 4; ++k) {
+      const int r = 4 * k + (lane >> 4);        // key row within the block
+      const int piece = (lane & 15) ^ r;        // global piece landing in slot lane % 16 (r < 16)
+      const int64_t off = slab + r * ROWB + piece * 16;
+      const int lrow = BS * w + 4 * k;          // first tile row this instruction writes
+      __builtin_amdgcn_global_load_lds((gmem_t*)(kc + off), (lmem_t*)(stage + lrow * ROWB), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gmem_t*)(vc + off), (lmem_t*)(stage + TILE_B + lrow * ROWB), 16, 0, 0);
     }
   };
-  auto issue = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t off = ((int64_t)ids[i] * a.n_kv + kvh) * (BS * D * 2) + tid * 16;
-      kreg[i] = ld16(kc + off);
-      vreg[i] = ld16(vc + off);
-    }
-  };
+  int id_next = -1;
   if (n_tiles > 0) {
-    fetch_ids(0);
-    issue();
-    if (n_tiles > 1) fetch_ids(1);
+    issue(0, fetch_id(0));
+    if (n_tiles > 1) id_next = fetch_id(1);
   }
 
   const float sl = a.scale_log2;
   for (int kt = 0; kt < n_tiles; ++kt) {
-    __syncthreads();  // the previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = tid + 256 * i;
-      const int row = p >> 4;              // key row within the tile
-      const int col = (p & 15) * 16;       // byte column
-      st16(k_lds + row * KROW + col, kreg[i]);
-      st16(v_lds + row * VROW + col, vreg[i]);
-    }
+    const char* const k_lds = smem + (kt % kStages) * STAGE_B;
+    const char* const v_lds = k_lds + TILE_B;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt have landed
     if (kt * KT + KT > total) {
-      // the sequence ends inside this tile: V rows past it may hold anything,
-      // NaN included, and their zero weights must not meet a NaN (K rows need
-      // no clearing: their scores are masked)
+      // the sequence ends inside this tile: V rows past it (and rows no load
+      // wrote) may hold anything, NaN included, and their zero weights must
+      // not meet a NaN.  K rows need no clearing: their scores are masked.
       no_if_conversion();
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i;
-        if (kt * KT + (p >> 4) >= total) st16(v_lds + (p >> 4) * VROW + (p & 15) * 16, u32x4{0, 0, 0, 0});
+      for (int idx = lane; idx < BS * 16; idx += kWave) {
+        const int r = BS * w + idx / 16;
+        if (kt * KT + r >= total) st16(const_cast<char*>(v_lds) + r * ROWB + (idx % 16) * 16, u32x4{0, 0, 0, 0});
       }
     }
-    __syncthreads();
+    __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
     if (kt + 1 < n_tiles) {
-      issue();
-      if (kt + 2 < n_tiles) fetch_ids(kt + 2);
+      issue(kt + 1, id_next);
+      if (kt + 2 < n_tiles) id_next = fetch_id(kt + 2);
     }
 
     // ---- S^T = K Q^T : four 16-key tiles x NT row tiles
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int ds = 0; ds < 4; ++ds) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const u32x4 kf = ld16(k_lds + (16 * t + n) * KROW + (32 * ds + 8 * g) * 2);
+        const u32x4 kf = ld16(k_lds + swz(16 * t + n, 4 * ds + g));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf, qf[nt][ds], st_[t][nt]);
       }
@@ -284,8 +285,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int key_b = key_a + 16;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const u32x2 lo = ds_read_tr(v_lds + key_a * VROW + (16 * dt + 4 * qq) * 2);
-        const u32x2 hi = ds_read_tr(v_lds + key_b * VROW + (16 * dt + 4 * qq) * 2);
+        const int pc = 2 * dt + (qq >> 1), half = (qq & 1) * 8;  // bytes (16 dt + 4 qq) * 2
+        const u32x2 lo = ds_read_tr(v_lds + swz(key_a, pc) + half);
+        const u32x2 hi = ds_read_tr(v_lds + swz(key_b, pc) + half);
         const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) o[dt][nt] = mfma_bf16(vf, pf[ks][nt], o[dt][nt]);
