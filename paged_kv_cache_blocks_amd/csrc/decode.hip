@@ -536,14 +536,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int p0 = part * a.part_tokens;
 
-  const int L = clamp_len(a, s);
-  if (a.n_parts > 1 && p0 >= L) return;
+  // the length, the q rows and the partition's block ids are fetched together
+  // (ids for every table entry the partition could use, whatever the length),
+  // so the first K/V loads wait on two dependent fetches, not three
+  const int nb_cap = min(a.part_tokens / kBlock, a.max_blocks - p0 / kBlock);
+  const BlockIds ids = load_ids<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_cap, w, lane);
   WaveState<KIND, D, GW> ws;
   load_q(a, s, h0, lane, ws);
+  const int L = clamp_len(a, s);
+  if (a.n_parts > 1 && p0 >= L) return;
   const int plen = max(0, min(a.part_tokens, L - p0));
   const int nb_part = (plen + kBlock - 1) / kBlock;
   reset_state(ws);
-  const BlockIds ids = load_ids<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, w, lane);
   SlabRegs<KIND, D, GW> slabs;
   if (wave_chunks<KIND, D, GW>(nb_part, w) > 0) issue_chunk<KIND, D, GW>(a, kvh, ids.id, 0, lane, slabs);
   run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids,
