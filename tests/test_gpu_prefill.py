@@ -86,3 +86,38 @@ def test_prefill_bf16_output(pkv):
     want = _oracle(p)
     got = _run(pkv, p, out_dtype=torch.bfloat16)
     assert np.max(np.abs(got - want)) <= 1e-2 + 2 ** -8 * np.max(np.abs(want))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_wide_score_range(pkv, causal):
+    """Scores whose row maxima keep climbing along the keys (q x 4, key rows
+    scaled up to 4x with position), so the running reference max moves many
+    times mid-sequence and the accumulators are rescaled on those moves."""
+    ctx = [3000, 517, 64]
+    p = synth.make_prefill_case(config=404, layer=int(causal), n_q=32, n_kv=8, d=128, context_lens=ctx,
+                                q_len=[200, 90, 64])
+    q = synth.f32_to_bf16_bits((oracle.bf16_bits_to_f64(p.q) * 4.0).astype(np.float32))
+    kc = oracle.bf16_bits_to_f64(p.k_cache)
+    for s, L in enumerate(np.asarray(ctx) + np.diff(p.cu_q_lens)):
+        for j in range(synth.blocks_for(int(L))):
+            b = p.block_table[s, j]
+            pos = j * 16 + np.arange(16)
+            kc[b] *= (1.0 + 3.0 * pos / L)[None, :, None]
+    p = dataclasses.replace(p, q=q, k_cache=synth.f32_to_bf16_bits(kc.astype(np.float32)))
+    note(f"prefill wide score range causal={causal}")
+    got = _run(pkv, p, causal)
+    want = _oracle(p, causal)
+    rep = err_report(got, want)
+    note("  " + rep)
+    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= 1e-2, rep
+
+
+def test_prefill_sequence_without_new_tokens(pkv):
+    """A sequence with no new tokens in the chunk leaves no output rows and
+    does not disturb its neighbours."""
+    p = synth.make_prefill_case(config=405, layer=0, n_q=32, n_kv=8, d=128, context_lens=[40, 300, 7],
+                                q_len=[33, 0, 20])
+    got = _run(pkv, p)
+    want = _oracle(p)
+    assert got.shape[0] == 53
+    assert np.max(np.abs(got - want)) <= 1e-2, err_report(got, want)
