@@ -155,3 +155,18 @@ def test_ranges_ending_mid_sequence(pkv, kind, n_q, n_kv):
         c = synth.make_decode_case(config=307, layer=len(lens), n_q=n_q, n_kv=n_kv, d=128, seq_lens=lens,
                                    kv_dtype=kind)
         _check(pkv, c, partition_tokens=QUEUE)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_queue_split_large_batch(pkv, kind):
+    """Batch 600 (three passes of the workgroups' per-sequence prefix sums),
+    lengths 0..160 including empty sequences, under the work-queue split and
+    the library's choice."""
+    lens = synth.rng(308, 0, synth.T_LEN).integers(0, 161, size=600).astype(np.int32)
+    lens[::97] = 0
+    c = synth.make_decode_case(config=308, layer=0, n_q=32, n_kv=8, d=128, seq_lens=lens, kv_dtype=kind)
+    t = upload_decode(c)
+    got, want = _check(pkv, c, partition_tokens=QUEUE)
+    assert np.all(got[lens == 0] == 0)
+    assert np.array_equal(got, run_decode(pkv, c, t=t, partition_tokens=QUEUE))
+    assert np.max(np.abs(run_decode(pkv, c, t=t) - want)) <= TOL[kind]
