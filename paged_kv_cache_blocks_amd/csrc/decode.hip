@@ -194,14 +194,16 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int kvh, int my
 // KV head kvh; the four waves interleave chunks.  Tokens at or past L, or past
 // the range, are masked.  Accumulates into this wave's state.  On entry the
 // loads of the wave's first chunk are in flight in `slabs` (if it has one).
+// first_staged() runs once, right after the wave's first chunk is staged;
 // after_stage() runs once the wave's last chunk is staged and the registers
 // are free (the caller may start the next range's loads there);
 // after_scores() once the last chunk's scores are done and q is free.
-template <int KIND, int D, int GW, class AfterStage, class AfterScores>
+template <int KIND, int D, int GW, class FirstStaged, class AfterStage, class AfterScores>
 __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int L,
                                            int w, int lane, char* wbase, WaveState<KIND, D, GW>& ws,
                                            SlabRegs<KIND, D, GW>& slabs, const BlockIds& ids,
-                                           AfterStage after_stage, AfterScores after_scores) {
+                                           FirstStaged first_staged, AfterStage after_stage,
+                                           AfterScores after_scores) {
   using Ly = Lay<KIND, D, GW>;
   using Gm = typename Ly::Gm;
   constexpr bool F32P = Ly::F32P;
@@ -313,6 +315,7 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
         }
       }
     }
+    if (c == 0) first_staged();
     // the registers are free again: fetch the next chunk while this one computes
     if (c + 1 < n_my) issue_chunk<KIND, D, GW>(a, kvh, my_id, c + 1, lane, slabs);
     else after_stage();
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   SlabRegs<KIND, D, GW> slabs;
   if (wave_chunks<KIND, D, GW>(nb_part, w) > 0) issue_chunk<KIND, D, GW>(a, kvh, ids.id, 0, lane, slabs);
   run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids,
-                          [] {}, [] {});
+                          [] {}, [] {}, [] {});
   merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
     const int hq = h0 + h;
     if (a.n_parts == 1) {
@@ -760,10 +763,8 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
   int cur = blockIdx.x;
   if (cur >= n_items) return;
   int parity = 0;  // item count of this workgroup, mod 2
-  int nxt = cur + a.n_wg < n_static ? cur + a.n_wg : n_items;
-  unsigned claimed = 0;
   const unsigned n_dyn = (unsigned)(n_items - n_static);
-  if (threadIdx.x == 0 && nxt < n_items && n_dyn > 0) claimed = atomicAdd(a.dyn_counter, 1u);
+  const int second = cur + a.n_wg < n_static ? cur + a.n_wg : n_items;  // static second item
 
   SlabRegs<KIND, D, GW> slabs;
   Item ic = locate(cur);
@@ -771,34 +772,49 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
   load_q(a, ic.s, head0(ic), lane, ws);
   if (wave_chunks<KIND, D, GW>(ic.nblk, w) > 0)
     issue_chunk<KIND, D, GW>(a, ic.kvc / a.head_chunks, ids_c.id, 0, lane, slabs);
-  Item in_{0, 0, 0, 0};
-  BlockIds ids_n{0, 1.f, 1.f};
-  if (nxt < n_items) {
-    in_ = locate(nxt);
-    ids_n = load_ids<KIND, D, GW>(a, in_.s, in_.kvc / a.head_chunks, in_.j0, in_.nblk, w, lane);
-    q_fetch(in_);
-  }
 
-  while (true) {
+  for (int k = 0;; ++k) {
+    // The next item: the static second one after the first, then an item
+    // claimed at the start of this one and published right after every wave
+    // has staged its first chunk of this one (a barrier each wave reaches
+    // exactly once per item), early enough to prefetch its block ids, q rows
+    // and first chunk before this item ends.
+    unsigned claimed = 0;
+    if (threadIdx.x == 0 && k >= 1 && n_dyn > 0) claimed = atomicAdd(a.dyn_counter, 1u);
+    int nxt = n_items;
+    Item in_{0, 0, 0, 0};
+    BlockIds ids_n{0, 1.f, 1.f};
+    int nmy_next = 0;
+    auto publish_next = [&] {
+      if (threadIdx.x == 0)
+        next_item = (k == 0) ? second : (claimed < n_dyn ? n_static + (int)claimed : n_items);
+      __syncthreads();
+      nxt = next_item;
+      if (nxt < n_items) {
+        in_ = locate(nxt);
+        ids_n = load_ids<KIND, D, GW>(a, in_.s, in_.kvc / a.head_chunks, in_.j0, in_.nblk, w, lane);
+        nmy_next = wave_chunks<KIND, D, GW>(in_.nblk, w);
+        q_fetch(in_);
+      }
+    };
     const int kvh = ic.kvc / a.head_chunks;
     const int h0 = head0(ic);
     const int L = clamp_len(a, ic.s);
     const int nb = (L + kBlock - 1) / kBlock;
-    const bool have_next = nxt < n_items;
-    const int nmy_next = have_next ? wave_chunks<KIND, D, GW>(in_.nblk, w) : 0;
-    const int kvh_n = in_.kvc / a.head_chunks;
     reset_state(ws);
     if (wave_chunks<KIND, D, GW>(ic.nblk, w) == 0) {
       // nothing of this item for this wave: go straight to the next one
-      if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, kvh_n, ids_n.id, 0, lane, slabs);
+      publish_next();
+      if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, in_.kvc / a.head_chunks, ids_n.id, 0, lane, slabs);
     } else {
       run_blocks<KIND, D, GW>(
-          a, ic.s, kvh, ic.j0, ic.nblk, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids_c,
+          a, ic.s, kvh, ic.j0, ic.nblk, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids_c, publish_next,
           [&] {
-            if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, kvh_n, ids_n.id, 0, lane, slabs);
+            if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, in_.kvc / a.head_chunks, ids_n.id, 0, lane, slabs);
           },
           [] {});
     }
+    const bool have_next = nxt < n_items;
     if (have_next) q_park(parity ^ 1);  // read after the merge's barriers
     // the merge below reads the states of all four waves
     const bool whole = (ic.j0 == 0 && ic.nblk == nb);
@@ -824,21 +840,11 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
       reinterpret_cast<int4*>(a.split_info)[(int64_t)ic.s * hk + ic.kvc] = info;
     }
     if (!have_next) break;
-    // rotate: the claimed item becomes the one after next
-    if (threadIdx.x == 0) next_item = claimed < n_dyn ? n_static + (int)claimed : n_items;
-    __syncthreads();
     cur = nxt;
     ic = in_;
     ids_c = ids_n;
-    nxt = next_item;
     parity ^= 1;
     q_from_lds(parity);
-    if (threadIdx.x == 0 && nxt < n_items) claimed = atomicAdd(a.dyn_counter, 1u);
-    if (nxt < n_items) {
-      in_ = locate(nxt);
-      ids_n = load_ids<KIND, D, GW>(a, in_.s, in_.kvc / a.head_chunks, in_.j0, in_.nblk, w, lane);
-      q_fetch(in_);
-    }
   }
 }
 
