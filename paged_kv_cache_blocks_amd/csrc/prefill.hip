@@ -41,10 +41,15 @@ constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
 
 // LDS layout of a tile: row r (key) holds its 16 pieces of 16 bytes with
-// piece c stored in slot c ^ (r % 16), so the 16 rows a column read touches
-// fall in 16 different slots (no bank conflicts) although rows are unpadded
-// (the direct global->LDS loads write 1 KiB of consecutive LDS each).
-__device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ (row & 15)) << 4); }
+// piece c stored in slot c ^ f(r % 16), rows unpadded (the direct
+// global->LDS loads write 1 KiB of consecutive LDS each).  f is the
+// permutation 2 (r & 7) + ((r >> 2) ^ (r >> 3)) & 1 of 0..15, chosen so that
+// both read patterns hit distinct banks: the score MFMAs read one piece of 16
+// consecutive rows (f is one-to-one, and f & 7 differs within 8 aligned
+// rows), the transposing value reads read pieces {2j, 2j + 1} of 4 (or 8)
+// aligned rows (f >> 1 differs there).
+__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
+__device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ swz_f(row & 15)) << 4); }
 
 typedef __attribute__((address_space(1))) const void gmem_t;
 typedef __attribute__((address_space(3))) void lmem_t;
@@ -167,7 +172,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int r = 4 * k + (lane >> 4);        // key row within the block
-      const int piece = (lane & 15) ^ r;        // global piece landing in slot lane % 16 (r < 16)
+      const int piece = (lane & 15) ^ swz_f(r);  // global piece landing in slot lane % 16 (r < 16)
       const int64_t off = slab + r * ROWB + piece * 16;
       const int lrow = BS * w + 4 * k;          // first tile row this instruction writes
       __builtin_amdgcn_global_load_lds((gmem_t*)(kc + off), (lmem_t*)(stage + lrow * ROWB), 16, 0, 0);
