@@ -850,17 +850,17 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
 
 // Merge the items of the pairs that several items cover: the rescale rule of
 // the online softmax applied to whole items.  grid = (pairs, GW / HPW): a
-// workgroup takes HPW heads of one pair; thread (k-slice, column) folds every
-// KS-th item of its column, eight items per batch of independent loads, and
-// the KS slices meet in LDS.  Empty pairs get zeros here.  Block (0, 0) also
-// rewinds the item counter for the next call (the decode kernel has finished
-// by now).
+// workgroup takes HPW heads of one pair, E = HPW * D output elements.  With
+// E >= 256 each thread folds all items of its elements; with fewer elements
+// KS = 256 / E threads share an element, each folding every KS-th item, and
+// meet in LDS.  Items are folded eight per batch of independent loads.  Empty
+// pairs get zeros here.  Block (0, 0) also rewinds the item counter for the
+// next call (the decode kernel has finished by now).
 template <int D, int GW>
 __global__ __launch_bounds__(256) void combine_queue_kernel(DecodeArgs a, int hpw) {
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.dyn_counter = 0u;
-  constexpr int KS = 256 / D;  // threads per column
-  constexpr int NB = 8;        // items per batch of loads
-  __shared__ float red_m[KS][D], red_l[KS][D], red_o[KS][D];
+  constexpr int NB = 8;  // items per batch of loads
+  __shared__ float red_m[256], red_l[256], red_o[256];
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
   const int s = blockIdx.x / hk;
@@ -868,17 +868,19 @@ __global__ __launch_bounds__(256) void combine_queue_kernel(DecodeArgs a, int hp
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int L = clamp_len(a, s);
   const int hb = blockIdx.y * hpw;
+  const int E = hpw * D;
   if (L == 0) {
-    for (int idx = threadIdx.x; idx < hpw * D; idx += 256)
+    for (int idx = threadIdx.x; idx < E; idx += 256)
       store_out(a, ((int64_t)s * a.n_q + h0 + hb + idx / D) * D + idx % D, 0.f);
     return;
   }
   const int4 info = reinterpret_cast<const int4*>(a.split_info)[(int64_t)s * hk + kvc];
   if (info.y <= info.x) return;
   const int n = info.y - info.x + 1;
-  const int col = threadIdx.x % D, ks = threadIdx.x / D;
-  for (int hh = 0; hh < hpw; ++hh) {
-    const int h = hb + hh;
+  const int KS = E >= 256 ? 1 : 256 / E;  // threads per element (E and 256 are powers of two)
+  const int ks = threadIdx.x / (256 / KS), e0 = threadIdx.x % (256 / KS);
+  for (int e = e0; e < E; e += 256 / KS) {
+    const int h = hb + e / D, col = e % D;
     float M = -INFINITY, l = 0.f, o = 0.f;
     for (int k0 = ks; k0 < n; k0 += KS * NB) {
       float mk[NB], lk[NB], ok[NB];
@@ -898,38 +900,41 @@ __global__ __launch_bounds__(256) void combine_queue_kernel(DecodeArgs a, int hp
 #pragma unroll
       for (int j = 0; j < NB; ++j) Mb = fmaxf(Mb, mk[j]);
       if (Mb == -INFINITY) continue;
-      const float e0 = exp2_fast(M - Mb);  // 0 while M is still -inf
-      l *= e0;
-      o *= e0;
+      const float e_old = exp2_fast(M - Mb);  // 0 while M is still -inf
+      l *= e_old;
+      o *= e_old;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const float e = (mk[j] == -INFINITY) ? 0.f : exp2_fast(mk[j] - Mb);
-        l = fmaf(e, lk[j], l);
-        o = fmaf(e, ok[j], o);
+        const float ej = (mk[j] == -INFINITY) ? 0.f : exp2_fast(mk[j] - Mb);
+        l = fmaf(ej, lk[j], l);
+        o = fmaf(ej, ok[j], o);
       }
       M = Mb;
     }
-    red_m[ks][col] = M;
-    red_l[ks][col] = l;
-    red_o[ks][col] = o;
-    __syncthreads();
-    if (ks == 0) {
-      float Mt = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < KS; ++j) Mt = fmaxf(Mt, red_m[j][col]);
-      float lt = 0.f, ot = 0.f;
-      if (Mt != -INFINITY) {
-#pragma unroll
-        for (int j = 0; j < KS; ++j) {
-          const float mj = red_m[j][col];
-          const float e = (mj == -INFINITY) ? 0.f : exp2_fast(mj - Mt);
-          lt = fmaf(e, red_l[j][col], lt);
-          ot = fmaf(e, red_o[j][col], ot);
+    const int64_t oi = ((int64_t)s * a.n_q + h0 + h) * D + col;
+    if (KS == 1) {
+      store_out(a, oi, l > 0.f ? o / l : 0.f);
+    } else {
+      // E < 256: this is the only pass of the element loop
+      red_m[threadIdx.x] = M;
+      red_l[threadIdx.x] = l;
+      red_o[threadIdx.x] = o;
+      __syncthreads();
+      if (ks == 0) {
+        float Mt = -INFINITY;
+        for (int j = 0; j < KS; ++j) Mt = fmaxf(Mt, red_m[j * E + e]);
+        float lt = 0.f, ot = 0.f;
+        if (Mt != -INFINITY) {
+          for (int j = 0; j < KS; ++j) {
+            const float mj = red_m[j * E + e];
+            const float w = (mj == -INFINITY) ? 0.f : exp2_fast(mj - Mt);
+            lt = fmaf(w, red_l[j * E + e], lt);
+            ot = fmaf(w, red_o[j * E + e], ot);
+          }
         }
+        store_out(a, oi, lt > 0.f ? ot / lt : 0.f);
       }
-      store_out(a, ((int64_t)s * a.n_q + h0 + h) * D + col, lt > 0.f ? ot / lt : 0.f);
     }
-    __syncthreads();
   }
 }
 
