@@ -39,6 +39,7 @@ constexpr int TILE_B = KT * ROWB;  // one K (or V) tile in LDS
 constexpr int STAGE_B = 2 * TILE_B;  // K tile then V tile
 constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
+constexpr int kMaxSortSeqs = 256;  // batches up to this size are ordered longest first
 
 // LDS layout of a tile: row r (key) holds its 16 pieces of 16 bytes with
 // piece c stored in slot c ^ f(r % 16), rows unpadded (the direct
@@ -84,13 +85,37 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int w = tid >> 6;
   const int G = a.group;
   const int tq = ROWS / G;              // tokens per workgroup
-  // Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Id
-  // i runs on XCD i % 8; it is given query tile (i / 8) % q_tiles of pair
-  // p = ((i / 8) / q_tiles) * 8 + i % 8, pair p = (sequence p / n_kv, KV head
-  // p % n_kv).  So every query tile of a pair, all reading the same K/V
-  // tiles, runs on one XCD and shares its L2, while the pairs of a sequence
-  // spread over the XCDs and keep their loads even.  (Pair counts that are
-  // not a multiple of 8 keep the plain order.)
+  // Work order.  Sequences are taken longest first (most keys: context plus
+  // chunk), so the long workgroups start early and short ones fill the end;
+  // within a sequence the later query tiles, which see more keys, go first.
+  // Workgroup ids go round-robin over the 8 XCDs, each with its own L2: id i
+  // runs on XCD i % 8 and takes query tile (i / 8) % q_tiles of pair
+  // p = ((i / 8) / q_tiles) * 8 + i % 8 in that order, pair p = (sequence
+  // rank p / n_kv, KV head p % n_kv).  So every query tile of a pair, all
+  // reading the same K/V tiles, runs on one XCD and shares its L2, while the
+  // pairs of a sequence spread over the XCDs and keep their loads even.
+  // (Pair counts that are not a multiple of 8 keep the XCD-blind order.)
+  __shared__ int seq_key[kMaxSortSeqs], seq_at_rank[kMaxSortSeqs];
+  const bool sorted = a.num_seqs <= kMaxSortSeqs;
+  if (sorted) {
+    const int t = threadIdx.x;
+    if (t < a.num_seqs) {
+      const int cs = min(max(a.ctx_lens[t], 0), a.max_blocks * BS);
+      const int qb = min(max(a.cu_q[t], 0), a.total_q), qe = min(max(a.cu_q[t + 1], qb), a.total_q);
+      seq_key[t] = cs + (qe - qb);
+    }
+    __syncthreads();
+    if (t < a.num_seqs) {
+      const int k = seq_key[t];
+      int rank = 0;
+      for (int u = 0; u < a.num_seqs; ++u) {
+        const int ku = seq_key[u];
+        rank += (ku > k) || (ku == k && u < t);
+      }
+      seq_at_rank[rank] = t;
+    }
+    __syncthreads();
+  }
   const int q_tiles = (a.max_q_len + tq - 1) / tq;
   const int n_pairs = a.n_kv * a.num_seqs;
   const int id = blockIdx.x;
@@ -103,8 +128,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     qt = id % q_tiles;
     pair = id / q_tiles;
   }
+  qt = q_tiles - 1 - qt;
   const int kvh = pair % a.n_kv;
-  const int s = pair / a.n_kv;
+  const int s = sorted ? seq_at_rank[pair / a.n_kv] : pair / a.n_kv;
   const int q0 = qt * tq;               // first chunk token of the tile
   // a packed-query range outside [0, total_q) is clipped so no access leaves q or out
   const int qs = min(max(a.cu_q[s], 0), a.total_q);
