@@ -4,9 +4,11 @@
 
 A step is one pass of the whole hot path over one batch, on inputs already
 resident in HBM:
-  * decode workloads: slot indexing for the batch's current token,
-    then for every layer kv_append of that token's K/V rows followed by paged
-    decode attention (split-K partitions + combine);
+  * decode workloads: slot indexing for the batch's current token, kv_append
+    of that token's K/V rows into every layer's cache, then paged decode
+    attention of every layer, back to back (each layer's append precedes its
+    attention; with no model between the layers the two orders do the same
+    work, and back-to-back calls keep launch gaps out of the decode timing);
   * prefill workload: slot indexing of the chunk, kv_append of its 8,192
     new rows, chunked-prefill attention.
 The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
@@ -14,7 +16,8 @@ The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
 
 Prints one JSON line.  `value` is achieved GB/s (algorithmic bytes / wall
 time of the K timed steps); `roofline` describes the decode call (split-K
-kernel + combine) timed with HIP events on the launch stream; `cpu_baseline`
+kernel + merge when split), timed with HIP events on the launch stream around
+each step's block of decode calls and divided by the calls; `cpu_baseline`
 times the float64 CPU oracle on a bounded sample of the same workload on the
 host cores and checks the sampled GPU outputs against it.
 """
@@ -166,16 +169,19 @@ class DecodeWorkload:
                                    self.n_q, self.n_kv, self.d, 16, self.scale, k_scale=self.ks[layer],
                                    v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws)
 
+    calls_per_event = property(lambda self: self.layers)
+
     def step(self, events=None):
         pkv = self.pkv
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
         for layer in range(self.layers):
             pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
-            if events is not None:
-                events[layer][0].record()
+        if events is not None:
+            events[0].record()
+        for layer in range(self.layers):
             self.decode_call(layer)
-            if events is not None:
-                events[layer][1].record()
+        if events is not None:
+            events[1].record()
 
     def kernel_desc(self):
         p = self.plan
@@ -186,7 +192,7 @@ class DecodeWorkload:
                  f"head), {p['workgroups']} workgroups)")
             if p["merge_pass"]:
                 k += " + combine_kernel"
-        return k + "; timed per decode call"
+        return k
 
     def describe(self):
         return {"workload": self.name, "batch": self.batch, "n_q_heads": self.n_q, "n_kv_heads": self.n_kv,
@@ -196,6 +202,8 @@ class DecodeWorkload:
 
 
 class PrefillWorkload:
+    calls_per_event = 1
+
     def __init__(self, cfg_id: int = 5):
         import torch
         import paged_kv_cache_blocks_amd as pkv
@@ -239,10 +247,10 @@ class PrefillWorkload:
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
         pkv.kv_append(self.k, self.v, self.slots, self.k_new, self.v_new)
         if events is not None:
-            events[0][0].record()
+            events[0].record()
         self.attn_call()
         if events is not None:
-            events[0][1].record()
+            events[1].record()
 
     def describe(self):
         return {"workload": self.name, "num_seqs": len(self.ctx), "q_len": self.q_len, "n_q_heads": self.n_q,
@@ -387,16 +395,14 @@ def main():
         w.step()
     torch.cuda.synchronize()
 
-    n_ev = w.layers
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(n_ev)]
-              for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         w.step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = [e0.elapsed_time(e1) for ev in events for e0, e1 in ev]
+    call_ms = [e0.elapsed_time(e1) / w.calls_per_event for e0, e1 in events]
     avg_call_s = float(np.mean(call_ms)) / 1e3
     ms_per_step = wall / args.steps * 1e3
 
@@ -428,6 +434,7 @@ def main():
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "kernel": w.kernel_desc(),
+                        "timing": f"HIP events around each step's {w.layers} back-to-back decode calls, / {w.layers}",
                         "avg_call_us": round(avg_call_s * 1e6, 3), "bytes_per_call": w.layer_bytes}}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
