@@ -52,8 +52,21 @@ constexpr int kMaxSortSeqs = 256;  // batches up to this size are ordered longes
 __device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
 __device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ swz_f(row & 15)) << 4); }
 
-typedef __attribute__((address_space(1))) const void gmem_t;
-typedef __attribute__((address_space(3))) void lmem_t;
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; the LDS base goes in M0).  Issued from inline
+// assembly on purpose: the compiler, unable to tell which LDS bytes such a
+// load writes, would otherwise wait for it before every later LDS read,
+// including reads of the other stage, and expose the load latency on every
+// tile.  The caller waits for these loads itself (vmcnt) before the barrier
+// that hands the stage to the readers.  The compiler keeps nothing in M0
+// across these statements in this kernel (checked in its assembly).
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
+  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(src)
+               : "memory", "m0");
+}
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -185,14 +198,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
   const int32_t* trow = a.block_table + (int64_t)s * a.max_blocks;
   const int n_lblocks = (kv_end + BS - 1) / BS;  // logical blocks any row of the tile sees
+  // The raw table entry is fetched one tile ahead and checked only when its
+  // loads are issued, so nothing waits on the fetch in between.
   auto fetch_id = [&](int kt) {
     const int lb = kt * (KT / BS) + w;
-    int id = -1;
-    if (lb < n_lblocks && lb < a.max_blocks) id = min(max(trow[lb], 0), (int)(a.num_blocks - 1));
-    return id;  // -1: nothing to load for this wave
+    return trow[min(lb, a.max_blocks - 1)];
   };
-  auto issue = [&](int kt, int id) {
-    if (id < 0) return;
+  auto issue = [&](int kt, int raw_id) {
+    const int lb = kt * (KT / BS) + w;
+    if (lb >= n_lblocks || lb >= a.max_blocks) return;  // nothing to load for this wave
+    const int id = min(max(raw_id, 0), (int)(a.num_blocks - 1));
     char* const stage = smem + (kt % kStages) * STAGE_B;
     const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
 #pragma unroll
@@ -201,11 +216,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int piece = (lane & 15) ^ swz_f(r);  // global piece landing in slot lane % 16 (r < 16)
       const int64_t off = slab + r * ROWB + piece * 16;
       const int lrow = BS * w + 4 * k;          // first tile row this instruction writes
-      __builtin_amdgcn_global_load_lds((gmem_t*)(kc + off), (lmem_t*)(stage + lrow * ROWB), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gmem_t*)(vc + off), (lmem_t*)(stage + TILE_B + lrow * ROWB), 16, 0, 0);
+      lds_dma16(kc + off, stage + lrow * ROWB);
+      lds_dma16(vc + off, stage + TILE_B + lrow * ROWB);
     }
   };
-  int id_next = -1;
+  int id_next = 0;
   if (n_tiles > 0) {
     issue(0, fetch_id(0));
     if (n_tiles > 1) id_next = fetch_id(1);
