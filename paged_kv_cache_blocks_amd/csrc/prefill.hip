@@ -253,14 +253,22 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) st_[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragments of the next 32-wide d step are read while this step's
+    // MFMAs run (two groups of four fragments in flight)
+    u32x4 kf[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kf[0][t] = ld16(k_lds + swz(16 * t + n, g));
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
+      if (ds + 1 < 4) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const u32x4 kf = ld16(k_lds + swz(16 * t + n, 4 * ds + g));
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf, qf[nt][ds], st_[t][nt]);
+        for (int t = 0; t < 4; ++t) kf[(ds + 1) & 1][t] = ld16(k_lds + swz(16 * t + n, 4 * (ds + 1) + g));
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf[ds & 1][t], qf[nt][ds], st_[t][nt]);
     }
 
     // ---- mask, online softmax, P^T fragments.  The reference max m is kept
