@@ -97,6 +97,32 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Exchanges across 16-lane rows without going through LDS: v_permlane16_swap
+// and v_permlane32_swap (gfx950 VALU ops) swap rows between two registers.
+// Given the same value in both, the two results of a lane are its own value and
+// that of lane ^ 16 (resp. lane ^ 32), so max or sum of the pair reduces over
+// the partner lanes in every lane.
+__device__ __forceinline__ float max_xor16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Order LDS traffic between lanes of one wave: LDS instructions of a wave
 // execute in order, so a compiler-level barrier with wavefront-scope fences is
 // enough for one lane to read what another lane of the same wave wrote.

@@ -300,8 +300,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int j = 0; j < 4; ++j) {
           mx = fmaxf(mx, st_[t][nt][j]);
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_xor32(max_xor16(mx));
       const float mt = mx * sl;
       const float m_new = (mt > m_run[nt] + kRescaleSlack) ? mt : m_run[nt];  // m_run = -inf takes mt
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -353,8 +352,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float l = l_run[nt];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    l = sum_xor32(sum_xor16(l));
     if (row_tok[nt] >= q_len) continue;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t obase = ((int64_t)(qs + row_tok[nt]) * a.n_q + row_head[nt]) * D;
