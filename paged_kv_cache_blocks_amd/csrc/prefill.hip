@@ -53,19 +53,23 @@ __device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2)
 __device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ swz_f(row & 15)) << 4); }
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4; the LDS base goes in M0).  Issued from inline
-// assembly on purpose: the compiler, unable to tell which LDS bytes such a
-// load writes, would otherwise wait for it before every later LDS read,
-// including reads of the other stage, and expose the load latency on every
-// tile.  The caller waits for these loads itself (vmcnt) before the barrier
-// that hands the stage to the readers.  The compiler keeps nothing in M0
-// across these statements in this kernel (checked in its assembly).
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds) {
-  const unsigned base = (unsigned)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+// (global_load_lds_dwordx4, scalar-base form: address = base + off, with the
+// base and the LDS address the same in every lane and the LDS address in M0).
+// Issued from inline assembly on purpose: the compiler, unable to tell which
+// LDS bytes such a load writes, would otherwise wait for it before every later
+// LDS read, including reads of the other stage, and expose the load latency on
+// every tile.  The caller waits for these loads itself (vmcnt) before the
+// barrier that hands the stage to the readers.  The compiler keeps nothing in
+// M0 across these statements in this kernel (checked in its assembly).
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(src)
+               : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int G = a.group;
   const int tq = ROWS / G;              // tokens per workgroup
   // Work order.  Sequences are taken longest first (most keys: context plus
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   }
   qt = q_tiles - 1 - qt;
   const int kvh = pair % a.n_kv;
-  const int s = sorted ? seq_at_rank[pair / a.n_kv] : pair / a.n_kv;
+  const int s = __builtin_amdgcn_readfirstlane(sorted ? seq_at_rank[pair / a.n_kv] : pair / a.n_kv);
   const int q0 = qt * tq;               // first chunk token of the tile
   // a packed-query range outside [0, total_q) is clipped so no access leaves q or out
   const int qs = min(max(a.cu_q[s], 0), a.total_q);
@@ -204,20 +208,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int lb = kt * (KT / BS) + w;
     return trow[min(lb, a.max_blocks - 1)];
   };
+  // Per-lane source offsets inside a block, one per instruction k: lane l
+  // brings key row r = 4k + l / 16 and the global piece that lands in slot
+  // l % 16 of that row (r < 16, so the swizzle takes r as is).
+  uint32_t src_off[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 4 * k + (lane >> 4);
+    src_off[k] = r * ROWB + (((lane & 15) ^ swz_f(r)) << 4);
+  }
+  const uint32_t lds0 = lds_addr(smem) + BS * w * ROWB;  // this wave's first tile row
   auto issue = [&](int kt, int raw_id) {
     const int lb = kt * (KT / BS) + w;
     if (lb >= n_lblocks || lb >= a.max_blocks) return;  // nothing to load for this wave
-    const int id = min(max(raw_id, 0), (int)(a.num_blocks - 1));
-    char* const stage = smem + (kt % kStages) * STAGE_B;
+    const int id = min(max(__builtin_amdgcn_readfirstlane(raw_id), 0), (int)(a.num_blocks - 1));
     const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
+    const uint32_t dst = lds0 + (kt % kStages) * STAGE_B;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int r = 4 * k + (lane >> 4);        // key row within the block
-      const int piece = (lane & 15) ^ swz_f(r);  // global piece landing in slot lane % 16 (r < 16)
-      const int64_t off = slab + r * ROWB + piece * 16;
-      const int lrow = BS * w + 4 * k;          // first tile row this instruction writes
-      lds_dma16(kc + off, stage + lrow * ROWB);
-      lds_dma16(vc + off, stage + TILE_B + lrow * ROWB);
+      lds_dma16(kc + slab, src_off[k], dst + 4 * k * ROWB);
+      lds_dma16(vc + slab, src_off[k], dst + TILE_B + 4 * k * ROWB);
     }
   };
   int id_next = 0;
