@@ -241,14 +241,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const char* const k_lds = smem + (kt % kStages) * STAGE_B;
     const char* const v_lds = k_lds + TILE_B;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt have landed
-    if (kt * KT + KT > total) {
-      // the sequence ends inside this tile: V rows past it (and rows no load
-      // wrote) may hold anything, NaN included, and their zero weights must
-      // not meet a NaN.  K rows need no clearing: their scores are masked.
+    if (kt * KT + KT > kv_end) {
+      // the keys this workgroup sees end inside this tile: V rows past them
+      // (rows no load wrote, or past the sequence end) may hold anything, NaN
+      // included, and the zero weights every real row gives them must not
+      // meet a NaN.  K rows need no clearing: their scores are masked.
       no_if_conversion();
       for (int idx = lane; idx < BS * 16; idx += kWave) {
         const int r = BS * w + idx / 16;
-        if (kt * KT + r >= total) st16(const_cast<char*>(v_lds) + r * ROWB + (idx % 16) * 16, u32x4{0, 0, 0, 0});
+        if (kt * KT + r >= kv_end) st16(const_cast<char*>(v_lds) + r * ROWB + (idx % 16) * 16, u32x4{0, 0, 0, 0});
       }
     }
     __syncthreads();  // tile kt is in LDS; every wave is done with tile kt - 1
