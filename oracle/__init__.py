@@ -14,6 +14,8 @@ Sources (three web pages):
   * "Memory Management in LLM Serving Systems" -- "KV cache sizing",
     "MHA, MQA, and GQA", "Method 3: PagedAttention", "Walking the table",
     "FlashAttention" (numerically stable softmax, causal -inf mask).
+    "Prefix sharing" (a shared prefix stored once); Problem 4 of the first
+    page for block sharing with reference counts and copy-on-write.
   * "The KV Cache from First Principles" -- "The redundancy" (the query
     attends positions 1..t including itself), "Implementation" (query head h
     uses KV head h // (n_q / n_kv); the head-ratio check runs before the cache
@@ -27,6 +29,7 @@ from .paging import (slot_of, slot_mapping, kv_append, gather_sequence, csr_page
                      kv_bytes_per_token, kv_bytes, waste_tokens)
 from .attention import (head_to_kv_head, softmax_attention_rows, paged_decode, paged_prefill,
                         decode_one, prefill_one)
+from .sharing import BlockPool, PoolExhausted, copy_blocks
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_to_f64", "f32_to_f64", "decode_storage",
@@ -34,4 +37,5 @@ __all__ = [
     "kv_bytes_per_token", "kv_bytes", "waste_tokens",
     "head_to_kv_head", "softmax_attention_rows", "paged_decode", "paged_prefill",
     "decode_one", "prefill_one",
+    "BlockPool", "PoolExhausted", "copy_blocks",
 ]

@@ -516,3 +516,135 @@ ALL_CHECKS = [
     check_paged_equals_contiguous, check_cache_equals_recompute, check_head_grouping, check_special_cases,
     check_online_softmax, check_demo_shapes, check_poison_ignored,
 ]
+
+
+# ---------------------------------------------------------------------------
+# block sharing and copy-on-write
+# ---------------------------------------------------------------------------
+
+def _replay_cow(pool, steps, B, width=8):
+    """Run the fixture's operations; yields (step, row or None, copies)."""
+    rows = {}
+    for st in steps:
+        row, copies = None, []
+        if st["op"] == "prompt":
+            n = -(-st["tokens"] // B)
+            rows[st["seq"]] = (list(pool.alloc(n)) + [0] * width)[:width]
+            row = rows[st["seq"]][:n]
+        elif st["op"] == "fork":
+            n = len(st["row"])
+            pool.share(rows[st["from"]][:n])
+            rows[st["seq"]] = list(rows[st["from"]])
+            row = rows[st["seq"]][:n]
+        elif st["op"] == "append":
+            r, copies = pool.prepare_append(rows[st["seq"]], st["seq_len"], st["tokens"], B)
+            rows[st["seq"]] = list(r)
+            row = list(r)[:-(-(st["seq_len"] + st["tokens"]) // B)]
+        elif st["op"] == "release":
+            pool.release(rows[st["seq"]][:4])  # the released sequence owns four blocks
+        yield st, row, [list(c) for c in copies]
+
+
+def check_cow_fixture(orc):
+    """The fork / append / release walk worked by hand from the page's rules."""
+    g = _golden("cow_fork.json")
+    pool = orc.BlockPool(g["num_blocks"])
+    for st, row, copies in _replay_cow(pool, g["steps"], g["block_size"]):
+        if row is not None:
+            assert row == st["row"], (st, row)
+        if st["op"] == "append":
+            assert copies == st["copies"], (st, copies)
+        if st["op"] == "release":
+            assert pool.free_blocks() == st["free"], st
+        assert list(pool.ref) == st["ref"], (st, list(pool.ref))
+
+
+def check_cow_invariants(orc):
+    """Random forks, appends and releases: a block's count equals the number
+    of live tables naming it, and after an append every block the new tokens
+    fall into is named by that table alone (so writing it touches no other
+    sequence)."""
+    rng = np.random.default_rng(7)
+    B, N = 4, 64
+    pool = orc.BlockPool(N)
+    live = {}  # seq -> (row, length)
+    nxt = 0
+    for _ in range(400):
+        op = rng.integers(0, 4)
+        if op == 0 or not live:
+            n = int(rng.integers(1, 10))
+            try:
+                row, _ = pool.prepare_append([0] * 32, 0, n, B)
+            except orc.PoolExhausted:
+                continue
+            live[nxt] = (row, n)
+            nxt += 1
+        elif op == 1:
+            s = int(rng.choice(list(live)))
+            row, L = live[s]
+            pool.share(row[:-(-L // B)])
+            live[nxt] = (list(row), L)
+            nxt += 1
+        elif op == 2:
+            s = int(rng.choice(list(live)))
+            row, L = live[s]
+            n = int(rng.integers(1, 7))
+            if -(-(L + n) // B) > 32:
+                continue
+            before = pool.free_blocks()
+            try:
+                new_row, copies = pool.prepare_append(row, L, n, B)
+            except orc.PoolExhausted:
+                assert pool.free_blocks() == before  # nothing changed
+                continue
+            for j in range(L // B, (L + n - 1) // B + 1):
+                assert pool.ref[new_row[j]] == 1
+            for src, dst in copies:
+                assert src in row[:-(-L // B)] and dst not in row[:-(-L // B)]
+            live[s] = (new_row, L + n)
+        else:
+            s = int(rng.choice(list(live)))
+            row, L = live.pop(s)
+            pool.release(row[:-(-L // B)])
+        counts = np.zeros(N, dtype=int)
+        for row, L in live.values():
+            for b in row[:-(-L // B)]:
+                counts[b] += 1
+        assert list(counts) == list(pool.ref)
+        assert pool.free_blocks() == int(np.sum(counts == 0))
+
+
+def check_copy_blocks(orc):
+    """A copied block equals its source in every head and slot, scales
+    included; no other block changes."""
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((6, 2, 4, 8)).astype(np.float32)
+    v = rng.standard_normal((6, 2, 4, 8)).astype(np.float32)
+    ks, vs = rng.random((6, 2)).astype(np.float32), rng.random((6, 2)).astype(np.float32)
+    k2, v2, ks2, vs2 = orc.copy_blocks(k, v, [(1, 4), (2, 0)], ks, vs)
+    for src, dst in [(1, 4), (2, 0)]:
+        assert np.array_equal(k2[dst], k[src]) and np.array_equal(v2[dst], v[src])
+        assert np.array_equal(ks2[dst], ks[src]) and np.array_equal(vs2[dst], vs[src])
+    for b in (1, 2, 3, 5):
+        assert np.array_equal(k2[b], k[b]) and np.array_equal(v2[b], v[b]) and np.array_equal(ks2[b], ks[b])
+
+
+def check_shared_prefix_decode(orc):
+    """'Prefix sharing': two sequences whose tables name the same prefix
+    blocks attend exactly as two sequences holding private copies."""
+    rng = np.random.default_rng(11)
+    B, n_kv, d, n_q = 4, 2, 8, 4
+    k = rng.standard_normal((10, n_kv, B, d)).astype(np.float32)
+    v = rng.standard_normal((10, n_kv, B, d)).astype(np.float32)
+    q = rng.standard_normal((2, n_q, d)).astype(np.float32)
+    shared = np.array([[0, 1, 2, 0], [0, 1, 3, 0]], dtype=np.int32)     # blocks 0, 1 shared
+    private = np.array([[0, 1, 2, 0], [4, 5, 3, 0]], dtype=np.int32)    # 4, 5 copies of 0, 1
+    k2, v2 = k.copy(), v.copy()
+    k2[4], k2[5], v2[4], v2[5] = k[0], k[1], v[0], v[1]
+    lens = np.array([10, 11], dtype=np.int32)
+    a = orc.paged_decode(q, "f32", k, v, "f32", None, None, shared, lens, n_q, n_kv, 0.3)
+    b = orc.paged_decode(q, "f32", k2, v2, "f32", None, None, private, lens, n_q, n_kv, 0.3)
+    assert np.array_equal(a, b)
+
+
+ALL_CHECKS += [check_cow_fixture, check_cow_invariants, check_copy_blocks, check_shared_prefix_decode]

@@ -40,6 +40,14 @@ MUTATIONS = [
     ("codecs.py", "normal = (1.0 + man / 8.0)", "normal = (1.0 + man / 16.0)"),
     ("codecs.py", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("codecs.py", "val = np.where(sign == 1, -mag, mag)", "val = mag"),
+    ("sharing.py", "                if self.ref[row[j]] > 1:", "                if self.ref[row[j]] >= 1:"),
+    ("sharing.py", "                    self.release([row[j]])\n", ""),
+    ("sharing.py", "out = [b for b, r in enumerate(self.ref) if r == 0][:n]",
+     "out = [b for b, r in enumerate(self.ref) if r == 0][::-1][:n]"),
+    ("sharing.py", "first, last = seq_len // block_size,", "first, last = (seq_len + 1) // block_size,"),
+    ("sharing.py", "            self.ref[b] += 1", "            self.ref[b] += 2"),
+    ("sharing.py", "        k[dst] = k_cache[src]", "        k[dst] = v_cache[src]"),
+    ("sharing.py", "            vs[dst] = v_scale[src]", "            vs[dst] = k_scale[src]"),
 ]
 
 
