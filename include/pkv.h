@@ -12,7 +12,9 @@
  *  - Pointers marked (device) must point to GPU memory of the current HIP
  *    device; pointers marked (host) to host memory.  The caller owns every
  *    buffer, including workspaces, whose sizes the *_workspace() calls give.
- *    The library allocates nothing and keeps no state between calls.
+ *    The library allocates no device memory and keeps no state between
+ *    calls; the one exception is the host-side block pool object below,
+ *    which the caller creates and destroys.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it and the call returns without synchronising.
  *  - Cache layout, one layer: cache[num_blocks][n_kv_heads][block_size][d_head],
@@ -51,7 +53,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad head ratio */
   PKV_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_head, block_size, dtype combination) */
   PKV_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace() size */
-  PKV_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  PKV_ERR_NO_BLOCKS = 5    /* a block pool has too few free blocks for the request */
 } pkv_status;
 
 /* Element types. FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN), with
@@ -110,6 +113,62 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
 pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                             int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
                             void* stream);
+
+/* ---- Block sharing: reference counts and copy-on-write ----
+ * [KVP] Problem 4, "The idea": blocks are handed out only when a sequence's
+ * previous block fills; because sequences reach blocks through their tables,
+ * several can name the same physical blocks -- parallel samples and beam
+ * branches share the prompt's blocks -- with a reference count per block, and
+ * a block named by more than one table is copied before it is written
+ * (copy-on-write); [MEM] "Prefix sharing" stores a shared prefix once.
+ *
+ * pkv_block_pool is host bookkeeping only (reference counts and the free
+ * list; it never touches the device).  Free blocks are handed out lowest id
+ * first, so a sequence of operations has one outcome.  Each call locks the
+ * pool, so pools may be used from several threads.  Calls that fail change
+ * nothing. */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* Creates a pool of num_blocks (1 .. 2^31 - 1) free blocks in *pool_out. */
+pkv_status pkv_pool_create(int64_t num_blocks, pkv_block_pool** pool_out);
+void pkv_pool_destroy(pkv_block_pool* pool);
+/* Free blocks, or -1 for a NULL pool. */
+int64_t pkv_pool_free_blocks(pkv_block_pool* pool);
+/* How many tables name `block` (0 = free), or -1 if it is not in the pool. */
+int32_t pkv_pool_refcount(pkv_block_pool* pool, int32_t block);
+/* n fresh blocks, each named once, into ids_out (host int32 [n]);
+ * PKV_ERR_NO_BLOCKS if fewer than n are free. */
+pkv_status pkv_pool_alloc(pkv_block_pool* pool, int32_t n, int32_t* ids_out);
+/* One more table names each of ids (host int32 [n]): a fork.  Every id must
+ * be allocated (else PKV_ERR_INVALID_ARG). */
+pkv_status pkv_pool_share(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+/* One table fewer names each of ids; a block no table names is free again.
+ * Every id must be allocated, counted with multiplicity. */
+pkv_status pkv_pool_release(pkv_block_pool* pool, const int32_t* ids, int32_t n);
+/* Before appending n_new tokens to a sequence of seq_len tokens whose table
+ * row (host int32 [max_blocks_per_seq], entries < ceil(seq_len / block_size)
+ * valid) names blocks of this pool: makes every block that positions
+ * seq_len .. seq_len + n_new - 1 fall into writable by this sequence alone.
+ * A logical block past the row's last is allocated; an existing one named by
+ * other tables too (only the partly filled last block can be one) is
+ * replaced in the row by a fresh block, whose contents must be copied from
+ * the old one before the append: *n_copies (0 or 1) gets the count and
+ * *copy_src / *copy_dst the pair, for pkv_copy_blocks.  The row is updated
+ * in place.  PKV_ERR_NO_BLOCKS if the pool cannot supply the blocks;
+ * PKV_ERR_INVALID_ARG if the row is too short or names a block outside the
+ * pool or not allocated. */
+pkv_status pkv_pool_prepare_append(pkv_block_pool* pool, int32_t* table_row, int32_t max_blocks_per_seq,
+                                   int32_t seq_len, int32_t n_new, int32_t block_size, int32_t* copy_src,
+                                   int32_t* copy_dst, int32_t* n_copies);
+
+/* Copies whole blocks src[i] -> dst[i] of one layer's K and V pools (every KV
+ * head and slot, bit for bit) and, when k_scale / v_scale are given (FP8
+ * caches), their per-(block, KV head) scales: the copy of copy-on-write.
+ * src, dst: (device) int32 [n_pairs]; a pair naming a block outside
+ * [0, num_blocks) is skipped.  No dst may equal a src of the same call. */
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, float* k_scale, float* v_scale,
+                           int64_t num_blocks, const int32_t* src, const int32_t* dst, int32_t n_pairs,
+                           int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
 
 /* Paged decode attention: one query per sequence attends every cached token
  * of its sequence, the current one included ([FP] "The redundancy"; [KVP]

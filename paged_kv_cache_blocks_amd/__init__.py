@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 _lib = None
 
 # status codes and element types (include/pkv.h)
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS = range(6)
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -46,6 +46,15 @@ _SIGS = {
                                       ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                       _sz, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_workspace": ([_i32, _i32, _i32, _i32], _sz),
+    "pkv_pool_create": ([_i64, _vp], ctypes.c_int),
+    "pkv_pool_destroy": ([_vp], None),
+    "pkv_pool_free_blocks": ([_vp], _i64),
+    "pkv_pool_refcount": ([_vp, _i32], _i32),
+    "pkv_pool_alloc": ([_vp, _i32, _vp], ctypes.c_int),
+    "pkv_pool_share": ([_vp, _vp, _i32], ctypes.c_int),
+    "pkv_pool_release": ([_vp, _vp, _i32], ctypes.c_int),
+    "pkv_pool_prepare_append": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "pkv_copy_blocks": ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
 }
 
 
@@ -170,6 +179,74 @@ def check_tables(block_table, seq_lens, num_blocks: int, block_size: int = 16, s
     _check(load().pkv_check_tables(_ptr(block_table), block_table.shape[1], _ptr(seq_lens), block_table.shape[0],
                                 num_blocks, block_size, _ptr(err), _stream(stream)))
     return int(err.item())
+
+
+class BlockPool:
+    """Host-side block pool of libpkv: reference counts, lowest-id-first
+    allocation and copy-on-write bookkeeping for appends (``pkv_pool_*``).
+    Ids are plain ints; rows are lists of int."""
+
+    def __init__(self, num_blocks: int):
+        h = ctypes.c_void_p()
+        _check(load().pkv_pool_create(int(num_blocks), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().pkv_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def free_blocks(self) -> int:
+        return load().pkv_pool_free_blocks(self._h)
+
+    def refcount(self, block: int) -> int:
+        return load().pkv_pool_refcount(self._h, int(block))
+
+    @staticmethod
+    def _ids(ids):
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*[int(b) for b in ids])
+        return arr, len(ids)
+
+    def alloc(self, n: int) -> list:
+        arr = (ctypes.c_int32 * max(1, n))()
+        _check(load().pkv_pool_alloc(self._h, int(n), ctypes.cast(arr, ctypes.c_void_p)))
+        return list(arr[:n])
+
+    def share(self, ids) -> None:
+        arr, n = self._ids(ids)
+        _check(load().pkv_pool_share(self._h, ctypes.cast(arr, ctypes.c_void_p), n))
+
+    def release(self, ids) -> None:
+        arr, n = self._ids(ids)
+        _check(load().pkv_pool_release(self._h, ctypes.cast(arr, ctypes.c_void_p), n))
+
+    def prepare_append(self, row, seq_len: int, n_new: int, block_size: int = 16):
+        """Returns (new row, [(src, dst)]) -- the copies to run before the append."""
+        arr, n = self._ids(row)
+        src, dst, nc = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(load().pkv_pool_prepare_append(self._h, ctypes.cast(arr, ctypes.c_void_p), n, int(seq_len), int(n_new),
+                                              int(block_size), ctypes.byref(src), ctypes.byref(dst), ctypes.byref(nc)))
+        return list(arr[:n]), [(src.value, dst.value)] if nc.value else []
+
+
+def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor, dst: torch.Tensor, *,
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Copy whole blocks src[i] -> dst[i] (int32 device tensors) of one layer's caches, scales included."""
+    _need(src, torch.int32, "src")
+    _need(dst, torch.int32, "dst")
+    if src.numel() != dst.numel():
+        raise ValueError("src and dst differ in length")
+    nb, n_kv, bs, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache must match")
+    _check(load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), nb,
+                                  _ptr(src), _ptr(dst), src.numel(), n_kv, d, bs, _stream(stream)))
 
 
 def paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,

@@ -100,6 +100,24 @@ __global__ __launch_bounds__(256) void check_tables_kernel(const int32_t* __rest
   if (bad) atomicAdd(err, bad);
 }
 
+// Copy-on-write copy: whole blocks src -> dst of the K and V pools.  One
+// thread moves 16 bytes; grid x over the block's 16-byte pieces, y = pair,
+// z = 0 for K, 1 for V.  The first n_kv threads of each (pair, K/V) also copy
+// the block's scales when there are any.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                                          float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                          int64_t num_blocks, const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int64_t block_bytes,
+                                                          int32_t n_kv) {
+  const int64_t piece = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t s = src[blockIdx.y], d = dst[blockIdx.y];
+  if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks) return;
+  char* const cache = blockIdx.z == 0 ? k_cache : v_cache;
+  if (piece * 16 < block_bytes) st16(cache + d * block_bytes + piece * 16, ld16(cache + s * block_bytes + piece * 16));
+  float* const scale = blockIdx.z == 0 ? k_scale : v_scale;
+  if (scale != nullptr && piece < n_kv) scale[d * n_kv + piece] = scale[s * n_kv + piece];
+}
+
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
                                const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,
                                hipStream_t stream) {
@@ -135,6 +153,19 @@ hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const i
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream) {
   hipLaunchKernelGGL(check_tables_kernel, dim3(batch), dim3(256), 0, stream, table, max_blocks, seq_lens, batch,
                      num_blocks, block_size, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                              const int32_t* src, const int32_t* dst, int32_t n_pairs, int64_t block_bytes,
+                              int32_t n_kv, hipStream_t stream) {
+  if (n_pairs == 0) return hipSuccess;
+  const int64_t pieces = block_bytes / 16;
+  const int64_t gx = ((pieces > n_kv ? pieces : (int64_t)n_kv) + 255) / 256;
+  if (gx > 0x7fffffff || n_pairs > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n_pairs, 2), dim3(256), 0, stream,
+                     static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scale, v_scale, num_blocks, src, dst,
+                     block_bytes, n_kv);
   return hipGetLastError();
 }
 

@@ -1,12 +1,17 @@
-// C ABI of libpkv: argument validation, launch-shape choice, error reporting.
-// Every check runs before any launch, so a failing call leaves the device
-// untouched.  No allocation, no global state beyond the thread-local message.
+// C ABI of libpkv: argument validation, launch-shape choice, error reporting,
+// and the host-side block pool.  Every check runs before any launch, so a
+// failing call leaves the device untouched.  No device allocation; no global
+// state beyond the thread-local message.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
+#include <functional>
+#include <mutex>
+#include <queue>
+#include <vector>
 
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
@@ -215,6 +220,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS";
   }
   return "PKV_ERR_UNKNOWN";
 }
@@ -461,6 +467,154 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   a.out_bf16 = out_dtype == PKV_BF16;
   a.scale_log2 = scale * kLog2e;
   return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
+}
+
+
+// ---- block pool: reference counts, lowest-id-first allocation, copy-on-write
+// ("KV cache, PagedAttention and FlashAttention", Problem 4, "The idea")
+
+}  // extern "C"
+
+struct pkv_block_pool {
+  std::mutex mu;
+  std::vector<int32_t> ref;  // tables naming each block; 0 = free
+  std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> free_ids;  // lowest id on top
+
+  int32_t take() {  // caller checked that a block is free
+    const int32_t b = free_ids.top();
+    free_ids.pop();
+    ref[b] = 1;
+    return b;
+  }
+  void drop(int32_t b) {
+    if (--ref[b] == 0) free_ids.push(b);
+  }
+  bool allocated(int32_t b) const { return b >= 0 && b < (int32_t)ref.size() && ref[b] > 0; }
+};
+
+extern "C" {
+
+pkv_status pkv_pool_create(int64_t num_blocks, pkv_block_pool** pool_out) {
+  if (!pool_out) return fail(PKV_ERR_INVALID_ARG, "pool_out is NULL");
+  if (num_blocks < 1 || num_blocks > 0x7fffffff) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be in [1, 2^31)");
+  auto* p = new pkv_block_pool;
+  p->ref.assign((size_t)num_blocks, 0);
+  std::vector<int32_t> ids((size_t)num_blocks);
+  for (int64_t i = 0; i < num_blocks; ++i) ids[(size_t)i] = (int32_t)i;
+  p->free_ids = decltype(p->free_ids)(std::greater<int32_t>(), std::move(ids));
+  *pool_out = p;
+  return ok();
+}
+
+void pkv_pool_destroy(pkv_block_pool* pool) { delete pool; }
+
+int64_t pkv_pool_free_blocks(pkv_block_pool* pool) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> g(pool->mu);
+  return (int64_t)pool->free_ids.size();
+}
+
+int32_t pkv_pool_refcount(pkv_block_pool* pool, int32_t block) {
+  if (!pool) return -1;
+  std::lock_guard<std::mutex> g(pool->mu);
+  if (block < 0 || block >= (int32_t)pool->ref.size()) return -1;
+  return pool->ref[block];
+}
+
+pkv_status pkv_pool_alloc(pkv_block_pool* pool, int32_t n, int32_t* ids_out) {
+  if (!pool || (n > 0 && !ids_out)) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  std::lock_guard<std::mutex> g(pool->mu);
+  if ((size_t)n > pool->free_ids.size())
+    return fail(PKV_ERR_NO_BLOCKS, "%d blocks wanted, %zu free", n, pool->free_ids.size());
+  for (int32_t i = 0; i < n; ++i) ids_out[i] = pool->take();
+  return ok();
+}
+
+pkv_status pkv_pool_share(pkv_block_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || (n > 0 && !ids)) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  std::lock_guard<std::mutex> g(pool->mu);
+  for (int32_t i = 0; i < n; ++i)
+    if (!pool->allocated(ids[i])) return fail(PKV_ERR_INVALID_ARG, "block %d is not allocated", ids[i]);
+  for (int32_t i = 0; i < n; ++i) ++pool->ref[ids[i]];
+  return ok();
+}
+
+pkv_status pkv_pool_release(pkv_block_pool* pool, const int32_t* ids, int32_t n) {
+  if (!pool || (n > 0 && !ids)) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (n < 0) return fail(PKV_ERR_INVALID_ARG, "n must be >= 0");
+  std::lock_guard<std::mutex> g(pool->mu);
+  // every reference released must exist, counting repeats in ids
+  std::vector<int32_t> sorted(ids, ids + n);
+  std::sort(sorted.begin(), sorted.end());
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i;
+    while (j < n && sorted[j] == sorted[i]) ++j;
+    const int32_t b = sorted[i];
+    if (!pool->allocated(b) || pool->ref[b] < j - i)
+      return fail(PKV_ERR_INVALID_ARG, "block %d released more often than it is named", b);
+    i = j;
+  }
+  for (int32_t i = 0; i < n; ++i) pool->drop(ids[i]);
+  return ok();
+}
+
+pkv_status pkv_pool_prepare_append(pkv_block_pool* pool, int32_t* table_row, int32_t max_blocks_per_seq,
+                                   int32_t seq_len, int32_t n_new, int32_t block_size, int32_t* copy_src,
+                                   int32_t* copy_dst, int32_t* n_copies) {
+  if (!pool || !table_row || !copy_src || !copy_dst || !n_copies) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (seq_len < 0 || n_new < 0 || block_size < 1 || max_blocks_per_seq < 1)
+    return fail(PKV_ERR_INVALID_ARG, "seq_len and n_new must be >= 0, block_size and max_blocks positive");
+  *n_copies = 0;
+  if (n_new == 0) return ok();
+  const int64_t have = ((int64_t)seq_len + block_size - 1) / block_size;  // blocks the sequence owns
+  const int64_t first = seq_len / block_size, last = ((int64_t)seq_len + n_new - 1) / block_size;
+  if (last >= max_blocks_per_seq) return fail(PKV_ERR_INVALID_ARG, "block table row too short");
+  std::lock_guard<std::mutex> g(pool->mu);
+  for (int64_t j = 0; j < have; ++j)
+    if (!pool->allocated(table_row[j]))
+      return fail(PKV_ERR_INVALID_ARG, "row entry %lld names block %d, which is not allocated", (long long)j,
+                  table_row[j]);
+  // only the partly filled last block can exist already
+  const bool cow = first < have && pool->ref[table_row[first]] > 1;
+  const int64_t need = (cow ? 1 : 0) + (last + 1 - std::max(have, first));
+  if ((size_t)need > pool->free_ids.size())
+    return fail(PKV_ERR_NO_BLOCKS, "the append needs %lld blocks, %zu free", (long long)need, pool->free_ids.size());
+  for (int64_t j = first; j <= last; ++j) {
+    if (j < have) {
+      if (cow) {
+        const int32_t fresh = pool->take();
+        *copy_src = table_row[j];
+        *copy_dst = fresh;
+        *n_copies = 1;
+        pool->drop(table_row[j]);
+        table_row[j] = fresh;
+      }
+    } else {
+      table_row[j] = pool->take();
+    }
+  }
+  return ok();
+}
+
+pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, float* k_scale, float* v_scale,
+                           int64_t num_blocks, const int32_t* src, const int32_t* dst, int32_t n_pairs,
+                           int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream) {
+  if (n_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "n_pairs must be >= 0");
+  if (n_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !src || !dst) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (!valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
+  if (num_blocks < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if ((cache_dtype == PKV_FP8_E4M3FN) != (k_scale != nullptr) || (k_scale != nullptr) != (v_scale != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale are given exactly for FP8 caches");
+  const int64_t block_bytes = (int64_t)n_kv_heads * block_size * d_head * elem_bytes(cache_dtype);
+  if (block_bytes % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "a block must be a multiple of 16 bytes");
+  if (n_pairs > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 pairs per call");
+  return hip_status(pkv::launch_copy_blocks(k_cache, v_cache, k_scale, v_scale, num_blocks, src, dst, n_pairs,
+                                            block_bytes, n_kv_heads, (hipStream_t)stream),
+                    "copy_blocks launch");
 }
 
 }  // extern "C"

@@ -60,6 +60,9 @@ hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const vo
                          const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, const int64_t* cu,
                          int64_t total_rows, int32_t batch, int32_t n_kv, int32_t row_bytes, int32_t block_size,
                          hipStream_t stream);
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                              const int32_t* src, const int32_t* dst, int32_t n_pairs, int64_t block_bytes,
+                              int32_t n_kv, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
 

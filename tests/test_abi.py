@@ -42,8 +42,9 @@ def test_version_and_status_strings(pkv):
     hdr = open(HEADER).read()
     assert pkv.abi_version() == int(re.search(r"#define PKV_ABI_VERSION (\d+)", hdr).group(1))
     lib = pkv.load()
-    names = [lib.pkv_status_string(i).decode() for i in range(5)]
-    assert names == ["PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP"]
+    names = [lib.pkv_status_string(i).decode() for i in range(6)]
+    assert names == ["PKV_OK", "PKV_ERR_INVALID_ARG", "PKV_ERR_UNSUPPORTED", "PKV_ERR_WORKSPACE", "PKV_ERR_HIP",
+                     "PKV_ERR_NO_BLOCKS"]
 
 
 def test_bytes_per_token_formula(pkv):
