@@ -188,7 +188,8 @@ class DecodeWorkload:
         if p["split"] == "queue":
             k = f"decode_queue_kernel ({p['workgroups']} workgroups claiming items) + combine_queue_kernel"
         else:
-            k = (f"decode_kernel ({p['n_parts']} partition(s) of {p['partition_tokens']} tokens per (sequence, KV "
+            name = "decode_mfma_kernel" if p.get("matrix_cores") else "decode_kernel"
+            k = (f"{name} ({p['n_parts']} partition(s) of {p['partition_tokens']} tokens per (sequence, KV "
                  f"head), {p['workgroups']} workgroups)")
             if p["merge_pass"]:
                 k += " + combine_kernel"

@@ -179,7 +179,10 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, 
  * attention").  Computed FlashAttention-style ([KVP] Problem 5, "Tiling",
  * "Online softmax"; [MEM] "FlashAttention-2"): the sequence is split across
  * workgroups, each keeping a running max and sum, and the pieces are merged;
- * scores never reach memory.  The split is the library's choice: fixed
+ * scores never reach memory.  With bf16 or fp8 KV, d_head 128 and 4, 8 or
+ * 16 query heads per KV head (or per chunk of them) the split kernel does the
+ * dot products on the matrix cores, always in fixed partitions of at most
+ * 4096 tokens; otherwise the split is the library's choice: fixed
  * partitions per (sequence, KV head) when equal partitions of at most 4096
  * tokens give one resident workgroup each, otherwise the work-queue split:
  * each (sequence, KV head) is cut into items of equal block counts, a
@@ -238,10 +241,11 @@ size_t pkv_paged_attn_decode_workspace(int32_t batch, int32_t n_q_heads, int32_t
 
 /* How the decode call with these arguments splits its work on the current
  * device (partition_tokens as for pkv_paged_attn_decode_partitioned).  info:
- * (host) int32[6], filled with {split: 0 fixed partitions / 1 work queue,
+ * (host) int32[7], filled with {split: 0 fixed partitions / 1 work queue,
  * partition tokens (0 for the queue), partitions per (sequence, KV head)
  * (0 for the queue), workgroups of the split kernel, 1 if a merge pass
- * follows else 0, query heads per workgroup}.  Errors as for the decode
+ * follows else 0, query heads per workgroup, 1 if the split kernel is the
+ * matrix-core one else 0}.  Errors as for the decode
  * call's argument checks; PKV_ERR_HIP when the split needs a device and none
  * is present. */
 pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,

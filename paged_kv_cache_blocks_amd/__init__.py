@@ -252,11 +252,12 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,
 def paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
                            kv_dtype: int = BF16, partition_tokens=0) -> dict:
     """How the decode call splits its work on the current device."""
-    info = (ctypes.c_int32 * 6)()
+    info = (ctypes.c_int32 * 7)()
     _check(load().pkv_paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size,
                                              kv_dtype, partition_tokens, ctypes.cast(info, ctypes.c_void_p)))
     return {"split": "queue" if info[0] else "partitions", "partition_tokens": info[1], "n_parts": info[2],
-            "workgroups": info[3], "merge_pass": bool(info[4]), "heads_per_workgroup": info[5]}
+            "workgroups": info[3], "merge_pass": bool(info[4]), "heads_per_workgroup": info[5],
+            "matrix_cores": bool(info[6])}
 
 
 def paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,

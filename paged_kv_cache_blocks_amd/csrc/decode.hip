@@ -1048,8 +1048,13 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   }
   const int64_t wgs = (int64_t)a.n_parts * a.n_kv * a.head_chunks * a.batch;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<KIND, D, GW>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (a.use_mfma) {
+    e = launch_decode_mfma(a, KIND, stream);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KIND, D, GW>), dim3((unsigned)wgs), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess || a.n_parts == 1) return e;
   hipLaunchKernelGGL((combine_kernel<D>), dim3(a.n_q, a.batch), dim3(64), 0, stream, a);
   return hipGetLastError();

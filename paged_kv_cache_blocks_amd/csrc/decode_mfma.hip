@@ -1,0 +1,345 @@
+// Paged GQA decode on the matrix cores (d = 128, bf16 or fp8 E4M3 KV).
+//
+// Same method as the VALU decode kernel ("KV cache, PagedAttention and
+// FlashAttention", Problem 5: tiles of K and V, running max and sum, deferred
+// division; "Memory Management in LLM Serving Systems", MHA/MQA/GQA: the G
+// query heads of a group share every K and V element), with the two dot
+// products done by v_mfma_f32_16x16x32_bf16.  A KV head's G query heads are
+// the 16 columns of the MFMA tile (columns G..15 are zero queries whose
+// results are dropped), so one K or V fragment read from LDS feeds all G
+// heads.  With fp8 KV the VALU work per byte (two bf16 dot products per
+// element and head) is what limits the VALU kernel; here the products cost
+// 16 MFMAs per 32 tokens and the vector units only convert, stage and run the
+// softmax.
+//
+// Work decomposition (as the VALU kernel's partition mode): one workgroup per
+// (sequence, KV head chunk, partition); its four waves take 32-token chunks
+// (two cache blocks) round robin and keep their own running state, merged at
+// the end through LDS.  Per chunk a wave:
+//   loads the two K and V slabs with coalesced 16-byte loads (issued one
+//   chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
+//   its own LDS region in the swizzled row layout (V rows past the end of the
+//   sequence are written as zeros: their zero weights must not meet a NaN);
+//   S^T = K q^T: 2 token tiles x 4 d steps, K fragments from LDS, q^T in
+//   registers; the fp8 K scale of each block multiplies its scores;
+//   online softmax per head column (in-lane max over the lane's 8 tokens,
+//   then across the four lane rows); weights rounded to bf16, the running sum
+//   adds the same rounded weights, and with fp8 each block's V scale
+//   multiplies its weights before the value product;
+//   O^T += V^T P^T: 8 d tiles, V^T fragments read with ds_read_b64_tr_b16.
+#include "pkv_device.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int D = 128;
+constexpr int kB = 16;                 // tokens per cache block
+constexpr int kCT = 32;                // tokens per wave chunk (two blocks)
+constexpr int kW = 4;                  // waves per workgroup
+constexpr int kTileB = kCT * 256;      // one K or V chunk in LDS (bf16 rows of 256 bytes)
+constexpr int kWaveB = 2 * kTileB;     // K then V
+constexpr int kMaxHeads = 16;          // MFMA columns
+constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+constexpr float kSlack = 8.f;          // log2 units: the running max moves only past this
+
+template <int KIND> struct Slab;
+// bf16: a (block, KV head) slab is 16 rows x 256 bytes; load i, lane l brings
+// row 4 i + l / 16, piece l % 16
+template <> struct Slab<KIND_BF16> {
+  static constexpr int bytes = kB * 256;
+  static constexpr int loads = 4;
+};
+// fp8: 16 rows x 128 bytes; load i, lane l brings row 8 i + l / 8, fp8 piece
+// l % 8 (16 codes = bf16 pieces 2 (l % 8) and 2 (l % 8) + 1)
+template <> struct Slab<KIND_FP8> {
+  static constexpr int bytes = kB * 128;
+  static constexpr int loads = 2;
+};
+
+__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int s) {
+  return min(max(a.seq_lens[s], 0), a.max_blocks * kB);
+}
+
+__device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float v) {
+  if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[idx] = (__bf16)v;
+  else reinterpret_cast<float*>(a.out)[idx] = v;
+}
+
+}  // namespace
+
+template <int KIND, int GW>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(GW >= 1 && GW <= kMaxHeads, "heads per workgroup");
+  using SL = Slab<KIND>;
+  __shared__ __align__(16) char smem[kW * kWaveB];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int n = lane & 15, g = lane >> 4;
+  const int hk = a.n_kv * a.head_chunks;
+  const int kvc = blockIdx.x % hk;
+  const int s = (blockIdx.x / hk) % a.batch;
+  const int part = blockIdx.x / (hk * a.batch);
+  const int kvh = kvc / a.head_chunks;
+  const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
+  const int p0 = part * a.part_tokens;
+  const int L = seq_len_of(a, s);
+  if (a.n_parts > 1 && p0 >= L) return;
+  const int plen = max(0, min(a.part_tokens, L - p0));  // tokens of this partition
+  const int nblk = (plen + kB - 1) / kB;
+  const int n_chunks = (nblk + 1) / 2;
+  const int n_my = n_chunks > w ? (n_chunks - w + kW - 1) / kW : 0;
+
+  // Block ids of this wave's chunks: lane i holds block (i & 1) of the wave's
+  // chunk i >> 1 (partition chunk w + 4 (i >> 1)); fp8 scales ride along.
+  int my_id = -1;
+  float my_ks = 1.f, my_vs = 1.f;
+  {
+    const int pb = (w + kW * (lane >> 1)) * 2 + (lane & 1);
+    if (pb < nblk) {
+      const int id = a.block_table[(int64_t)s * a.max_blocks + p0 / kB + pb];
+      my_id = min(max(id, 0), (int)(a.num_blocks - 1));
+      if constexpr (KIND == KIND_FP8) {
+        my_ks = a.k_scale[(int64_t)my_id * a.n_kv + kvh];
+        my_vs = a.v_scale[(int64_t)my_id * a.n_kv + kvh];
+      }
+    }
+  }
+
+  // q^T fragments (B operand): lane (n, g) holds head n, d = 32 ks + 8 g .. + 7
+  u32x4 qf[4];
+  {
+    const bool real = n < GW;
+    const char* qrow = reinterpret_cast<const char*>(a.q) + ((int64_t)s * a.n_q + h0 + (real ? n : 0)) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const u32x4 v = ld16(qrow + (32 * ks + 8 * g) * 2);
+      qf[ks] = real ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  char* const k_lds = smem + w * kWaveB;
+  char* const v_lds = k_lds + kTileB;
+  const char* const kc = reinterpret_cast<const char*>(a.k_cache);
+  const char* const vc = reinterpret_cast<const char*>(a.v_cache);
+
+  // A chunk's second block may lie past the partition (id -1): it is loaded
+  // from block 0 all the same, so the loads need no branch, and its rows,
+  // being past the end, are masked (K) or staged as zeros (V).
+  u32x4 bk[2][SL::loads], bv[2][SL::loads];
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int id = max(__builtin_amdgcn_readlane(my_id, 2 * c + b), 0);
+      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * SL::bytes;
+#pragma unroll
+      for (int i = 0; i < SL::loads; ++i) {
+        bk[b][i] = ld16(kc + slab + (i * kWave + lane) * 16);
+        bv[b][i] = ld16(vc + slab + (i * kWave + lane) * 16);
+      }
+    }
+  };
+
+  const float sl = a.scale_log2;
+  if (n_my > 0) issue(0);
+  for (int c = 0; c < n_my; ++c) {
+    const int t0 = (w + kW * c) * kCT;  // first token of the chunk (partition-relative)
+
+    // ---- stage K and V of the chunk into LDS (bf16 rows, swizzled) ----
+    wave_lds_sync();  // this wave's reads of the previous chunk are done
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+      for (int i = 0; i < SL::loads; ++i) {
+        if constexpr (KIND == KIND_BF16) {
+          const int r = kB * b + 4 * i + (lane >> 4);  // chunk row
+          const int pc = lane & 15;
+          const bool live = t0 + r < plen;
+          st16(k_lds + swz(r, pc), bk[b][i]);
+          st16(v_lds + swz(r, pc), live ? bv[b][i] : u32x4{0, 0, 0, 0});
+        } else {
+          const int r = kB * b + 8 * i + (lane >> 3);
+          const int p8 = lane & 7;
+          const bool live = t0 + r < plen;
+          uint32_t kb[8], vb[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            fp8x4_to_bf16x4(bk[b][i][e], kb[2 * e], kb[2 * e + 1]);
+            fp8x4_to_bf16x4(bv[b][i][e], vb[2 * e], vb[2 * e + 1]);
+          }
+          st16(k_lds + swz(r, 2 * p8), u32x4{kb[0], kb[1], kb[2], kb[3]});
+          st16(k_lds + swz(r, 2 * p8 + 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
+          st16(v_lds + swz(r, 2 * p8), live ? u32x4{vb[0], vb[1], vb[2], vb[3]} : u32x4{0, 0, 0, 0});
+          st16(v_lds + swz(r, 2 * p8 + 1), live ? u32x4{vb[4], vb[5], vb[6], vb[7]} : u32x4{0, 0, 0, 0});
+        }
+      }
+    }
+    // the registers are free again: fetch the next chunk while this one computes
+    if (c + 1 < n_my) issue(c + 1);
+    wave_lds_sync();
+
+    // ---- S^T = K q^T: token tiles t (block t of the chunk) x 4 d steps ----
+    f32x4 st[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) st[t] = mfma_bf16(ld16(k_lds + swz(16 * t + n, 4 * ks + g)), qf[ks], st[t]);
+    }
+
+    // ---- online softmax for head column n over tokens t0 + 16 t + 4 g + j ----
+    float sc[2][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float kscale = KIND == KIND_FP8
+                               ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                               __builtin_bit_cast(int, my_ks), 2 * c + t))
+                               : 1.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = t0 + 16 * t + 4 * g + j;
+        sc[t][j] = tok < plen ? st[t][j] * (sl * kscale) : -INFINITY;
+        mx = fmaxf(mx, sc[t][j]);
+      }
+    }
+    mx = max_xor32(max_xor16(mx));
+    const float m_new = (mx > m_run + kSlack) ? mx : m_run;  // m_run = -inf takes mx
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast(m_run - m_use);
+    m_run = m_new;
+    uint32_t pw[2][2];  // weights for the value product (fp8: times the block's V scale)
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float p[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = exp2_fast(sc[t][j] - m_use);
+      const uint32_t r0 = pack_bf16(p[0], p[1]), r1 = pack_bf16(p[2], p[3]);
+      ls = dot2_bf16(r1, kOnes, dot2_bf16(r0, kOnes, ls));  // the sum adds the rounded weights
+      if constexpr (KIND == KIND_FP8) {
+        const float vscale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                           __builtin_bit_cast(int, my_vs), 2 * c + t));
+        pw[t][0] = pack_bf16(p[0] * vscale, p[1] * vscale);
+        pw[t][1] = pack_bf16(p[2] * vscale, p[3] * vscale);
+      } else {
+        pw[t][0] = r0;
+        pw[t][1] = r1;
+      }
+    }
+    l_run = l_run * alpha + ls;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o[dt] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T: lane group g's weights are tokens {4g..4g+3,
+    // 16+4g..16+4g+3}; the transposing reads fetch V rows in that order ----
+    const u32x4 pf = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
+    {
+      const int jj = (lane >> 2) & 3, qq = lane & 3;
+      const int key_a = 4 * g + jj, key_b = key_a + 16;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int pc = 2 * dt + (qq >> 1), half = (qq & 1) * 8;
+        const u32x2 lo = ds_read_tr(v_lds + swz(key_a, pc) + half);
+        const u32x2 hi = ds_read_tr(v_lds + swz(key_b, pc) + half);
+        o[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[dt]);
+      }
+    }
+  }
+
+  // ---- merge the four waves: lane (n, g) holds O^T[16 dt + 4 g + j][head n] ----
+  const float l_head = sum_xor32(sum_xor16(l_run));
+  __syncthreads();  // every wave is done with its LDS region
+  float* mo = reinterpret_cast<float*>(smem);     // [wave][head][d]
+  float* mml = mo + kW * kMaxHeads * D;           // [wave][head][2]
+  if (g == 0) {
+    mml[(w * kMaxHeads + n) * 2 + 0] = m_run;
+    mml[(w * kMaxHeads + n) * 2 + 1] = l_head;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mo[(w * kMaxHeads + n) * D + 16 * dt + 4 * g + j] = o[dt][j];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < GW * D; idx += 256) {
+    const int h = idx / D, col = idx % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) M = fmaxf(M, mml[(ww * kMaxHeads + h) * 2]);
+    float lsum = 0.f, osum = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < kW; ++ww) {
+        const float mw = mml[(ww * kMaxHeads + h) * 2];
+        const float e = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+        lsum = fmaf(e, mml[(ww * kMaxHeads + h) * 2 + 1], lsum);
+        osum = fmaf(e, mo[(ww * kMaxHeads + h) * D + col], osum);
+      }
+    }
+    const int hq = h0 + h;
+    if (a.n_parts == 1) {
+      put_out(a, ((int64_t)s * a.n_q + hq) * D + col, lsum > 0.f ? osum / lsum : 0.f);
+    } else {
+      const int64_t pi = ((int64_t)s * a.n_q + hq) * a.n_parts + part;
+      a.ws_o[pi * D + col] = osum;
+      if (col == 0) {
+        a.ws_ml[pi * 2 + 0] = M;
+        a.ws_ml[pi * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
+bool decode_mfma_supported(int kv_kind, int d, int heads_per_wg) {
+  return (kv_kind == KIND_BF16 || kv_kind == KIND_FP8) && d == D &&
+         (heads_per_wg == 16 || heads_per_wg == 8 || heads_per_wg == 4);
+}
+
+template <int KIND, int GW>
+static int mfma_wgs_per_cu() {
+  int nwg = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nwg, decode_mfma_kernel<KIND, GW>, 256, 0) != hipSuccess) return 1;
+  return nwg > 0 ? nwg : 1;
+}
+
+int decode_mfma_wgs_per_cu(int kv_kind, int heads_per_wg) {
+  static int cache[3][17] = {};
+  int& c = cache[kv_kind][heads_per_wg];
+  if (c == 0) {
+    if (kv_kind == KIND_BF16)
+      c = heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_BF16, 16>()
+          : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_BF16, 8>() : mfma_wgs_per_cu<KIND_BF16, 4>();
+    else
+      c = heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_FP8, 16>()
+          : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_FP8, 8>() : mfma_wgs_per_cu<KIND_FP8, 4>();
+  }
+  return c;
+}
+
+template <int KIND>
+static hipError_t launch_kind(const DecodeArgs& a, unsigned wgs, hipStream_t stream) {
+  switch (a.group / a.head_chunks) {
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<KIND, 16>), dim3(wgs), dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<KIND, 8>), dim3(wgs), dim3(256), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<KIND, 4>), dim3(wgs), dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_kind, hipStream_t stream) {
+  const int64_t wgs = (int64_t)a.n_parts * a.n_kv * a.head_chunks * a.batch;
+  if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+  return kv_kind == KIND_FP8 ? launch_kind<KIND_FP8>(a, (unsigned)wgs, stream)
+                             : launch_kind<KIND_BF16>(a, (unsigned)wgs, stream);
+}
+
+}  // namespace pkv

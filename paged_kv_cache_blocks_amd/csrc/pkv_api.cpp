@@ -63,6 +63,7 @@ pkv_status check_heads(int32_t n_q, int32_t n_kv) {
 
 struct DecodePlan {
   int32_t head_chunks;
+  int32_t use_mfma;     // partition mode on the matrix-core kernel
   int32_t part_tokens;  // partition mode
   int32_t n_parts;      // partition mode
   int32_t n_wg;         // queue mode: workgroups (0 = partition mode)
@@ -126,8 +127,19 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
   if (max_tokens > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq too large");
   plan->head_chunks = group / gw;
   const int64_t hk = (int64_t)n_kv * plan->head_chunks;
+  // bf16 and fp8 KV at d = 128 run their fixed partitions on the matrix-core
+  // kernel: with fp8 the VALU kernel's dot products, not HBM, set its pace
+  // (1.7x slower on the fp8 serving mix), and with bf16 the two kernels
+  // stream at the same rate or the matrix-core one faster
+  const bool mfma = pkv::decode_mfma_supported(kv_dtype, d, gw);
+  plan->use_mfma = 0;
   int32_t part = partition_tokens;
-  if (part == 0) {
+  if (part == 0 && mfma) {
+    // fewest equal partitions of at most kMaxPartition tokens; the matrix-core
+    // kernel has no work-queue form, so this holds whatever the residency
+    const int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
+    part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + 255) / 256 * 256);
+  } else if (part == 0) {
     // Library's choice.  Cut each (sequence, KV head chunk) into the fewest
     // equal partitions of at most kMaxPartition tokens; if all of those
     // workgroups are resident at once, use them (long per-wave streams, no
@@ -186,6 +198,7 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
     return PKV_OK;
   }
   plan->n_wg = 0;
+  plan->use_mfma = mfma ? 1 : 0;
   plan->merge_splits = 1;
   plan->n_slots = 0;
   plan->items_per_wg = 0;
@@ -318,6 +331,7 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
   info[3] = plan.n_wg ? plan.n_wg : (int32_t)std::min<int64_t>(pairs * plan.n_parts, 0x7fffffff);
   info[4] = (plan.n_wg || plan.n_parts > 1) ? 1 : 0;
   info[5] = (n_q_heads / n_kv_heads) / plan.head_chunks;
+  info[6] = plan.use_mfma;
   return ok();
 }
 
@@ -386,6 +400,7 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.n_kv = n_kv_heads;
   a.group = group;
   a.head_chunks = plan.head_chunks;
+  a.use_mfma = plan.use_mfma;
   a.part_tokens = plan.part_tokens;
   a.n_parts = plan.n_parts;
   a.out_bf16 = out_dtype == PKV_BF16;

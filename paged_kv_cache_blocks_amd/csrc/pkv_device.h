@@ -132,6 +132,34 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---- matrix-core tiles (d = 128, bf16) ----
+// LDS layout of a K or V tile: row r (one token) is 256 bytes, its 16 pieces
+// of 16 bytes with piece c stored in slot c ^ f(r % 16).  f is the
+// permutation 2 (r & 7) + ((r >> 2) ^ (r >> 3)) & 1 of 0..15, chosen so both
+// read patterns hit distinct banks: the score MFMAs read one piece of 16
+// consecutive rows (f is one-to-one, and f & 7 differs within 8 aligned
+// rows), the transposing value reads read pieces {2j, 2j + 1} of 4 (or 8)
+// aligned rows (f >> 1 differs there).
+__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
+__device__ __forceinline__ int swz(int row, int piece) { return row * 256 + ((piece ^ swz_f(row & 15)) << 4); }
+
+// D (16x16, fp32) += A (16x32, bf16) B (32x16, bf16): lane l supplies
+// A[l % 16][8 (l / 16) .. +7] and B[8 (l / 16) .. +7][l % 16] and holds
+// D[4 (l / 16) .. +3][l % 16].
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// ds_read_b64_tr_b16: 8 bytes per lane, transposed across the lanes of a
+// 16-lane row group (the A/B fragment of a product over the rows read).
+__device__ __forceinline__ u32x2 ds_read_tr(const char* p) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 

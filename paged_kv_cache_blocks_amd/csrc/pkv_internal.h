@@ -37,6 +37,7 @@ struct DecodeArgs {
   int32_t part_tokens;
   int32_t n_parts;
   int32_t out_bf16;
+  int32_t use_mfma;     // partition mode: the matrix-core split kernel (decode_mfma.hip)
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -49,6 +50,10 @@ int decode_queue_items_per_wg();           // items the queue kernel aims for pe
 int decode_queue_max_item_blocks();      // largest item the queue kernel makes
 int decode_queue_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch);
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream);
+// matrix-core decode (partition mode only): bf16 / fp8 KV, d = 128, 4, 8 or 16 heads per workgroup
+bool decode_mfma_supported(int kv_kind, int d, int heads_per_wg);
+int decode_mfma_wgs_per_cu(int kv_kind, int heads_per_wg);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_kind, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
                                const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,

@@ -41,16 +41,9 @@ constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
 constexpr int kMaxSortSeqs = 256;  // batches up to this size are ordered longest first
 
-// LDS layout of a tile: row r (key) holds its 16 pieces of 16 bytes with
-// piece c stored in slot c ^ f(r % 16), rows unpadded (the direct
-// global->LDS loads write 1 KiB of consecutive LDS each).  f is the
-// permutation 2 (r & 7) + ((r >> 2) ^ (r >> 3)) & 1 of 0..15, chosen so that
-// both read patterns hit distinct banks: the score MFMAs read one piece of 16
-// consecutive rows (f is one-to-one, and f & 7 differs within 8 aligned
-// rows), the transposing value reads read pieces {2j, 2j + 1} of 4 (or 8)
-// aligned rows (f >> 1 differs there).
-__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
-__device__ __forceinline__ int swz(int row, int piece) { return row * ROWB + ((piece ^ swz_f(row & 15)) << 4); }
+// LDS tiles use the swizzled row layout of swz() (pkv_device.h): rows unpadded, since the
+// direct global->LDS loads write 1 KiB of consecutive LDS each.
+
 
 // 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
 // (global_load_lds_dwordx4, scalar-base form: address = base + off, with the
@@ -72,7 +65,6 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
 }
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 constexpr float kRescaleSlack = 8.f;           // log2 units: weights stay <= 256
@@ -80,17 +72,6 @@ constexpr float kRescaleSlack = 8.f;           // log2 units: weights stay <= 25
 // Keeps a rarely taken branch a branch: without it the compiler may turn the
 // body into selects executed on every tile.
 __device__ __forceinline__ void no_if_conversion() { asm volatile("" ::: "memory"); }
-
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                 0, 0, 0);
-}
-
-__device__ __forceinline__ u32x2 ds_read_tr(const char* p) {
-  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)(__attribute__((address_space(3))) char*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
 
 }  // namespace
 
