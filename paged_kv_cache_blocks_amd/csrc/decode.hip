@@ -198,27 +198,6 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int kvh, int my
 // after_stage() runs once the wave's last chunk is staged and the registers
 // are free (the caller may start the next range's loads there);
 // after_scores() once the last chunk's scores are done and q is free.
-// Wave issue priority from the fraction of its own chunks a wave has done:
-// 3 below half, 2 below 80%, 1 below 95%, then 0.  Two workgroups share each
-// CU and the SIMD arbiter otherwise favours the older wave, so the workgroup
-// dispatched first streams faster and finishes early while its neighbour
-// still runs, leaving the CU half busy at the end.  With this rule a wave
-// that gets ahead drops below its neighbour and the one behind catches up at
-// every step, so co-resident workgroups finish together (in proportion to
-// their work when it differs).  Only the issue order changes, not what is
-// computed.
-// s_setprio is a scalar instruction that ignores the exec mask, so the level
-// is made wave-uniform first: only scalar branches may choose which one runs.
-__device__ __forceinline__ void set_priority_for_progress(int done, int total) {
-  const int level = 20 * done < 10 * total ? 3 : 20 * done < 16 * total ? 2 : 20 * done < 19 * total ? 1 : 0;
-  switch (__builtin_amdgcn_readfirstlane(level)) {
-    case 3: __builtin_amdgcn_s_setprio(3); break;
-    case 2: __builtin_amdgcn_s_setprio(2); break;
-    case 1: __builtin_amdgcn_s_setprio(1); break;
-    default: __builtin_amdgcn_s_setprio(0); break;
-  }
-}
-
 template <int KIND, int D, int GW, class FirstStaged, class AfterStage, class AfterScores>
 __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int L,
                                            int w, int lane, char* wbase, WaveState<KIND, D, GW>& ws,
