@@ -334,7 +334,7 @@ def cpu_baseline(w: DecodeWorkload, sample_layers: int):
 
 def source_hash():
     h = hashlib.sha256()
-    for f in ("decode.hip", "pkv_device.h"):
+    for f in ("decode.hip", "decode_mfma.hip", "pkv_device.h"):
         h.update(open(os.path.join(ROOT, "paged_kv_cache_blocks_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
