@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
                           [] {}, [] {}, [] {});
   merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
     const int hq = h0 + h;
-    if (a.n_parts == 1) {
+    if (a.n_parts == 1 || L <= a.part_tokens) {  // the sequence's only partition: final output
       store_out(a, ((int64_t)s * a.n_q + hq) * D + col, l > 0.f ? o / l : 0.f);
     } else {
       const int64_t pi = ((int64_t)s * a.n_q + hq) * a.n_parts + part;
@@ -582,6 +582,7 @@ __global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
   const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
   const int L = clamp_len(a, s);
   const int nv = (L + a.part_tokens - 1) / a.part_tokens;
+  if (nv == 1) return;  // the split kernel wrote this sequence's output itself
   const int64_t base = ((int64_t)s * a.n_q + hq) * a.n_parts;
   const float* ml = a.ws_ml + base * 2;
   const float* op = a.ws_o + base * D;

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       }
     }
     const int hq = h0 + h;
-    if (a.n_parts == 1) {
+    if (a.n_parts == 1 || L <= a.part_tokens) {  // the sequence's only partition: final output
       put_out(a, ((int64_t)s * a.n_q + hq) * D + col, lsum > 0.f ? osum / lsum : 0.f);
     } else {
       const int64_t pi = ((int64_t)s * a.n_q + hq) * a.n_parts + part;
