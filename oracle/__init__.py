@@ -30,6 +30,7 @@ from .paging import (slot_of, slot_mapping, kv_append, gather_sequence, csr_page
 from .attention import (head_to_kv_head, softmax_attention_rows, paged_decode, paged_prefill,
                         decode_one, prefill_one)
 from .sharing import BlockPool, PoolExhausted, copy_blocks
+from .quant import encode_e4m3fn, append_block_fp8, kv_append_fp8
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_to_f64", "f32_to_f64", "decode_storage",
@@ -38,4 +39,5 @@ __all__ = [
     "head_to_kv_head", "softmax_attention_rows", "paged_decode", "paged_prefill",
     "decode_one", "prefill_one",
     "BlockPool", "PoolExhausted", "copy_blocks",
+    "encode_e4m3fn", "append_block_fp8", "kv_append_fp8",
 ]

@@ -648,3 +648,99 @@ def check_shared_prefix_decode(orc):
 
 
 ALL_CHECKS += [check_cow_fixture, check_cow_invariants, check_copy_blocks, check_shared_prefix_decode]
+
+
+# ---------------------------------------------------------------------------
+# fp8 quantisation on append
+# ---------------------------------------------------------------------------
+
+def check_e4m3_encode(orc):
+    """Every finite code's value encodes to that code; midpoints go to the even
+    code; magnitudes past 448 saturate; random in-range values agree with
+    torch's float8_e4m3fn cast."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = orc.e4m3fn_to_f64(codes)
+    finite = ~np.isnan(vals)
+    back = orc.encode_e4m3fn(vals[finite])
+    assert np.array_equal(back, codes[finite])
+    pos = np.sort(np.unique(vals[finite & (vals >= 0)]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    enc = orc.encode_e4m3fn(mids)
+    lo_codes = orc.encode_e4m3fn(pos[:-1])
+    hi_codes = orc.encode_e4m3fn(pos[1:])
+    want = np.where(lo_codes % 2 == 0, lo_codes, hi_codes)
+    assert np.array_equal(enc, want)
+    assert list(orc.encode_e4m3fn(np.array([449.0, 1e9, -500.0]))) == [0x7E, 0x7E, 0xFE]
+    x = (np.random.default_rng(5).standard_normal(20000) * np.exp2(np.random.default_rng(6).integers(-12, 9, 20000))
+         ).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    t = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.encode_e4m3fn(x), t)
+
+
+def check_fp8_append_fixture(orc):
+    g = _golden("fp8_append.json")
+    B, d = g["block_size"], 2
+    codes = np.zeros((B, d), dtype=np.uint8)
+    scale = np.float32(0)
+    for st in g["steps"]:
+        codes, scale = orc.append_block_fp8(codes, scale, st["n_old"], np.array(st["rows"], dtype=np.float32))
+        n = len(st["codes"])
+        assert [[hex(c) for c in row] for row in codes[:n]] == [[c if c != "0x00" else "0x0" for c in row]
+                                                                for row in st["codes"]], st
+        assert scale == np.float32(st["scale_num"]) / np.float32(448.0)
+
+
+def check_fp8_append_one_shot(orc):
+    """A block filled by one append holds exactly the workload's encoding:
+    scale = largest magnitude / 448 and codes = x / scale cast to E4M3FN
+    (torch's float32 division and cast)."""
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((16, 32)) * 3).astype(np.float32)
+    codes, scale = orc.append_block_fp8(np.zeros((16, 32), np.uint8), np.float32(0), 0, x)
+    tx = torch.from_numpy(x)
+    ts = tx.abs().max() / 448.0
+    assert scale == np.float32(ts.item())
+    assert np.array_equal(codes, (tx / ts).to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+
+
+def check_fp8_append_invariants(orc):
+    """Appending token by token: the scale covers every value appended to the
+    block (scale * 448 >= max |x|), never shrinks, and every stored value is
+    within the rounding of a few E4M3 steps of what was appended."""
+    rng = np.random.default_rng(12)
+    B, n_kv, d, nb = 4, 2, 8, 6
+    k = np.zeros((nb, n_kv, B, d), np.uint8)
+    v = np.zeros_like(k)
+    ks = np.zeros((nb, n_kv), np.float32)
+    vs = np.zeros_like(ks)
+    table = np.array([[3, 1, 5], [0, 2, 4]], dtype=np.int32)
+    lens = [0, 0]
+    hist = {0: [], 1: []}
+    for step in range(9):
+        n = [int(rng.integers(1, 3)), 1]
+        n = [min(n[s], 12 - lens[s]) for s in range(2)]
+        if sum(n) == 0:
+            break
+        kn = (rng.standard_normal((sum(n), n_kv, d)) * rng.choice([0.1, 1, 10])).astype(np.float32)
+        vn = (rng.standard_normal((sum(n), n_kv, d))).astype(np.float32)
+        cu = [0, n[0], n[0] + n[1]]
+        before = ks.copy()
+        k, v, ks, vs = orc.kv_append_fp8(k, v, ks, vs, table, lens, cu, kn, vn, B)
+        for s in range(2):
+            for t in range(n[s]):
+                hist[s].append(kn[cu[s] + t])
+            lens[s] += n[s]
+        touched = ks != before
+        assert np.all(ks[touched] > before[touched]) or not touched.any()
+        for s in range(2):
+            rows = np.array(hist[s])
+            for p in range(lens[s]):
+                blk = table[s][p // B]
+                got = orc.e4m3fn_to_f64(k[blk, :, p % B]) * ks[blk][:, None]
+                assert np.all(ks[blk][:, None] * 448 >= np.abs(rows[p]) * (1 - 1e-6))
+                # each re-encoding adds at most half a step (1/16 relative) plus subnormal steps
+                assert np.all(np.abs(got - rows[p]) <= np.abs(rows[p]) / 8 + ks[blk][:, None] * 2.0 ** -8)
+
+
+ALL_CHECKS += [check_e4m3_encode, check_fp8_append_fixture, check_fp8_append_one_shot, check_fp8_append_invariants]

@@ -48,6 +48,13 @@ MUTATIONS = [
     ("sharing.py", "            self.ref[b] += 1", "            self.ref[b] += 2"),
     ("sharing.py", "        k[dst] = k_cache[src]", "        k[dst] = v_cache[src]"),
     ("sharing.py", "            vs[dst] = v_scale[src]", "            vs[dst] = k_scale[src]"),
+    ("quant.py", "        codes[:n_old] = encode_e4m3fn(vals / new)\n", ""),
+    ("quant.py", "np.float32(m / _F448)", "np.float32(m / np.float32(256.0))"),
+    ("quant.py", "(codes[hi] % 2 == 0)", "(codes[hi] % 2 == 1)"),
+    ("quant.py", "old = np.float32(scale) if n_old > 0 else np.float32(0.0)", "old = np.float32(0.0)"),
+    ("quant.py", "n_old = min(max(ctx - j * B, 0), B)", "n_old = min(max(ctx - j * B - 1, 0), B)"),
+    ("quant.py", "vals = e4m3fn_to_f64(codes[:n_old]).astype(np.float32) * old",
+     "vals = e4m3fn_to_f64(codes[:n_old]).astype(np.float32) * new"),
 ]
 
 
