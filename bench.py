@@ -11,6 +11,9 @@ resident in HBM:
     work, and back-to-back calls keep launch gaps out of the decode timing);
   * prefill workload: slot indexing of the chunk, kv_append of its 8,192
     new rows, chunked-prefill attention.
+With --fp8-append quantize the FP8 workload's append takes the token's rows
+in bf16 and quantises them into the cache (kv_append_fp8: per-block scale
+update, re-encoding when a scale grows) instead of copying ready-made codes.
 The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
 8 KV heads, d 128, lengths uniform in [1024, 2048], 32 layers, bf16 KV).
 
@@ -72,6 +75,13 @@ def append_bytes(tokens, n_kv, d, kv_bytes):
     return tokens * (n_kv * d * kv_bytes * 2 * 2 + 8)
 
 
+def append_fp8_bytes(tokens, n_kv, d, in_bytes):
+    """Read the new bf16/f32 K/V rows and the (block, KV head) scales, write the
+    codes and the scales (the rows of a block whose scale grows are re-read and
+    re-written on top; not counted)."""
+    return tokens * n_kv * 2 * (d * (in_bytes + 1) + 8) + tokens * 4 * 3
+
+
 def slot_bytes(tokens, max_blocks):
     return tokens * (4 + 4 + 4 + 8)
 
@@ -89,7 +99,7 @@ def prefill_flops(ctx_lens, q_len, n_q, d):
 # ---------------------------------------------------------------------------
 
 class DecodeWorkload:
-    def __init__(self, cfg_id: int, layers: int = None):
+    def __init__(self, cfg_id: int, layers: int = None, fp8_append: str = "copy"):
         import torch
         import paged_kv_cache_blocks_amd as pkv
         self.pkv, self.torch = pkv, torch
@@ -98,6 +108,7 @@ class DecodeWorkload:
         self.name = c["name"]
         self.n_q, self.n_kv, self.d, self.kind = c["n_q"], c["n_kv"], c["d"], c["kv_dtype"]
         self.layers = layers or c["layers"]
+        self.quantize_append = self.kind == "fp8" and fp8_append == "quantize"
         self.seq_lens = synth.config_seq_lens(cfg_id)
         self.batch = len(self.seq_lens)
         dev = torch.device("cuda")
@@ -143,11 +154,19 @@ class DecodeWorkload:
             # the step's new token rows: the rows already at each sequence's last slot
             last = torch.from_numpy(self.seq_lens - 1).to(dev).long()
             blk = self.block_table[torch.arange(self.batch, device=dev), last // 16].long()
-            self.k_new.append(kv[0][blk, :, last % 16, :].contiguous())
-            self.v_new.append(kv[1][blk, :, last % 16, :].contiguous())
+            if self.quantize_append:
+                # the token's rows as the model would hand them over: bf16 values
+                # of the codes already there (code x block scale)
+                for j, lst in ((0, self.k_new), (1, self.v_new)):
+                    vals = kv[j][blk, :, last % 16, :].view(torch.float8_e4m3fn).float() * sc[j][blk][:, :, None]
+                    lst.append(vals.to(torch.bfloat16).contiguous())
+            else:
+                self.k_new.append(kv[0][blk, :, last % 16, :].contiguous())
+                self.v_new.append(kv[1][blk, :, last % 16, :].contiguous())
         self.seq_ids = torch.arange(self.batch, dtype=torch.int32, device=dev)
         self.positions = (self.seq_lens_t - 1).to(torch.int32)
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
+        self.cu_new = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
         self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
                     for _ in range(self.layers)]
         ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
@@ -161,8 +180,9 @@ class DecodeWorkload:
         qb = 4 if self.kind == "f32" else 2
         self.layer_bytes = decode_layer_bytes(self.seq_lens, self.n_q, self.n_kv, self.d, kvb, qb, 4,
                                               self.kind == "fp8")
-        self.step_bytes = (slot_bytes(self.batch, self.max_blocks) +
-                           self.layers * (self.layer_bytes + append_bytes(self.batch, self.n_kv, self.d, kvb)))
+        app = (append_fp8_bytes(self.batch, self.n_kv, self.d, 2) if self.quantize_append
+               else append_bytes(self.batch, self.n_kv, self.d, kvb))
+        self.step_bytes = slot_bytes(self.batch, self.max_blocks) + self.layers * (self.layer_bytes + app)
 
     def decode_call(self, layer):
         self.pkv.paged_attn_decode(self.q[layer], self.k[layer], self.v[layer], self.block_table, self.seq_lens_t,
@@ -175,7 +195,11 @@ class DecodeWorkload:
         pkv = self.pkv
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
         for layer in range(self.layers):
-            pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
+            if self.quantize_append:
+                pkv.kv_append_fp8(self.k[layer], self.v[layer], self.ks[layer], self.vs[layer], self.block_table,
+                                  self.positions, self.cu_new, 1, self.k_new[layer], self.v_new[layer])
+            else:
+                pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
         if events is not None:
             events[0].record()
         for layer in range(self.layers):
@@ -198,6 +222,7 @@ class DecodeWorkload:
     def describe(self):
         return {"workload": self.name, "batch": self.batch, "n_q_heads": self.n_q, "n_kv_heads": self.n_kv,
                 "d_head": self.d, "block_size": 16, "layers": self.layers, "kv_dtype": self.kind,
+                **({"append": "quantize bf16 -> fp8"} if self.quantize_append else {}),
                 "mean_seq_len": float(np.mean(self.seq_lens)), "max_blocks_per_seq": int(self.max_blocks),
                 "num_blocks_per_layer": int(self.num_blocks)}
 
@@ -363,6 +388,8 @@ def main():
     ap.add_argument("--workload", default="llama8b-bf16", choices=list(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling only)")
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--fp8-append", choices=["copy", "quantize"], default="copy",
+                    help="FP8 workload: copy ready-made codes, or quantise bf16 rows on append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
@@ -389,7 +416,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
     t_build = time.perf_counter()
-    w = PrefillWorkload(cfg) if prefill else DecodeWorkload(cfg, args.layers)
+    w = PrefillWorkload(cfg) if prefill else DecodeWorkload(cfg, args.layers, args.fp8_append)
     print(f"[bench] built {args.workload} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):

@@ -94,6 +94,44 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
                          const int64_t* slot_mapping, const void* k, const void* v, int32_t num_tokens,
                          int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
 
+/* Append with FP8 quantisation ([KVP] Problem 3: an FP8 cache takes half the
+ * bytes of a 16-bit one; [MEM] "Long-context optimization": quantising the
+ * cached keys and values shrinks the per-token cost).  The pages fix neither
+ * the scale granularity nor how a scale evolves while a block fills token by
+ * token; this library keeps one fp32 scale per (block, KV head) (the FP8
+ * format above) and its rule is:
+ *   - appending rows to (block, KV head) sets
+ *     scale = max(old scale, max |new values| / 448), the old scale counting
+ *     only if the block already holds rows of the sequence;
+ *   - if the scale grew, the block's existing rows are re-encoded:
+ *     code = nearest(e4m3fn(code) * old / new);
+ *   - a new value x is stored as nearest(x / scale); a block whose scale is 0
+ *     (all values zero) stores code 0.
+ * nearest() picks the closest E4M3FN value, ties to an even mantissa field,
+ * magnitudes above 448 saturating to 448, the sign kept (zero included); every
+ * product, quotient and the division by 448 is one fp32 operation.
+ * Sequence s appends its rows cu_new_lens[s] .. cu_new_lens[s+1] - 1 of
+ * k_new / v_new at positions context_lens[s] onwards, through its table row.
+ *   k_cache, v_cache: (device) FP8 [num_blocks][n_kv_heads][B][d_head];
+ *   k_scale, v_scale: (device) f32 [num_blocks][n_kv_heads], read and written;
+ *   block_table: (device) int32 [batch][max_blocks_per_seq];
+ *   context_lens: (device) int32 [batch], tokens already cached;
+ *   cu_new_lens: (device) int32 [batch + 1], nondecreasing, starting at 0;
+ *     each cu_new_lens[s+1] - cu_new_lens[s] <= max_new_len (more is not
+ *     appended past the first max_new_len / B + 1 blocks);
+ *   k_new, v_new: (device) new_dtype (BF16 or F32) [total_new][n_kv_heads][d_head].
+ * A sequence with a negative context length, positions past
+ * max_blocks_per_seq * B and table entries outside [0, num_blocks) are
+ * skipped.  The blocks appended to must be named by one sequence only (a
+ * shared block is copied first: pkv_pool_prepare_append); two sequences
+ * writing one block race.  Supported: block_size 16; d_head 64 or 128;
+ * pointers 16-byte aligned.  batch == 0 or max_new_len == 0 is a no-op. */
+pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             const int32_t* cu_new_lens, int32_t batch, int32_t max_new_len, const void* k_new,
+                             const void* v_new, pkv_dtype new_dtype, int32_t n_kv_heads, int32_t d_head,
+                             int32_t block_size, void* stream);
+
 /* Gather (test/debug export of the block-table walk of [MEM] "Walking the
  * table"): k_out[cu_seq_lens[s] + p][h][:] = k_cache[block_table[s][p / B]][h][p % B][:]
  * for p < seq_lens[s]; same for v.  k_out, v_out: (device)

@@ -1,11 +1,13 @@
 """FP8 E4M3FN quantisation on append.  (Oracle; test infrastructure only.)
 
-The pages name FP8 (one byte per value) for KV caches ("KV cache,
-PagedAttention and FlashAttention", Problem 3, worked answer) and the serving
-workload stores one fp32 scale per (block, KV head) equal to the block's
-largest magnitude divided by 448, the format's largest finite value.  They
-do not say what happens to that scale while a block fills one token at a
-time; the reading used here (listed with the other readings):
+The pages size FP8 KV caches at one byte per value ("KV cache, PagedAttention
+and FlashAttention", Problem 3) and name quantising the cached keys and values
+as a way to shrink the per-token cost ("Memory Management in LLM Serving
+Systems", "Long-context optimization").  They fix neither the scale
+granularity nor the rounding.  Here a (block, KV head) carries one fp32 scale,
+the block's largest magnitude divided by 448 (the format's largest finite
+value), and since the pages do not say what happens to that scale while a
+block fills one token at a time, the reading used is:
 
   * a block's scale only grows: appending rows to a (block, KV head) sets
     scale = max(old scale, max |new values| / 448), the old scale counting

@@ -31,6 +31,8 @@ _SIGS = {
     "pkv_kv_bytes_per_token": ([_i32, _i32, _i32, _i32], _i64),
     "pkv_slot_mapping": ([_vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_kv_append": ([_vp, _vp, ctypes.c_int, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "pkv_kv_append_fp8": ([_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_int, _i32,
+                           _i32, _i32, _vp], ctypes.c_int),
     "pkv_paged_gather": ([_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
                           _vp],
                          ctypes.c_int),
@@ -155,6 +157,33 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.
         raise ValueError("k, v must be [num_tokens, n_kv, d]")
     _check(load().pkv_kv_append(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, _ptr(slot_mapping), _ptr(k),
                              _ptr(v), slot_mapping.numel(), n_kv, d, bs, _stream(stream)))
+
+
+def kv_append_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                  block_table: torch.Tensor, context_lens: torch.Tensor, cu_new_lens: torch.Tensor, max_new_len: int,
+                  k_new: torch.Tensor, v_new: torch.Tensor, stream=None) -> None:
+    """Quantise and append each sequence's new rows ([total_new, n_kv, d], bf16
+    or f32) to one layer's FP8 caches at positions context_lens[s] onwards,
+    updating the per-(block, KV head) scales (``pkv_kv_append_fp8``)."""
+    nb, n_kv, bs, d = k_cache.shape
+    if dtype_code(k_cache) != FP8_E4M3FN or v_cache.shape != k_cache.shape or dtype_code(v_cache) != FP8_E4M3FN:
+        raise TypeError("k_cache and v_cache must be matching FP8 caches")
+    _need(k_scale, torch.float32, "k_scale")
+    _need(v_scale, torch.float32, "v_scale")
+    if k_scale.shape != (nb, n_kv) or v_scale.shape != (nb, n_kv):
+        raise ValueError("scales must be [num_blocks, n_kv]")
+    _need(block_table, torch.int32, "block_table")
+    _need(context_lens, torch.int32, "context_lens")
+    _need(cu_new_lens, torch.int32, "cu_new_lens")
+    batch = context_lens.numel()
+    if cu_new_lens.numel() != batch + 1 or block_table.shape[0] != batch:
+        raise ValueError("cu_new_lens must hold batch + 1 entries and block_table batch rows")
+    if k_new.dtype != v_new.dtype or k_new.shape != v_new.shape or k_new.dim() != 3 or k_new.shape[1:] != (n_kv, d):
+        raise ValueError("k_new, v_new must be [total_new, n_kv, d] of one dtype")
+    _check(load().pkv_kv_append_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), nb,
+                                    _ptr(block_table), block_table.shape[1], _ptr(context_lens), _ptr(cu_new_lens),
+                                    batch, int(max_new_len), _ptr(k_new), _ptr(v_new), dtype_code(k_new), n_kv, d, bs,
+                                    _stream(stream)))
 
 
 def paged_gather(k_cache, v_cache, block_table, seq_lens, cu_seq_lens, total_tokens: int, stream=None):

@@ -118,6 +118,150 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_c
   if (scale != nullptr && piece < n_kv) scale[d * n_kv + piece] = scale[s * n_kv + piece];
 }
 
+// ---- fp8 E4M3FN quantisation on append ----
+// float -> E4M3FN code: nearest value, ties to an even mantissa field,
+// magnitudes above 448 saturating to 448 (OCP 8-bit floating point: round to
+// nearest even, E4M3FN has no infinities).  Inputs are finite.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.f);  // subnormals: m * 2^-9 (8 is the smallest normal, 0x08)
+  } else {
+    const uint32_t ab = __float_as_uint(a);
+    int e = (int)(ab >> 23) - 127;  // -6 .. 8
+    const uint32_t man = ab & 0x7FFFFFu;
+    uint32_t m = man >> 20;
+    const uint32_t rem = man & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) {
+      m = 0u;
+      ++e;
+    }
+    code = ((uint32_t)(e + 7) << 3) | m;  // at most (15, 6): 448
+  }
+  return sign | code;
+}
+
+// E4M3FN code (not NaN) -> its exact float value
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float mag = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// D / 64 consecutive values of one row, widened to float
+template <typename TIn, int N>
+__device__ __forceinline__ void load_row_part(const TIn* p, float (&x)[N]) {
+  if constexpr (sizeof(TIn) == 2) {
+    if constexpr (N == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+      x[0] = __uint_as_float(w << 16);
+      x[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      x[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+    }
+  } else {
+    if constexpr (N == 2) {
+      const float2 w = *reinterpret_cast<const float2*>(p);
+      x[0] = w.x;
+      x[1] = w.y;
+    } else {
+      x[0] = *reinterpret_cast<const float*>(p);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void store_codes(uint8_t* p, const uint32_t (&c)[N]) {
+  if constexpr (N == 2)
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)(c[0] | (c[1] << 8));
+  else
+    *p = (uint8_t)c[0];
+}
+
+// Workgroup per (sequence, logical block touched by the append), one wave per
+// (KV head, K|V) pair.  The block's new scale is max(old scale, max |new
+// values| / 448) (the old one only if the block already holds rows of the
+// sequence); when it grows, the existing rows are re-encoded (code * old /
+// new); the new rows are encoded as x / scale.  A wave walks the block's rows
+// with lane l holding values l * D/64 ...: a first pass over the new rows
+// finds their largest magnitude, a second encodes them (the first row's
+// values stay in registers, later rows are read again from cache).
+template <int D, typename TIn>
+__global__ __launch_bounds__(1024) void kv_append_fp8_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
+                                                            float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                            int64_t num_blocks, const int32_t* __restrict__ table,
+                                                            int32_t max_blocks, const int32_t* __restrict__ ctx_lens,
+                                                            const int32_t* __restrict__ cu_new,
+                                                            const TIn* __restrict__ k_new,
+                                                            const TIn* __restrict__ v_new, int32_t n_kv) {
+  constexpr int B = 16, VPL = D / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int pair = (int)blockIdx.z * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
+  if (pair >= 2 * n_kv) return;
+  const int h = pair >> 1, is_v = pair & 1, s = blockIdx.y;
+  const int ctx = ctx_lens[s], t0 = cu_new[s], n = cu_new[s + 1] - t0;
+  if (ctx < 0 || n <= 0) return;
+  const int j = ctx / B + (int)blockIdx.x;  // logical block
+  if (j * B >= ctx + n || j >= max_blocks) return;
+  const int32_t raw = table[(int64_t)s * max_blocks + j];
+  if (raw < 0 || raw >= num_blocks) return;
+  const int64_t blk = raw;
+  const int n_old = max(min(ctx - j * B, B), 0);  // rows the block already holds
+  const int lo = max(ctx, j * B) - ctx;           // first new row of the block, relative to t0
+  const int cnt = min(ctx + n, (j + 1) * B) - ctx - lo;
+  uint8_t* const codes = (is_v ? v_cache : k_cache) + (blk * n_kv + h) * B * D + lane * VPL;
+  float* const sc = (is_v ? v_scale : k_scale) + blk * n_kv + h;
+  const float sc_in = *sc;
+  const int64_t stride = (int64_t)n_kv * D;
+  const TIn* const src = (is_v ? v_new : k_new) + ((int64_t)(t0 + lo) * n_kv + h) * D + lane * VPL;
+
+  float x0[VPL];
+  load_row_part(src, x0);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) m = fmaxf(m, fabsf(x0[e]));
+  for (int i = 1; i < cnt; ++i) {
+    float x[VPL];
+    load_row_part(src + i * stride, x);
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
+  m = group_max<kWave>(m);
+  const float old = n_old > 0 ? sc_in : 0.f;
+  const float nw = fmaxf(old, m / 448.f);
+  if (nw > old) {
+    for (int r = 0; r < n_old; ++r) {
+      uint32_t c[VPL];
+      if constexpr (VPL == 2) {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(codes + r * D);
+        c[0] = f32_to_e4m3fn((e4m3fn_to_f32(w & 0xFFu) * old) / nw);
+        c[1] = f32_to_e4m3fn((e4m3fn_to_f32(w >> 8) * old) / nw);
+      } else {
+        c[0] = f32_to_e4m3fn((e4m3fn_to_f32(codes[r * D]) * old) / nw);
+      }
+      store_codes(codes + r * D, c);
+    }
+  }
+  {
+    uint32_t c[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) c[e] = nw > 0.f ? f32_to_e4m3fn(x0[e] / nw) : 0u;
+    store_codes(codes + n_old * D, c);
+  }
+  for (int i = 1; i < cnt; ++i) {
+    float x[VPL];
+    load_row_part(src + i * stride, x);
+    uint32_t c[VPL];
+#pragma unroll
+    for (int e = 0; e < VPL; ++e) c[e] = nw > 0.f ? f32_to_e4m3fn(x[e] / nw) : 0u;
+    store_codes(codes + (n_old + i) * D, c);
+  }
+  if (lane == 0) *sc = nw;
+}
+
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
                                const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,
                                hipStream_t stream) {
@@ -166,6 +310,30 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)gx, (unsigned)n_pairs, 2), dim3(256), 0, stream,
                      static_cast<char*>(k_cache), static_cast<char*>(v_cache), k_scale, v_scale, num_blocks, src, dst,
                      block_bytes, n_kv);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                                 const int32_t* table, int32_t max_blocks, const int32_t* ctx_lens,
+                                 const int32_t* cu_new, int32_t batch, int32_t max_new, const void* k_new,
+                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, hipStream_t stream) {
+  if (batch == 0 || max_new == 0) return hipSuccess;
+  // n consecutive rows starting anywhere in a block touch at most (n + 14) / 16 + 1 blocks
+  const int gx = (max_new + 14) / 16 + 1;
+  const int pairs = 2 * n_kv, waves = pairs < 16 ? pairs : 16;
+  const dim3 grid((unsigned)gx, (unsigned)batch, (unsigned)((pairs + waves - 1) / waves));
+  const dim3 block((unsigned)(waves * kWave));
+  auto* kc = static_cast<uint8_t*>(k_cache);
+  auto* vc = static_cast<uint8_t*>(v_cache);
+#define PKV_APPEND_FP8(DD, T)                                                                                   \
+  hipLaunchKernelGGL((kv_append_fp8_kernel<DD, T>), grid, block, 0, stream, kc, vc, k_scale, v_scale,          \
+                     num_blocks, table, max_blocks, ctx_lens, cu_new, static_cast<const T*>(k_new),             \
+                     static_cast<const T*>(v_new), n_kv)
+  if (d == 128 && new_bytes == 2) PKV_APPEND_FP8(128, uint16_t);
+  else if (d == 128) PKV_APPEND_FP8(128, float);
+  else if (new_bytes == 2) PKV_APPEND_FP8(64, uint16_t);
+  else PKV_APPEND_FP8(64, float);
+#undef PKV_APPEND_FP8
   return hipGetLastError();
 }
 

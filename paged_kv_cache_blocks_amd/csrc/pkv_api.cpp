@@ -275,6 +275,33 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
                     "kv_append launch");
 }
 
+pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             const int32_t* cu_new_lens, int32_t batch, int32_t max_new_len, const void* k_new,
+                             const void* v_new, pkv_dtype new_dtype, int32_t n_kv_heads, int32_t d_head,
+                             int32_t block_size, void* stream) {
+  if (batch < 0 || max_new_len < 0) return fail(PKV_ERR_INVALID_ARG, "batch and max_new_len must be >= 0");
+  if (new_dtype != PKV_BF16 && new_dtype != PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "new K/V must be BF16 or F32 (got dtype %d)", (int)new_dtype);
+  if (batch == 0 || max_new_len == 0) return ok();
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !cu_new_lens || !k_new ||
+      !v_new)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  if (d_head != 64 && d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d (supported: 64, 128)", d_head);
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "table too wide");
+  if (batch > 65535 || 2 * n_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) & 15)
+    return fail(PKV_ERR_UNSUPPORTED, "caches and new K/V must be 16-byte aligned");
+  return hip_status(pkv::launch_kv_append_fp8(k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
+                                              max_blocks_per_seq, context_lens, cu_new_lens, batch, max_new_len,
+                                              k_new, v_new, new_dtype == PKV_BF16 ? 2 : 4, n_kv_heads, d_head,
+                                              (hipStream_t)stream),
+                    "kv_append_fp8 launch");
+}
+
 pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
                             int64_t num_blocks, const int32_t* block_table, int32_t max_blocks_per_seq,
                             const int32_t* seq_lens, const int64_t* cu_seq_lens, int64_t total_tokens, int32_t batch,

@@ -68,6 +68,10 @@ hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const vo
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
                               const int32_t* src, const int32_t* dst, int32_t n_pairs, int64_t block_bytes,
                               int32_t n_kv, hipStream_t stream);
+hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                                 const int32_t* table, int32_t max_blocks, const int32_t* ctx_lens,
+                                 const int32_t* cu_new, int32_t batch, int32_t max_new, const void* k_new,
+                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
 

@@ -103,6 +103,22 @@ def test_other_entry_points_validate(pkv):
     assert lib.pkv_kv_append(None, None, 1, 1, None, None, None, 0, 8, 128, 16, None) == pkv.OK
     assert lib.pkv_kv_append(0x1000, 0x1000, 7, 1, 0x1000, 0x1000, 0x1000, 1, 8, 128, 16, None) == pkv.ERR_INVALID_ARG
     assert lib.pkv_kv_append(0x1000, 0x1000, 2, 1, 0x1000, 0x1000, 0x1000, 1, 8, 8, 16, None) == pkv.ERR_UNSUPPORTED
+    fa = lib.pkv_kv_append_fp8
+    good = [0x1000, 0x2000, 0x3000, 0x4000, 8, 0x5000, 2, 0x6000, 0x7000, 1, 4, 0x8000, 0x9000, 1, 2, 128, 16, None]
+    args = list(good); args[10] = 0
+    assert fa(*args) == pkv.OK                       # max_new_len 0: no-op
+    args = list(good); args[13] = 2
+    assert fa(*args) == pkv.ERR_UNSUPPORTED          # new rows already FP8
+    args = list(good); args[16] = 8
+    assert fa(*args) == pkv.ERR_UNSUPPORTED          # block size 8
+    args = list(good); args[15] = 96
+    assert fa(*args) == pkv.ERR_UNSUPPORTED          # d 96
+    args = list(good); args[11] = 0x8004
+    assert fa(*args) == pkv.ERR_UNSUPPORTED          # misaligned new K
+    args = list(good); args[2] = None
+    assert fa(*args) == pkv.ERR_INVALID_ARG          # no scales
+    args = list(good); args[9] = -1
+    assert fa(*args) == pkv.ERR_INVALID_ARG          # negative batch
     assert lib.pkv_paged_gather(0x1000, 0x1000, 0x1000, 0x1000, 1, 4, 0x1000, 2, 0x1000, 0x1000, 0, 1, 2, 64, 16,
                                 None) == pkv.OK
     assert lib.pkv_check_tables(None, 1, None, 1, 1, 16, None, None) == pkv.ERR_INVALID_ARG
