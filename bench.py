@@ -230,10 +230,11 @@ class DecodeWorkload:
 class PrefillWorkload:
     calls_per_event = 1
 
-    def __init__(self, cfg_id: int = 5):
+    def __init__(self, cfg_id: int = 5, kv: str = "bf16"):
         import torch
         import paged_kv_cache_blocks_amd as pkv
         self.pkv, self.torch = pkv, torch
+        self.kind = kv
         c = synth.CONFIGS[cfg_id]
         self.name = c["name"]
         self.n_q, self.n_kv, self.d = c["n_q"], c["n_kv"], c["d"]
@@ -247,8 +248,19 @@ class PrefillWorkload:
         table, _ = synth.build_tables(total, self.num_blocks, perm)
         self.block_table = torch.from_numpy(table).to(dev)
         shape = (self.num_blocks, self.n_kv, 16, self.d)
-        self.k = synth.device_normal_(torch.empty(shape, device=dev), 5001).to(torch.bfloat16)
-        self.v = synth.device_normal_(torch.empty(shape, device=dev), 5002).to(torch.bfloat16)
+        self.ks = self.vs = None
+        if kv == "fp8":
+            # codes and per-(block, KV head) scales = max |x| / 448 over the block
+            cs = []
+            for seed in (5001, 5002):
+                x = synth.device_normal_(torch.empty(shape, device=dev), seed)
+                sc = (x.abs().amax(dim=(2, 3)) / 448.0).float().contiguous()
+                cs.append(((x / sc[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), sc))
+                del x
+            (self.k, self.ks), (self.v, self.vs) = cs
+        else:
+            self.k = synth.device_normal_(torch.empty(shape, device=dev), 5001).to(torch.bfloat16)
+            self.v = synth.device_normal_(torch.empty(shape, device=dev), 5002).to(torch.bfloat16)
         nq = len(self.ctx) * self.q_len
         self.q = synth.device_normal_(torch.empty((nq, self.n_q, self.d), device=dev), 5003).to(torch.bfloat16)
         self.seq_ids = torch.repeat_interleave(torch.arange(len(self.ctx), dtype=torch.int32), self.q_len).to(dev)
@@ -266,12 +278,18 @@ class PrefillWorkload:
 
     def attn_call(self):
         self.pkv.paged_attn_prefill_chunk(self.q, self.cu, self.ctx_t, self.q_len, self.k, self.v, self.block_table,
-                                          self.n_q, self.n_kv, self.d, 16, self.scale, out=self.out)
+                                          self.n_q, self.n_kv, self.d, 16, self.scale, out=self.out,
+                                          k_scale=self.ks, v_scale=self.vs)
 
     def step(self, events=None):
         pkv = self.pkv
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
-        pkv.kv_append(self.k, self.v, self.slots, self.k_new, self.v_new)
+        if self.kind == "fp8":
+            # the chunk's bf16 rows are quantised into the cache
+            pkv.kv_append_fp8(self.k, self.v, self.ks, self.vs, self.block_table, self.ctx_t, self.cu, self.q_len,
+                              self.k_new, self.v_new)
+        else:
+            pkv.kv_append(self.k, self.v, self.slots, self.k_new, self.v_new)
         if events is not None:
             events[0].record()
         self.attn_call()
@@ -280,7 +298,8 @@ class PrefillWorkload:
 
     def describe(self):
         return {"workload": self.name, "num_seqs": len(self.ctx), "q_len": self.q_len, "n_q_heads": self.n_q,
-                "n_kv_heads": self.n_kv, "d_head": self.d, "block_size": 16, "mean_ctx": float(np.mean(self.ctx))}
+                "n_kv_heads": self.n_kv, "d_head": self.d, "block_size": 16, "kv_dtype": self.kind,
+                "mean_ctx": float(np.mean(self.ctx))}
 
 
 # ---------------------------------------------------------------------------
@@ -390,6 +409,8 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--fp8-append", choices=["copy", "quantize"], default="copy",
                     help="FP8 workload: copy ready-made codes, or quantise bf16 rows on append")
+    ap.add_argument("--prefill-kv", choices=["bf16", "fp8"], default="bf16",
+                    help="prefill workload: KV cache element type (fp8: the chunk is quantised on append)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
@@ -416,7 +437,7 @@ def main():
     cfg = WORKLOADS[args.workload]
     prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
     t_build = time.perf_counter()
-    w = PrefillWorkload(cfg) if prefill else DecodeWorkload(cfg, args.layers, args.fp8_append)
+    w = PrefillWorkload(cfg, args.prefill_kv) if prefill else DecodeWorkload(cfg, args.layers, args.fp8_append)
     print(f"[bench] built {args.workload} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -440,7 +461,7 @@ def main():
         rec = {"metric": "chunked prefill over a paged cache: achieved TFLOP/s (bf16 MFMA)", "value": round(tflops, 3),
                "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), config-5 shapes)",
+               "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
                "config": w.describe(),
                "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,

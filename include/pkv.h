@@ -295,15 +295,19 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
  * With causal = 1, query i attends keys 0 .. context_lens[s] + i; with
  * causal = 0, every key of the context and the chunk ([MEM] "FlashAttention":
  * masked positions get -inf and fully masked blocks are skipped).  The chunk's
- * own K/V must already be appended to the cache (pkv_kv_append).  Computed
- * with bf16 MFMA tiles, fp32 accumulation and an online softmax per query row;
- * the softmax weights enter the value product as bf16.
+ * own K/V must already be appended to the cache (pkv_kv_append or
+ * pkv_kv_append_fp8).  Computed with bf16 MFMA tiles, fp32 accumulation and an
+ * online softmax per query row; the softmax weights enter the value product as
+ * bf16.  FP8 caches ([KVP] Problem 3) are widened to bf16 exactly; a key's K
+ * scale multiplies its score and its V scale its weight in the value product
+ * (k_scale, v_scale: (device) f32 [num_blocks][n_kv_heads], required for FP8,
+ * ignored otherwise).
  *   q, out: (device) packed [total_q][n_q_heads][d_head];
  *   cu_q_lens: (device) int32 [num_seqs + 1], cu_q_lens[0] = 0, nondecreasing,
  *   cu_q_lens[num_seqs] = total_q, each q_len <= max_q_len;
  *   context_lens: (device) int32 [num_seqs];
  *   context_lens[s] + q_len <= max_blocks_per_seq * B.
- * Supported: d_head 128; block_size 16; q and KV BF16; out F32 or BF16.
+ * Supported: d_head 128; block_size 16; q BF16; KV BF16 or FP8; out F32 or BF16.
  * workspace: pkv_paged_attn_prefill_workspace(...) bytes (may be 0, then the
  * pointer may be NULL). */
 pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,

@@ -320,8 +320,9 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
 
 def paged_attn_prefill_chunk(q, cu_q_lens, context_lens, max_q_len, k_cache, v_cache, block_table, n_q_heads,
                              n_kv_heads, d_head, block_size, scale, *, causal: bool = True, out=None,
-                             out_dtype=torch.float32, stream=None) -> torch.Tensor:
-    """Packed chunk queries [total_q, n_q, d] against cached context + chunk (already appended)."""
+                             out_dtype=torch.float32, k_scale=None, v_scale=None, stream=None) -> torch.Tensor:
+    """Packed chunk queries [total_q, n_q, d] against cached context + chunk (already appended);
+    FP8 caches take their per-(block, KV head) scales in k_scale / v_scale."""
     total_q = q.shape[0]
     _need(cu_q_lens, torch.int32, "cu_q_lens")
     _need(context_lens, torch.int32, "context_lens")
@@ -330,7 +331,8 @@ def paged_attn_prefill_chunk(q, cu_q_lens, context_lens, max_q_len, k_cache, v_c
         out = torch.empty((total_q, n_q_heads, d_head), dtype=out_dtype, device=q.device)
     _check(load().pkv_paged_attn_prefill_chunk(
         _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(cu_q_lens), _ptr(context_lens),
-        context_lens.numel(), total_q, int(max_q_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), None, None,
+        context_lens.numel(), total_q, int(max_q_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale),
         _ptr(block_table), block_table.shape[1], k_cache.shape[0], n_q_heads, n_kv_heads, d_head, block_size,
         float(scale), 1 if causal else 0, None, 0, _stream(stream)))
     return out

@@ -464,8 +464,6 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
                                         int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads,
                                         int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale,
                                         int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)k_scale;
-  (void)v_scale;
   (void)workspace;
   (void)workspace_bytes;
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
@@ -480,7 +478,10 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
   if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
   if (d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "prefill supports d_head 128 only");
-  if (q_dtype != PKV_BF16 || kv_dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 q and KV");
+  if (q_dtype != PKV_BF16 || kv_dtype == PKV_F32)
+    return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 q and bf16 or fp8 KV");
+  if (kv_dtype == PKV_FP8_E4M3FN && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "fp8 caches need k_scale and v_scale");
   if (out_dtype == PKV_FP8_E4M3FN) return fail(PKV_ERR_UNSUPPORTED, "fp8 output unsupported");
   const int group = n_q_heads / n_kv_heads;
   if (!pkv::prefill_supported_group(group))
@@ -496,6 +497,8 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   a.ctx_lens = context_lens;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.block_table = block_table;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
@@ -507,6 +510,7 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   a.group = group;
   a.causal = causal;
   a.out_bf16 = out_dtype == PKV_BF16;
+  a.kv_fp8 = kv_dtype == PKV_FP8_E4M3FN;
   a.scale_log2 = scale * kLog2e;
   return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
 }

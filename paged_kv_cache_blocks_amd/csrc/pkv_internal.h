@@ -82,6 +82,8 @@ struct PrefillArgs {
   const int32_t* ctx_lens;
   const void* k_cache;
   const void* v_cache;
+  const float* k_scale;  // FP8 KV: per (block, KV head)
+  const float* v_scale;
   const int32_t* block_table;
   int64_t num_blocks;
   int32_t num_seqs;
@@ -93,6 +95,7 @@ struct PrefillArgs {
   int32_t group;
   int32_t causal;
   int32_t out_bf16;
+  int32_t kv_fp8;
   float scale_log2;
 };
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream);

@@ -22,6 +22,13 @@
 //     row (in-lane max over 16 keys + two cross-lane steps);
 //     P^T (bf16) is already in the B-operand layout of the next product, so
 //     O^T += V^T P^T uses V^T fragments read with ds_read_b64_tr_b16.
+//   FP8 KV: each wave brings its block's codes (half the bytes) into a
+//   double-buffered staging area and, once the previous tile is consumed,
+//   widens them to bf16 (exact) into the same single tile layout; each
+//   16-key score tile is one cache block, so its K scale multiplies that
+//   tile's scores, and the V scale of a key's block multiplies the key's
+//   softmax weight as it is packed for the value product (the row sum takes
+//   the weights unscaled).
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -40,6 +47,9 @@ constexpr int STAGE_B = 2 * TILE_B;  // K tile then V tile
 constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
 constexpr int kMaxSortSeqs = 256;  // batches up to this size are ordered longest first
+constexpr int BLK8_B = BS * D;     // one block's K (or V) codes, FP8
+constexpr int STG8_B = (KT / BS) * 2 * BLK8_B;  // one tile's K and V codes
+static_assert(STAGE_B + 2 * STG8_B <= kStages * STAGE_B, "FP8 tile + staging must fit the bf16 stages");
 
 // LDS tiles use the swizzled row layout of swz() (pkv_device.h): rows unpadded, since the
 // direct global->LDS loads write 1 KiB of consecutive LDS each.
@@ -75,8 +85,12 @@ __device__ __forceinline__ void no_if_conversion() { asm volatile("" ::: "memory
 
 }  // namespace
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  // bf16 KV: kStages tiles (K then V).  FP8 KV: one bf16 tile at the start,
+  // then two staging buffers of codes, per wave [K block][V block].
   __shared__ __align__(16) char smem[kStages * STAGE_B];
+  __shared__ float blk_scale[2][KT / BS];  // FP8: K and V scale of the tile's blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,16 +213,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     src_off[k] = r * ROWB + (((lane & 15) ^ swz_f(r)) << 4);
   }
   const uint32_t lds0 = lds_addr(smem) + BS * w * ROWB;  // this wave's first tile row
+  // FP8: this wave's staging slot and the scales of the block it loads
+  const uint32_t stg0 = lds_addr(smem) + STAGE_B + w * 2 * BLK8_B;
+  float ks_load = 0.f, vs_load = 0.f;  // scales of the block last issued (0 when none)
   auto issue = [&](int kt, int raw_id) {
     const int lb = kt * (KT / BS) + w;
+    if (FP8) {
+      ks_load = 0.f;
+      vs_load = 0.f;
+    }
     if (lb >= n_lblocks || lb >= a.max_blocks) return;  // nothing to load for this wave
     const int id = min(max(__builtin_amdgcn_readfirstlane(raw_id), 0), (int)(a.num_blocks - 1));
-    const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
-    const uint32_t dst = lds0 + (kt % kStages) * STAGE_B;
+    if (FP8) {
+      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * BLK8_B;
+      const uint32_t dst = stg0 + (kt & 1) * STG8_B;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lds_dma16(kc + slab, src_off[k], dst + 4 * k * ROWB);
-      lds_dma16(vc + slab, src_off[k], dst + TILE_B + 4 * k * ROWB);
+      for (int k = 0; k < 2; ++k) {
+        lds_dma16(kc + slab, k * 1024 + 16 * lane, dst + k * 1024);
+        lds_dma16(vc + slab, k * 1024 + 16 * lane, dst + BLK8_B + k * 1024);
+      }
+      ks_load = a.k_scale[(int64_t)id * a.n_kv + kvh];
+      vs_load = a.v_scale[(int64_t)id * a.n_kv + kvh];
+    } else {
+      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
+      const uint32_t dst = lds0 + (kt % kStages) * STAGE_B;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        lds_dma16(kc + slab, src_off[k], dst + 4 * k * ROWB);
+        lds_dma16(vc + slab, src_off[k], dst + TILE_B + 4 * k * ROWB);
+      }
     }
   };
   int id_next = 0;
@@ -219,10 +252,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   const float sl = a.scale_log2;
   for (int kt = 0; kt < n_tiles; ++kt) {
-    const char* const k_lds = smem + (kt % kStages) * STAGE_B;
+    const char* const k_lds = smem + (FP8 ? 0 : (kt % kStages) * STAGE_B);
     const char* const v_lds = k_lds + TILE_B;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt have landed
-    if (kt * KT + KT > kv_end) {
+    const float ks_tile = ks_load, vs_tile = vs_load;  // FP8: scales of this wave's block of tile kt
+    if (!FP8 && kt * KT + KT > kv_end) {
       // the keys this workgroup sees end inside this tile: V rows past them
       // (rows no load wrote, or past the sequence end) may hold anything, NaN
       // included, and the zero weights every real row gives them must not
@@ -237,6 +271,42 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     if (kt + 1 < n_tiles) {
       issue(kt + 1, id_next);
       if (kt + 2 < n_tiles) id_next = fetch_id(kt + 2);
+    }
+    float ksc[KT / BS], vsc[KT / BS];
+    if (FP8) {
+      // widen this wave's block of codes into rows 16w .. 16w+15 of the bf16
+      // tile: lane l converts row l / 4, values 32 (l % 4) .. +31; V rows past
+      // the keys the tile sees become zeros (their weights are zero, and a
+      // zero weight must not meet a NaN)
+      const char* stg = smem + STAGE_B + (kt & 1) * STG8_B + w * 2 * BLK8_B;
+      const int r = lane >> 2, c = (lane & 3) * 32;
+      const int row = BS * w + r;
+      const bool live = kt * KT + row < kv_end;
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const u32x4 c0 = ld16(stg + kv * BLK8_B + r * D + c);
+        const u32x4 c1 = ld16(stg + kv * BLK8_B + r * D + c + 16);
+        const uint32_t cw[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        uint32_t bw[16];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) fp8x4_to_bf16x4(cw[i], bw[2 * i], bw[2 * i + 1]);
+        const bool keep = kv == 0 || live;
+        char* dst = smem + kv * TILE_B;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          st16(dst + swz(row, (lane & 3) * 4 + i),
+               keep ? u32x4{bw[4 * i], bw[4 * i + 1], bw[4 * i + 2], bw[4 * i + 3]} : u32x4{0, 0, 0, 0});
+      }
+      if (lane == 0) {
+        blk_scale[0][w] = ks_tile;
+        blk_scale[1][w] = vs_tile;
+      }
+      __syncthreads();  // the bf16 tile and its scales are complete
+#pragma unroll
+      for (int t = 0; t < KT / BS; ++t) {
+        ksc[t] = blk_scale[0][t];
+        vsc[t] = blk_scale[1][t];
+      }
     }
 
     // ---- S^T = K Q^T : four 16-key tiles x NT row tiles
@@ -261,6 +331,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf[ds & 1][t], qf[nt][ds], st_[t][nt]);
+    }
+
+    if (FP8) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st_[t][nt] *= ksc[t];
     }
 
     // ---- mask, online softmax, P^T fragments.  The reference max m is kept
@@ -305,11 +382,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         float p4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) p4[j] = exp2_fast(fmaf(st_[t][nt][j], sl, -m_use));
-        pk[t][0] = pack_bf16(p4[0], p4[1]);
-        pk[t][1] = pack_bf16(p4[2], p4[3]);
-        // the row sum takes the same bf16-rounded weights the product uses
-        ls = dot2_bf16(pk[t][0], kOnesBf16x2, ls);
-        ls = dot2_bf16(pk[t][1], kOnesBf16x2, ls);
+        if (FP8) {
+          // weights enter the value product scaled by their block's V scale
+          ls += (p4[0] + p4[1]) + (p4[2] + p4[3]);
+          pk[t][0] = pack_bf16(p4[0] * vsc[t], p4[1] * vsc[t]);
+          pk[t][1] = pack_bf16(p4[2] * vsc[t], p4[3] * vsc[t]);
+        } else {
+          pk[t][0] = pack_bf16(p4[0], p4[1]);
+          pk[t][1] = pack_bf16(p4[2], p4[3]);
+          // the row sum takes the same bf16-rounded weights the product uses
+          ls = dot2_bf16(pk[t][0], kOnesBf16x2, ls);
+          ls = dot2_bf16(pk[t][1], kOnesBf16x2, ls);
+        }
       }
       l_run[nt] = l_run[nt] * alpha + ls;
 #pragma unroll
@@ -372,7 +456,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream) {
   const int64_t n_work = (int64_t)((a.max_q_len + tq - 1) / tq) * a.n_kv * a.num_seqs;
   if (n_work == 0) return hipSuccess;
   if (n_work > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)n_work), dim3(256), 0, stream, a);
+  if (a.kv_fp8)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)n_work), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)n_work), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -208,6 +208,8 @@ class PrefillCase:
     positions: np.ndarray    # int32 [total_q]
     block_table: np.ndarray
     scale: float
+    k_scale: Optional[np.ndarray] = None  # FP8: float32 [num_blocks, n_kv]
+    v_scale: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -306,12 +308,17 @@ def make_prefill_case(*, config: int, layer: int, n_q: int, n_kv: int, d: int, c
     # the chunk's new rows are the pool values at their slots
     blk = table[seq_ids, positions // block_size]
     off = positions % block_size
-    knf = kf[blk, :, off, :]
-    vnf = vf[blk, :, off, :]
-    if kv_dtype == FP8:
-        raise NotImplementedError("fp8 prefill inputs are not part of the prefill workloads")
-    kc, vc = encode(kf, kv_dtype), encode(vf, kv_dtype)
     keep = filled_all if chunk_in_cache else ctx_mask
+    k_scale = v_scale = None
+    if kv_dtype == FP8:
+        # scales over every slot the sequences will hold (context and chunk),
+        # so appending the chunk's codes leaves them valid
+        k_scale = fp8_block_scales(kf, filled_all)
+        v_scale = fp8_block_scales(vf, filled_all)
+        kc, vc = quantize_fp8(kf, k_scale), quantize_fp8(vf, v_scale)
+    else:
+        kc, vc = encode(kf, kv_dtype), encode(vf, kv_dtype)
+    k_new_rows, v_new_rows = kc[blk, :, off, :], vc[blk, :, off, :]
     if poison:
         mask = np.broadcast_to(~keep[:, None, :, None], kc.shape)
         kc = np.where(mask, POISON[kv_dtype], kc)
@@ -319,9 +326,9 @@ def make_prefill_case(*, config: int, layer: int, n_q: int, n_kv: int, d: int, c
     return PrefillCase(n_q=n_q, n_kv=n_kv, d=d, block_size=block_size, kv_dtype=kv_dtype, q_dtype=BF16,
                        q=encode(qf, BF16), cu_q_lens=cu, context_lens=context_lens,
                        k_cache=np.ascontiguousarray(kc), v_cache=np.ascontiguousarray(vc),
-                       k_new=np.ascontiguousarray(encode(knf, kv_dtype)),
-                       v_new=np.ascontiguousarray(encode(vnf, kv_dtype)),
-                       seq_ids=seq_ids, positions=positions, block_table=table, scale=softmax_scale(d))
+                       k_new=np.ascontiguousarray(k_new_rows), v_new=np.ascontiguousarray(v_new_rows),
+                       seq_ids=seq_ids, positions=positions, block_table=table, scale=softmax_scale(d),
+                       k_scale=k_scale, v_scale=v_scale)
 
 
 # ---------------------------------------------------------------------------

@@ -130,7 +130,9 @@ def test_other_entry_points_validate(pkv):
     args = list(base); args[19] = 64
     assert pf(*args) == pkv.ERR_UNSUPPORTED          # d 64
     args = list(base); args[11] = 2
-    assert pf(*args) == pkv.ERR_UNSUPPORTED          # fp8 KV
+    assert pf(*args) == pkv.ERR_INVALID_ARG          # fp8 KV without scales
+    args = list(base); args[11] = 0
+    assert pf(*args) == pkv.ERR_UNSUPPORTED          # f32 KV
     args = list(base); args[22] = 3
     assert pf(*args) == pkv.ERR_INVALID_ARG          # causal flag
     args = list(base); args[7] = 0

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev, err_report, host_bits, note
+from gpu_util import TOL, dev, err_report, host_bits, note
 
 pytestmark = pytest.mark.gpu
 
@@ -121,3 +121,67 @@ def test_prefill_sequence_without_new_tokens(pkv):
     want = _oracle(p)
     assert got.shape[0] == 53
     assert np.max(np.abs(got - want)) <= 1e-2, err_report(got, want)
+
+
+# ---- FP8 KV (codes widened to bf16 in LDS, per-block K/V scales)
+
+def _run_fp8(pkv, p, causal=True, k_cache=None, v_cache=None, k_scale=None, v_scale=None):
+    q_lens = np.diff(p.cu_q_lens)
+    out = pkv.paged_attn_prefill_chunk(
+        dev(p.q, "bf16"), dev(p.cu_q_lens), dev(p.context_lens), int(q_lens.max()),
+        dev(p.k_cache) if k_cache is None else k_cache, dev(p.v_cache) if v_cache is None else v_cache,
+        dev(p.block_table), p.n_q, p.n_kv, p.d, 16, p.scale, causal=causal,
+        k_scale=dev(p.k_scale) if k_scale is None else k_scale,
+        v_scale=dev(p.v_scale) if v_scale is None else v_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (16, 2), (8, 1), (64, 8)])
+def test_prefill_fp8_ragged(pkv, causal, n_q, n_kv):
+    ctx = [0, 5, 16, 37, 300, 1000]
+    ql = [7, 1, 33, 128, 200, 65]
+    p = synth.make_prefill_case(config=402, layer=n_q + n_kv, n_q=n_q, n_kv=n_kv, d=128, context_lens=ctx, q_len=ql,
+                                kv_dtype="fp8")
+    note(f"prefill fp8 n_q={n_q} n_kv={n_kv} causal={causal}")
+    got = _run_fp8(pkv, p, causal)
+    want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, p.k_cache, p.v_cache, "fp8", p.k_scale,
+                                p.v_scale, p.block_table, p.n_q, p.n_kv, p.scale, causal=causal)
+    rep = err_report(got, want)
+    note("  " + rep)
+    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= TOL["fp8"], rep
+
+
+def test_fp8_append_then_prefill(pkv):
+    """A chunk of bf16 K/V rows is quantised into an FP8 cache that already
+    holds each sequence's context (kv_append_fp8), then attended; the oracle
+    runs the same two steps.  Caches must agree bit for bit, outputs within
+    the FP8 tolerance."""
+    ctx = [0, 9, 40, 250]
+    ql = [20, 64, 3, 130]
+    p = synth.make_prefill_case(config=403, layer=0, n_q=32, n_kv=8, d=128, context_lens=ctx, q_len=ql,
+                                kv_dtype="fp8", chunk_in_cache=False)
+    r = synth.rng(403, 0, 99)
+    total = int(p.cu_q_lens[-1])
+    kb = synth.encode(r.standard_normal((total, p.n_kv, p.d)).astype(np.float32) * 2, "bf16")
+    vb = synth.encode(r.standard_normal((total, p.n_kv, p.d)).astype(np.float32), "bf16")
+    kf = oracle.bf16_bits_to_f64(kb).astype(np.float32)
+    vf = oracle.bf16_bits_to_f64(vb).astype(np.float32)
+    tk, tv, tks, tvs = dev(p.k_cache), dev(p.v_cache), dev(p.k_scale), dev(p.v_scale)
+    table = dev(p.block_table)
+    pkv.kv_append_fp8(tk, tv, tks, tvs, table, dev(p.context_lens), dev(p.cu_q_lens), int(max(ql)), dev(kb, "bf16"),
+                      dev(vb, "bf16"))
+    k, v, ks, vs = oracle.kv_append_fp8(p.k_cache, p.v_cache, p.k_scale, p.v_scale, p.block_table, p.context_lens,
+                                        p.cu_q_lens, kf, vf, 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(tk.cpu().numpy(), k) and np.array_equal(tv.cpu().numpy(), v)
+    assert np.array_equal(tks.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(tvs.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    note("fp8 append then prefill")
+    got = _run_fp8(pkv, p, True, tk, tv, tks, tvs)
+    want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, k, v, "fp8", ks, vs, p.block_table, p.n_q,
+                                p.n_kv, p.scale, causal=True)
+    rep = err_report(got, want)
+    note("  " + rep)
+    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= TOL["fp8"], rep
