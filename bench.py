@@ -58,10 +58,10 @@ WORKLOADS = {
 # algorithmic bytes / flops
 # ---------------------------------------------------------------------------
 
-def decode_layer_bytes(seq_lens, n_q, n_kv, d, kv_bytes, q_bytes, out_bytes, fp8):
+def decode_layer_bytes(seq_lens, n_q, n_kv, d, kv_bytes, q_bytes, out_bytes, fp8, block_size=16):
     """Every cached K/V byte read once, plus q, output, scales, table and lengths."""
     L = np.asarray(seq_lens, dtype=np.int64)
-    blocks = (L + 15) // 16
+    blocks = (L + block_size - 1) // block_size
     b = int((L * n_kv * 2 * d * kv_bytes).sum())
     if fp8:
         b += int((blocks * n_kv * 2 * 4).sum())
@@ -99,7 +99,8 @@ def prefill_flops(ctx_lens, q_len, n_q, d):
 # ---------------------------------------------------------------------------
 
 class DecodeWorkload:
-    def __init__(self, cfg_id: int, layers: int = None, fp8_append: str = "copy"):
+    def __init__(self, cfg_id: int, layers: int = None, fp8_append: str = "copy", block_size: int = 16,
+                 csr: bool = False):
         import torch
         import paged_kv_cache_blocks_amd as pkv
         self.pkv, self.torch = pkv, torch
@@ -109,20 +110,31 @@ class DecodeWorkload:
         self.n_q, self.n_kv, self.d, self.kind = c["n_q"], c["n_kv"], c["d"], c["kv_dtype"]
         self.layers = layers or c["layers"]
         self.quantize_append = self.kind == "fp8" and fp8_append == "quantize"
+        self.bs, self.csr = block_size, csr
+        B = block_size
         self.seq_lens = synth.config_seq_lens(cfg_id)
         self.batch = len(self.seq_lens)
         dev = torch.device("cuda")
-        need = sum(synth.blocks_for(L) for L in self.seq_lens)
-        self.num_blocks = 64 if cfg_id == 1 else need
+        need = sum(synth.blocks_for(L, B) for L in self.seq_lens)
+        self.num_blocks = 64 if (cfg_id == 1 and B == 16) else need
         perm = synth.rng(cfg_id, 0, synth.T_PERM).permutation(self.num_blocks).astype(np.int32)
-        table, filled = synth.build_tables(self.seq_lens, self.num_blocks, perm)
+        table, filled = synth.build_tables(self.seq_lens, self.num_blocks, perm, B)
+        # slots allocated but not holding a token: the tail of each sequence's last block
+        self.waste = 1.0 - float(np.sum(self.seq_lens)) / float(need * B)
         self.block_table_np = table
         self.block_table = torch.from_numpy(table).to(dev)
         self.seq_lens_t = torch.from_numpy(self.seq_lens).to(dev)
         self.max_blocks = table.shape[1]
+        if csr:
+            # the same pages as a CSR table: request s owns kv_indices[kv_indptr[s]:kv_indptr[s+1]]
+            counts = np.array([synth.blocks_for(L, B) for L in self.seq_lens], np.int64)
+            indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+            indices = np.concatenate([table[s, :counts[s]] for s in range(self.batch)]).astype(np.int32)
+            self.kv_indptr = torch.from_numpy(indptr).to(dev)
+            self.kv_indices = torch.from_numpy(indices).to(dev)
         tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[self.kind]
         qdt = torch.float32 if self.kind == "f32" else torch.bfloat16
-        shape = (self.num_blocks, self.n_kv, 16, self.d)
+        shape = (self.num_blocks, self.n_kv, B, self.d)
         filled_t = torch.from_numpy(filled).to(dev)[:, None, :, None]
         self.k, self.v, self.ks, self.vs, self.q, self.k_new, self.v_new = [], [], [], [], [], [], []
         for layer in range(self.layers):
@@ -153,47 +165,53 @@ class DecodeWorkload:
             self.q.append(qf.to(qdt).contiguous())
             # the step's new token rows: the rows already at each sequence's last slot
             last = torch.from_numpy(self.seq_lens - 1).to(dev).long()
-            blk = self.block_table[torch.arange(self.batch, device=dev), last // 16].long()
+            blk = self.block_table[torch.arange(self.batch, device=dev), last // B].long()
             if self.quantize_append:
                 # the token's rows as the model would hand them over: bf16 values
                 # of the codes already there (code x block scale)
                 for j, lst in ((0, self.k_new), (1, self.v_new)):
-                    vals = kv[j][blk, :, last % 16, :].view(torch.float8_e4m3fn).float() * sc[j][blk][:, :, None]
+                    vals = kv[j][blk, :, last % B, :].view(torch.float8_e4m3fn).float() * sc[j][blk][:, :, None]
                     lst.append(vals.to(torch.bfloat16).contiguous())
             else:
-                self.k_new.append(kv[0][blk, :, last % 16, :].contiguous())
-                self.v_new.append(kv[1][blk, :, last % 16, :].contiguous())
+                self.k_new.append(kv[0][blk, :, last % B, :].contiguous())
+                self.v_new.append(kv[1][blk, :, last % B, :].contiguous())
         self.seq_ids = torch.arange(self.batch, dtype=torch.int32, device=dev)
         self.positions = (self.seq_lens_t - 1).to(torch.int32)
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
         self.cu_new = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
         self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
                     for _ in range(self.layers)]
-        ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
+        ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, B,
                                              pkv.dtype_code(self.k[0]))
         self.ws = torch.zeros(max(ws, 256), dtype=torch.uint8, device=dev)
-        self.plan = pkv.paged_attn_decode_plan(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, 16,
+        self.plan = pkv.paged_attn_decode_plan(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, B,
                                                pkv.dtype_code(self.k[0]))
         self.scale = synth.softmax_scale(self.d)
         torch.cuda.synchronize()
         kvb = synth.ELEM_BYTES[self.kind]
         qb = 4 if self.kind == "f32" else 2
         self.layer_bytes = decode_layer_bytes(self.seq_lens, self.n_q, self.n_kv, self.d, kvb, qb, 4,
-                                              self.kind == "fp8")
+                                              self.kind == "fp8", B)
         app = (append_fp8_bytes(self.batch, self.n_kv, self.d, 2) if self.quantize_append
                else append_bytes(self.batch, self.n_kv, self.d, kvb))
         self.step_bytes = slot_bytes(self.batch, self.max_blocks) + self.layers * (self.layer_bytes + app)
 
     def decode_call(self, layer):
+        if self.csr:
+            self.pkv.paged_attn_decode_csr(self.q[layer], self.k[layer], self.v[layer], self.kv_indptr,
+                                           self.kv_indices, self.max_blocks, self.seq_lens_t, self.n_q, self.n_kv,
+                                           self.d, self.bs, self.scale, k_scale=self.ks[layer],
+                                           v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws)
+            return
         self.pkv.paged_attn_decode(self.q[layer], self.k[layer], self.v[layer], self.block_table, self.seq_lens_t,
-                                   self.n_q, self.n_kv, self.d, 16, self.scale, k_scale=self.ks[layer],
+                                   self.n_q, self.n_kv, self.d, self.bs, self.scale, k_scale=self.ks[layer],
                                    v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws)
 
     calls_per_event = property(lambda self: self.layers)
 
     def step(self, events=None):
         pkv = self.pkv
-        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
+        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
         for layer in range(self.layers):
             if self.quantize_append:
                 pkv.kv_append_fp8(self.k[layer], self.v[layer], self.ks[layer], self.vs[layer], self.block_table,
@@ -221,8 +239,10 @@ class DecodeWorkload:
 
     def describe(self):
         return {"workload": self.name, "batch": self.batch, "n_q_heads": self.n_q, "n_kv_heads": self.n_kv,
-                "d_head": self.d, "block_size": 16, "layers": self.layers, "kv_dtype": self.kind,
+                "d_head": self.d, "block_size": self.bs, "layers": self.layers, "kv_dtype": self.kind,
                 **({"append": "quantize bf16 -> fp8"} if self.quantize_append else {}),
+                **({"page_table": "csr"} if self.csr else {}),
+                "tail_waste": round(self.waste, 5),
                 "mean_seq_len": float(np.mean(self.seq_lens)), "max_blocks_per_seq": int(self.max_blocks),
                 "num_blocks_per_layer": int(self.num_blocks)}
 
@@ -409,6 +429,9 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--fp8-append", choices=["copy", "quantize"], default="copy",
                     help="FP8 workload: copy ready-made codes, or quantise bf16 rows on append")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64, 128, 256],
+                    help="decode workloads: tokens per cache block (the same sequences, re-paged)")
+    ap.add_argument("--csr", action="store_true", help="decode workloads: pass the page table in CSR form")
     ap.add_argument("--prefill-kv", choices=["bf16", "fp8"], default="bf16",
                     help="prefill workload: KV cache element type (fp8: the chunk is quantised on append)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -437,7 +460,8 @@ def main():
     cfg = WORKLOADS[args.workload]
     prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
     t_build = time.perf_counter()
-    w = PrefillWorkload(cfg, args.prefill_kv) if prefill else DecodeWorkload(cfg, args.layers, args.fp8_append)
+    w = (PrefillWorkload(cfg, args.prefill_kv) if prefill
+         else DecodeWorkload(cfg, args.layers, args.fp8_append, args.block_size, args.csr))
     print(f"[bench] built {args.workload} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):

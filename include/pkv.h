@@ -124,8 +124,8 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
  * max_blocks_per_seq * B and table entries outside [0, num_blocks) are
  * skipped.  The blocks appended to must be named by one sequence only (a
  * shared block is copied first: pkv_pool_prepare_append); two sequences
- * writing one block race.  Supported: block_size 16; d_head 64 or 128;
- * pointers 16-byte aligned.  batch == 0 or max_new_len == 0 is a no-op. */
+ * writing one block race.  Supported: block_size 8, 16, 32, 64, 128 or 256;
+ * d_head 64 or 128; pointers 16-byte aligned.  batch == 0 or max_new_len == 0 is a no-op. */
 pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
                              const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                              const int32_t* cu_new_lens, int32_t batch, int32_t max_new_len, const void* k_new,
@@ -233,9 +233,11 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, 
  *   k_scale, v_scale: (device) fp32 [num_blocks][n_kv_heads] for FP8, else NULL.
  *   seq_lens: (device) int32 [batch], 0 <= seq_lens[s] <= max_blocks_per_seq * B;
  *   a sequence of length 0 yields zeros.
- * Supported: d_head in {64, 128}; block_size 16; (q, kv) in {(F32, F32),
- * (BF16, BF16), (BF16, FP8_E4M3FN)}; out F32 or BF16; n_q_heads a multiple of
- * n_kv_heads.  workspace: (device) at least
+ * Supported: d_head in {64, 128}; block_size 8, 16, 32, 64, 128 or 256
+ * ([KVP] Problem 4, "Trade-offs": small blocks waste less, large ones read
+ * more contiguously); num_blocks * n_kv_heads * block_size <= 2^32; (q, kv)
+ * in {(F32, F32), (BF16, BF16), (BF16, FP8_E4M3FN)}; out F32 or BF16;
+ * n_q_heads a multiple of n_kv_heads.  workspace: (device) at least
  * pkv_paged_attn_decode_workspace(...) bytes, 256-byte aligned.  It must be
  * zero-filled before its first use: the work-queue split keeps its item
  * counter there, and every call leaves the counter at zero again, so a
@@ -290,6 +292,33 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
                                       int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
                                       int32_t partition_tokens, int32_t* info);
 
+/* ---- CSR page tables ([MEM] "Method 3: PagedAttention", "Walking the
+ * table"): request s owns pages kv_indices[kv_indptr[s] .. kv_indptr[s+1]),
+ * its token p sits in page kv_indices[kv_indptr[s] + p / B] at offset p % B.
+ *   kv_indptr: (device) int32 [batch + 1], nondecreasing, kv_indptr[0] = 0;
+ *   kv_indices: (device) int32 [kv_indptr[batch]];
+ *   max_pages_per_seq: a bound on kv_indptr[s+1] - kv_indptr[s] (it sizes
+ *   the split like max_blocks_per_seq; pages past it are not read). */
+
+/* Decode over a CSR page table: as pkv_paged_attn_decode (library's split)
+ * with the table given as above; seq_lens[s] <= its page count * B (longer
+ * sequences are cut there).  Workspace as pkv_paged_attn_decode_workspace
+ * with max_blocks_per_seq = max_pages_per_seq. */
+pkv_status pkv_paged_attn_decode_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                     const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                     const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                                     const int32_t* kv_indices, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                     int32_t batch, int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t d_head, int32_t block_size, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Expands a CSR page table into the 2-D table the other calls take: row s of
+ * block_table_out (device, int32 [batch][max_blocks_per_seq]) gets request
+ * s's pages, then -1 (a request with more pages keeps its first
+ * max_blocks_per_seq).  batch == 0 is a no-op. */
+pkv_status pkv_csr_to_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t* block_table_out, void* stream);
+
 /* Chunked prefill attention: each sequence s brings q_len = cu_q_lens[s+1] -
  * cu_q_lens[s] new query tokens at absolute positions context_lens[s] + i.
  * With causal = 1, query i attends keys 0 .. context_lens[s] + i; with
@@ -307,7 +336,8 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
  *   cu_q_lens[num_seqs] = total_q, each q_len <= max_q_len;
  *   context_lens: (device) int32 [num_seqs];
  *   context_lens[s] + q_len <= max_blocks_per_seq * B.
- * Supported: d_head 128; block_size 16; q BF16; KV BF16 or FP8; out F32 or BF16.
+ * Supported: d_head 128; block_size 8, 16, 32, 64, 128 or 256; num_blocks *
+ * n_kv_heads * block_size <= 2^32; q BF16; KV BF16 or FP8; out F32 or BF16.
  * workspace: pkv_paged_attn_prefill_workspace(...) bytes (may be 0, then the
  * pointer may be NULL). */
 pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
@@ -320,6 +350,18 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
                                         int32_t causal, void* workspace, size_t workspace_bytes, void* stream);
 
 size_t pkv_paged_attn_prefill_workspace(int32_t num_seqs, int32_t max_q_len, int32_t n_q_heads, int32_t d_head);
+
+/* Chunked prefill over a CSR page table (see "CSR page tables" above): as
+ * pkv_paged_attn_prefill_chunk; context_lens[s] + q_len <= the request's page
+ * count * B.  Needs no workspace. */
+pkv_status pkv_paged_attn_prefill_chunk_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                            const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                            const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                                            const float* v_scale, const int32_t* kv_indptr,
+                                            const int32_t* kv_indices, int32_t max_pages_per_seq, int64_t num_blocks,
+                                            int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                            int32_t block_size, float scale, int32_t causal, void* stream);
 
 #ifdef __cplusplus
 }

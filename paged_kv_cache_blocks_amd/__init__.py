@@ -48,6 +48,12 @@ _SIGS = {
                                       ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp,
                                       _sz, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_workspace": ([_i32, _i32, _i32, _i32], _sz),
+    "pkv_paged_attn_decode_csr": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                   _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp], ctypes.c_int),
+    "pkv_paged_attn_prefill_chunk_csr": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
+                                          ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _vp], ctypes.c_int),
+    "pkv_csr_to_block_table": ([_vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_pool_create": ([_i64, _vp], ctypes.c_int),
     "pkv_pool_destroy": ([_vp], None),
     "pkv_pool_free_blocks": ([_vp], _i64),
@@ -315,6 +321,64 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
         _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb, n_q_heads,
         n_kv_heads, d_head, block_size, float(scale), int(partition_tokens), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_csr(q, k_cache, v_cache, kv_indptr, kv_indices, max_pages_per_seq, seq_lens, n_q_heads,
+                          n_kv_heads, d_head, block_size, scale, *, k_scale=None, v_scale=None, out=None,
+                          out_dtype=torch.float32, workspace=None, stream=None) -> torch.Tensor:
+    """Decode with a CSR page table: request s owns kv_indices[kv_indptr[s]:kv_indptr[s+1]]."""
+    batch = q.shape[0]
+    nb = k_cache.shape[0]
+    _need(kv_indptr, torch.int32, "kv_indptr")
+    _need(kv_indices, torch.int32, "kv_indices")
+    _need(seq_lens, torch.int32, "seq_lens")
+    if kv_indptr.numel() != batch + 1:
+        raise ValueError("kv_indptr must hold batch + 1 entries")
+    if out is None:
+        out = torch.empty((batch, n_q_heads, d_head), dtype=out_dtype, device=q.device)
+    ws_bytes = paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_pages_per_seq, block_size,
+                                           dtype_code(k_cache), 0)
+    if workspace is None and ws_bytes:
+        workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().pkv_paged_attn_decode_csr(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(kv_indptr), _ptr(kv_indices), int(max_pages_per_seq), _ptr(seq_lens),
+        batch, nb, n_q_heads, n_kv_heads, d_head, block_size, float(scale), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def csr_to_block_table(kv_indptr, kv_indices, max_blocks_per_seq: int, out=None, stream=None) -> torch.Tensor:
+    """2-D block table [batch, max_blocks_per_seq] (padded with -1) from a CSR page table."""
+    _need(kv_indptr, torch.int32, "kv_indptr")
+    _need(kv_indices, torch.int32, "kv_indices")
+    batch = kv_indptr.numel() - 1
+    if out is None:
+        out = torch.empty((batch, max_blocks_per_seq), dtype=torch.int32, device=kv_indptr.device)
+    _check(load().pkv_csr_to_block_table(_ptr(kv_indptr), _ptr(kv_indices), batch, int(max_blocks_per_seq), _ptr(out),
+                                         _stream(stream)))
+    return out
+
+
+def paged_attn_prefill_chunk_csr(q, cu_q_lens, context_lens, max_q_len, k_cache, v_cache, kv_indptr, kv_indices,
+                                 max_pages_per_seq, n_q_heads, n_kv_heads, d_head, block_size, scale, *,
+                                 causal: bool = True, out=None, out_dtype=torch.float32, k_scale=None, v_scale=None,
+                                 stream=None) -> torch.Tensor:
+    """Chunked prefill with a CSR page table."""
+    total_q = q.shape[0]
+    _need(cu_q_lens, torch.int32, "cu_q_lens")
+    _need(context_lens, torch.int32, "context_lens")
+    _need(kv_indptr, torch.int32, "kv_indptr")
+    _need(kv_indices, torch.int32, "kv_indices")
+    if out is None:
+        out = torch.empty((total_q, n_q_heads, d_head), dtype=out_dtype, device=q.device)
+    _check(load().pkv_paged_attn_prefill_chunk_csr(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(cu_q_lens), _ptr(context_lens),
+        context_lens.numel(), total_q, int(max_q_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(kv_indptr), _ptr(kv_indices), int(max_pages_per_seq), k_cache.shape[0],
+        n_q_heads, n_kv_heads, d_head, block_size, float(scale), 1 if causal else 0, _stream(stream)))
     return out
 
 

@@ -11,11 +11,12 @@
 // the query heads of a group are processed against the same K/V block).
 //
 // A workgroup (4 waves) serves GW query heads that share one KV head.  Its
-// waves take the blocks of a range round-robin in chunks of CB blocks; per
-// chunk a wave
-//   1. has the chunk's K and V slabs in registers (coalesced 16-byte loads,
-//      issued while the previous chunk computed; block ids come from the
-//      table once per range, one id per lane);
+// waves take the 16-token tiles of a range round-robin in chunks of CB tiles;
+// a tile is two 8-token halves, each inside one cache block whatever the
+// block size (8 .. 256) and table format; per chunk a wave
+//   1. has the chunk's K and V rows in registers (coalesced 16-byte loads,
+//      issued while the previous chunk computed; the table is walked once per
+//      range, one tile per lane);
 //   2. stages K into LDS as bf16 rows (fp8 converted here, once per element)
 //      and V as bf16 token *pairs* interleaved per column, so the value
 //      product runs on v_dot2c_f32_bf16;
@@ -23,7 +24,7 @@
 //      and reads half of the K row from LDS; a DPP add joins the halves.
 //      Every K element is fetched from HBM once and serves all GW heads;
 //   4. online softmax over the chunk with DPP lane-group reductions; the
-//      weights go to LDS as bf16 pairs;
+//      weights go to LDS as bf16 pairs (fp8: times their half's V scale);
 //   5. values: lane c owns output columns (2c, 2c+1) for all GW heads and
 //      accumulates dot2(weight pair, value pair) in f32.
 // f32 caches take the same path with f32 rows and fma in place of dot2.
@@ -39,7 +40,7 @@
 
 namespace pkv {
 
-constexpr int kBlock = 16;  // tokens per cache block
+constexpr int kBlock = 16;  // tokens per tile (two 8-token halves; a cache block holds 8 .. 256 tokens)
 constexpr int kWaves = 4;   // waves per workgroup
 constexpr int kSegBlocks = kWaves * kWave;  // blocks one id load covers (one id per lane per wave)
 
@@ -50,11 +51,10 @@ template <int KIND, int D>
 struct Geo {
   static constexpr int esize = KindBytes<KIND>::v;
   static constexpr int row_bytes = D * esize;           // one token row of one KV head in HBM
-  static constexpr int slab_bytes = kBlock * row_bytes;  // one (block, KV head) slab
   static constexpr int LW = row_bytes >= 128 ? 16 : 8;   // bytes per lane per load
   static constexpr int LPR = row_bytes / LW;             // lanes per row
   static constexpr int RPI = kWave / LPR;                // rows per load instruction
-  static constexpr int NLK = kBlock / RPI;               // load instructions per slab
+  static constexpr int NLK = kBlock / RPI;               // load instructions per tile
   static constexpr int EPL = LW / esize;                 // elements per lane per load
   static_assert(LPR <= kWave && NLK >= 2 && NLK % 2 == 0, "slab geometry");
 };
@@ -127,27 +127,35 @@ __device__ __forceinline__ void reset_state(WaveState<KIND, D, GW>& ws) {
     for (int k = 0; k < Lay<KIND, D, GW>::COLS; ++k) ws.o[h][k] = 0.f;
 }
 
-// This wave's block ids for blocks [blk_begin, blk_begin + nblk) (nblk <=
-// kSegBlocks) of sequence s, one per lane: lane i <-> block (i % CB) of the
-// wave's chunk i / CB (= range chunk w + 4 * (i / CB)); ids outside the pool
-// are clamped into it.  fp8: the block's K and V scales ride along.
+// Where this wave's 16-token tiles [blk_begin, blk_begin + nblk) (nblk <=
+// kSegBlocks) of sequence s live, one tile per lane: lane i <-> tile (i % CB)
+// of the wave's chunk i / CB (= range chunk w + 4 * (i / CB)), as the cache
+// row index (KV head kvh) of the first row of each 8-token half; block ids
+// outside the pool or the table row are clamped into the pool, and tiles past
+// the range keep row 0 (loaded all the same, then masked).  fp8: the K and V
+// scales of each half's block ride along.
 struct BlockIds {
-  int id;
-  float ks, vs;
+  uint32_t row[2];
+  float ks[2], vs[2];
 };
 
 template <int KIND, int D, int GW>
 __device__ __forceinline__ BlockIds load_ids(const DecodeArgs& a, int s, int kvh, int blk_begin, int nblk, int w,
                                              int lane) {
   constexpr int CB = Lay<KIND, D, GW>::CB;
-  BlockIds r{0, 1.f, 1.f};
+  BlockIds r{{0u, 0u}, {1.f, 1.f}, {1.f, 1.f}};
   const int pb_lane = (w + kWaves * (lane / CB)) * CB + lane % CB;
   if (pb_lane < nblk) {
-    const int id = a.block_table[(int64_t)s * a.max_blocks + blk_begin + pb_lane];
-    r.id = min(max(id, 0), (int)(a.num_blocks - 1));
-    if constexpr (KIND == KIND_FP8) {
-      r.ks = a.k_scale[(int64_t)r.id * a.n_kv + kvh];
-      r.vs = a.v_scale[(int64_t)r.id * a.n_kv + kvh];
+    const PageRow pr = page_row(a, s);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tok = (blk_begin + pb_lane) * kBlock + 8 * h;
+      const int id = page_block(a, pr, tok);
+      r.row[h] = page_row_index(a, id, kvh, tok);
+      if constexpr (KIND == KIND_FP8) {
+        r.ks[h] = a.k_scale[(int64_t)id * a.n_kv + kvh];
+        r.vs[h] = a.v_scale[(int64_t)id * a.n_kv + kvh];
+      }
     }
   }
   return r;
@@ -168,22 +176,25 @@ struct SlabRegs {
   typename Ly::LV bk[Ly::CB][Ly::Gm::NLK], bv[Ly::CB][Ly::Gm::NLK];
 };
 
-// Issue the 16-byte loads of the wave's chunk c (ids from load_ids).
+// Issue the 16-byte loads of the wave's chunk c (rows from load_ids): load
+// instruction i covers rows RPI i .. RPI i + RPI - 1 of a tile, so the first
+// NLK / 2 fall in the first half and the rest in the second.
 template <int KIND, int D, int GW>
-__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, int kvh, int my_id, int c, int lane,
+__device__ __forceinline__ void issue_chunk(const DecodeArgs& a, const BlockIds& ids, int c, int lane,
                                             SlabRegs<KIND, D, GW>& r) {
   using Ly = Lay<KIND, D, GW>;
   using Gm = typename Ly::Gm;
   using LV = typename Ly::LV;
+  constexpr int LH = Gm::NLK / 2;
   const char* const kc = reinterpret_cast<const char*>(a.k_cache);
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
 #pragma unroll
   for (int b = 0; b < Ly::CB; ++b) {
-    const int id = __builtin_amdgcn_readlane(my_id, c * Ly::CB + b);
-    const int64_t slab = ((int64_t)id * a.n_kv + kvh) * Gm::slab_bytes;
+    const int64_t half0 = (int64_t)__builtin_amdgcn_readlane(ids.row[0], c * Ly::CB + b) * Gm::row_bytes;
+    const int64_t half1 = (int64_t)__builtin_amdgcn_readlane(ids.row[1], c * Ly::CB + b) * Gm::row_bytes;
 #pragma unroll
     for (int i = 0; i < Gm::NLK; ++i) {
-      const int64_t off = slab + (int64_t)(i * kWave + lane) * Gm::LW;
+      const int64_t off = (i < LH ? half0 : half1) + (int64_t)((i % LH) * kWave + lane) * Gm::LW;
       r.bk[b][i] = *reinterpret_cast<const LV*>(kc + off);
       r.bv[b][i] = *reinterpret_cast<const LV*>(vc + off);
     }
@@ -217,8 +228,6 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
   // there belong to another range even when the sequence goes on
   L = min(L, (blk_begin + nblk) * kBlock);
   const int sh = lane / TG, st = (lane % TG) / QS, qh = lane % QS;
-  const int my_id = ids.id;
-  const float my_ks = ids.ks, my_vs = ids.vs;
   const int tok0 = blk_begin * kBlock;  // sequence position of the range's first token
 
   char* const k_lds = wbase;
@@ -232,15 +241,19 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
     set_priority_for_progress(c, n_my);
     const int ct0 = (w + kWaves * c) * CT;      // first token of the chunk (range-relative)
     const int nvalid = L - (tok0 + ct0);        // tokens of the chunk that exist (may exceed CT)
-    float kscale[CB], vscale[CB];
+    float kscale[2 * CB], vscale[2 * CB];  // per 8-token half of the chunk
 #pragma unroll
-    for (int b = 0; b < CB; ++b) {
-      kscale[b] = vscale[b] = 1.f;
-      if constexpr (KIND == KIND_FP8) {
-        kscale[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks), c * CB + b));
-        vscale[b] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs), c * CB + b));
+    for (int b = 0; b < CB; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        kscale[2 * b + h] = vscale[2 * b + h] = 1.f;
+        if constexpr (KIND == KIND_FP8) {
+          kscale[2 * b + h] =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.ks[h]), c * CB + b));
+          vscale[2 * b + h] =
+              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.vs[h]), c * CB + b));
+        }
       }
-    }
 
     wave_lds_sync();
     // ---- stage K rows (bf16 or f32) and V (bf16 pairs or f32 rows) into LDS ----
@@ -318,7 +331,7 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
     }
     if (c == 0) first_staged();
     // the registers are free again: fetch the next chunk while this one computes
-    if (c + 1 < n_my) issue_chunk<KIND, D, GW>(a, kvh, my_id, c + 1, lane, slabs);
+    if (c + 1 < n_my) issue_chunk<KIND, D, GW>(a, ids, c + 1, lane, slabs);
     else after_stage();
     wave_lds_sync();
 
@@ -358,10 +371,8 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
       float dot = (acc0 + acc1) + (acc2 + acc3);
       dot += dpp_f<DPP_QUAD_XOR1>(dot);  // the other d-half of this (token, head)
       float ksc = kscale[0];
-      if constexpr (CB > 1) {
 #pragma unroll
-        for (int b = 1; b < CB; ++b) ksc = (tau / kBlock == b) ? kscale[b] : ksc;
-      }
+      for (int hb = 1; hb < 2 * CB; ++hb) ksc = (tau / 8 == hb) ? kscale[hb] : ksc;
       const float sv = dot * (a.scale_log2 * ksc);
       sc[r] = (tau < nvalid) ? sv : -INFINITY;
       cmax_ = fmaxf(cmax_, sc[r]);
@@ -384,7 +395,15 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
         const int b = tau / kBlock, t = tau % kBlock;
         const int i = t / Gm::RPI, g = t % Gm::RPI;
         const int pq = g + Gm::RPI * (i / 2);
-        if (qh == 0) reinterpret_cast<__bf16*>(p_lds)[((b * NPAIR + pq) * GW + sh) * 2 + (i & 1)] = (__bf16)p;
+        // fp8: the weight enters the value product times its half's V scale
+        float pv = p;
+        if constexpr (KIND == KIND_FP8) {
+          float vsc = vscale[0];
+#pragma unroll
+          for (int hb = 1; hb < 2 * CB; ++hb) vsc = (tau / 8 == hb) ? vscale[hb] : vsc;
+          pv = p * vsc;
+        }
+        if (qh == 0) reinterpret_cast<__bf16*>(p_lds)[((b * NPAIR + pq) * GW + sh) * 2 + (i & 1)] = (__bf16)pv;
       }
       lsum += (qh == 0) ? p : 0.f;
     }
@@ -425,13 +444,11 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
       const int dcol = (lane % PVL) * 2;
 #pragma unroll
       for (int b = 0; b < CB; ++b) {
-        // bf16 accumulates into o directly; fp8 gathers the block's product
-        // first and multiplies it by the block's V scale once
         float t[GW][2];
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
-          t[h][0] = (KIND == KIND_FP8) ? 0.f : ws.o[h][0];
-          t[h][1] = (KIND == KIND_FP8) ? 0.f : ws.o[h][1];
+          t[h][0] = ws.o[h][0];
+          t[h][1] = ws.o[h][1];
         }
 #pragma unroll
         for (int qq = 0; qq < NPAIR / PVG; ++qq) {
@@ -449,13 +466,8 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
         }
 #pragma unroll
         for (int h = 0; h < GW; ++h) {
-          if constexpr (KIND == KIND_FP8) {
-            ws.o[h][0] = fmaf(vscale[b], t[h][0], ws.o[h][0]);
-            ws.o[h][1] = fmaf(vscale[b], t[h][1], ws.o[h][1]);
-          } else {
-            ws.o[h][0] = t[h][0];
-            ws.o[h][1] = t[h][1];
-          }
+          ws.o[h][0] = t[h][0];
+          ws.o[h][1] = t[h][1];
         }
       }
     }
@@ -517,8 +529,9 @@ __device__ __forceinline__ void store_out(const DecodeArgs& a, int64_t idx, floa
   else reinterpret_cast<float*>(a.out)[idx] = v;
 }
 
+// tokens of sequence s: its length, capped by what its table row can hold
 __device__ __forceinline__ int clamp_len(const DecodeArgs& a, int s) {
-  return min(max(a.seq_lens[s], 0), a.max_blocks * kBlock);
+  return min(max(a.seq_lens[s], 0), page_row(a, s).n << a.log2_bs);
 }
 
 // ---------------------------------------------------------------------------
@@ -543,7 +556,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   // the length, the q rows and the partition's block ids are fetched together
   // (ids for every table entry the partition could use, whatever the length),
   // so the first K/V loads wait on two dependent fetches, not three
-  const int nb_cap = min(a.part_tokens / kBlock, a.max_blocks - p0 / kBlock);
+  const int nb_cap = a.part_tokens / kBlock;
   const BlockIds ids = load_ids<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_cap, w, lane);
   WaveState<KIND, D, GW> ws;
   load_q(a, s, h0, lane, ws);
@@ -553,7 +566,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int nb_part = (plen + kBlock - 1) / kBlock;
   reset_state(ws);
   SlabRegs<KIND, D, GW> slabs;
-  if (wave_chunks<KIND, D, GW>(nb_part, w) > 0) issue_chunk<KIND, D, GW>(a, kvh, ids.id, 0, lane, slabs);
+  if (wave_chunks<KIND, D, GW>(nb_part, w) > 0) issue_chunk<KIND, D, GW>(a, ids, 0, lane, slabs);
   run_blocks<KIND, D, GW>(a, s, kvh, p0 / kBlock, nb_part, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids,
                           [] {}, [] {}, [] {});
   merge_waves<KIND, D, GW>(smem, w, lane, ws, [&](int h, int col, float M, float l, float o) {
@@ -773,7 +786,7 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
   BlockIds ids_c = load_ids<KIND, D, GW>(a, ic.s, ic.kvc / a.head_chunks, ic.j0, ic.nblk, w, lane);
   load_q(a, ic.s, head0(ic), lane, ws);
   if (wave_chunks<KIND, D, GW>(ic.nblk, w) > 0)
-    issue_chunk<KIND, D, GW>(a, ic.kvc / a.head_chunks, ids_c.id, 0, lane, slabs);
+    issue_chunk<KIND, D, GW>(a, ids_c, 0, lane, slabs);
 
   for (int k = 0;; ++k) {
     // The next item: the static second one after the first, then an item
@@ -785,7 +798,7 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
     if (threadIdx.x == 0 && k >= 1 && n_dyn > 0) claimed = atomicAdd(a.dyn_counter, 1u);
     int nxt = n_items;
     Item in_{0, 0, 0, 0};
-    BlockIds ids_n{0, 1.f, 1.f};
+    BlockIds ids_n{{0u, 0u}, {1.f, 1.f}, {1.f, 1.f}};
     int nmy_next = 0;
     auto publish_next = [&] {
       if (threadIdx.x == 0)
@@ -807,12 +820,12 @@ __global__ __launch_bounds__(256) void decode_queue_kernel(DecodeArgs a) {
     if (wave_chunks<KIND, D, GW>(ic.nblk, w) == 0) {
       // nothing of this item for this wave: go straight to the next one
       publish_next();
-      if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, in_.kvc / a.head_chunks, ids_n.id, 0, lane, slabs);
+      if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, ids_n, 0, lane, slabs);
     } else {
       run_blocks<KIND, D, GW>(
           a, ic.s, kvh, ic.j0, ic.nblk, L, w, lane, smem + w * Ly::WAVE_BYTES, ws, slabs, ids_c, publish_next,
           [&] {
-            if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, in_.kvc / a.head_chunks, ids_n.id, 0, lane, slabs);
+            if (nmy_next > 0) issue_chunk<KIND, D, GW>(a, ids_n, 0, lane, slabs);
           },
           [] {});
     }

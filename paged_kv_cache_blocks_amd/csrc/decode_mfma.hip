@@ -14,17 +14,19 @@
 //
 // Work decomposition (as the VALU kernel's partition mode): one workgroup per
 // (sequence, KV head chunk, partition); its four waves take 32-token chunks
-// (two cache blocks) round robin and keep their own running state, merged at
-// the end through LDS.  Per chunk a wave:
-//   loads the two K and V slabs with coalesced 16-byte loads (issued one
-//   chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
+// (two 16-token tiles) round robin and keep their own running state, merged
+// at the end through LDS.  Each tile is two 8-token halves, each inside one
+// cache block whatever the block size (8 .. 256) and table format.  Per chunk
+// a wave:
+//   loads the K and V rows of its two tiles with coalesced 16-byte loads
+//   (issued one chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
 //   its own LDS region in the swizzled row layout (V rows past the end of the
 //   sequence are written as zeros: their zero weights must not meet a NaN);
 //   S^T = K q^T: 2 token tiles x 4 d steps, K fragments from LDS, q^T in
-//   registers; the fp8 K scale of each block multiplies its scores;
+//   registers; the fp8 K scale of each half's block multiplies its scores;
 //   online softmax per head column (in-lane max over the lane's 8 tokens,
 //   then across the four lane rows); weights rounded to bf16, the running sum
-//   adds the same rounded weights, and with fp8 each block's V scale
+//   adds the same rounded weights, and with fp8 each half's V scale
 //   multiplies its weights before the value product;
 //   O^T += V^T P^T: 8 d tiles, V^T fragments read with ds_read_b64_tr_b16.
 #include "pkv_device.h"
@@ -35,8 +37,8 @@ namespace pkv {
 namespace {
 
 constexpr int D = 128;
-constexpr int kB = 16;                 // tokens per cache block
-constexpr int kCT = 32;                // tokens per wave chunk (two blocks)
+constexpr int kB = 16;                 // tokens per tile
+constexpr int kCT = 32;                // tokens per wave chunk (two tiles)
 constexpr int kW = 4;                  // waves per workgroup
 constexpr int kTileB = kCT * 256;      // one K or V chunk in LDS (bf16 rows of 256 bytes)
 constexpr int kWaveB = 2 * kTileB;     // K then V
@@ -45,21 +47,21 @@ constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 constexpr float kSlack = 8.f;          // log2 units: the running max moves only past this
 
 template <int KIND> struct Slab;
-// bf16: a (block, KV head) slab is 16 rows x 256 bytes; load i, lane l brings
-// row 4 i + l / 16, piece l % 16
+// bf16: a tile is 16 rows x 256 bytes; load i, lane l brings row 4 i + l / 16,
+// piece l % 16 (loads 0, 1: the first half, 2, 3: the second)
 template <> struct Slab<KIND_BF16> {
-  static constexpr int bytes = kB * 256;
+  static constexpr int row_bytes = 256;
   static constexpr int loads = 4;
 };
 // fp8: 16 rows x 128 bytes; load i, lane l brings row 8 i + l / 8, fp8 piece
-// l % 8 (16 codes = bf16 pieces 2 (l % 8) and 2 (l % 8) + 1)
+// l % 8 (16 codes = bf16 pieces 2 (l % 8) and 2 (l % 8) + 1); load i is half i
 template <> struct Slab<KIND_FP8> {
-  static constexpr int bytes = kB * 128;
+  static constexpr int row_bytes = 128;
   static constexpr int loads = 2;
 };
 
-__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int s) {
-  return min(max(a.seq_lens[s], 0), a.max_blocks * kB);
+__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, const PageRow& pr, int s) {
+  return min(max(a.seq_lens[s], 0), pr.n << a.log2_bs);
 }
 
 __device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float v) {
@@ -84,25 +86,34 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int p0 = part * a.part_tokens;
-  const int L = seq_len_of(a, s);
+  const PageRow pr = page_row(a, s);
+  const int L = seq_len_of(a, pr, s);
   if (a.n_parts > 1 && p0 >= L) return;
   const int plen = max(0, min(a.part_tokens, L - p0));  // tokens of this partition
   const int nblk = (plen + kB - 1) / kB;
   const int n_chunks = (nblk + 1) / 2;
   const int n_my = n_chunks > w ? (n_chunks - w + kW - 1) / kW : 0;
 
-  // Block ids of this wave's chunks: lane i holds block (i & 1) of the wave's
-  // chunk i >> 1 (partition chunk w + 4 (i >> 1)); fp8 scales ride along.
-  int my_id = -1;
-  float my_ks = 1.f, my_vs = 1.f;
+  // Where this wave's tiles live: lane i holds tile (i & 1) of the wave's
+  // chunk i >> 1 (partition chunk w + 4 (i >> 1)) as the cache row index of
+  // each half's first row; fp8 scales of each half's block ride along.  A
+  // tile past the partition keeps row 0: it is loaded all the same, so the
+  // loads need no branch, and its rows, being past the end, are masked (K)
+  // or staged as zeros (V).
+  uint32_t my_row[2] = {0u, 0u};
+  float my_ks[2] = {1.f, 1.f}, my_vs[2] = {1.f, 1.f};
   {
     const int pb = (w + kW * (lane >> 1)) * 2 + (lane & 1);
     if (pb < nblk) {
-      const int id = a.block_table[(int64_t)s * a.max_blocks + p0 / kB + pb];
-      my_id = min(max(id, 0), (int)(a.num_blocks - 1));
-      if constexpr (KIND == KIND_FP8) {
-        my_ks = a.k_scale[(int64_t)my_id * a.n_kv + kvh];
-        my_vs = a.v_scale[(int64_t)my_id * a.n_kv + kvh];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int tok = p0 + kB * pb + 8 * h;
+        const int id = page_block(a, pr, tok);
+        my_row[h] = page_row_index(a, id, kvh, tok);
+        if constexpr (KIND == KIND_FP8) {
+          my_ks[h] = a.k_scale[(int64_t)id * a.n_kv + kvh];
+          my_vs[h] = a.v_scale[(int64_t)id * a.n_kv + kvh];
+        }
       }
     }
   }
@@ -129,19 +140,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const char* const kc = reinterpret_cast<const char*>(a.k_cache);
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
 
-  // A chunk's second block may lie past the partition (id -1): it is loaded
-  // from block 0 all the same, so the loads need no branch, and its rows,
-  // being past the end, are masked (K) or staged as zeros (V).
   u32x4 bk[2][SL::loads], bv[2][SL::loads];
   auto issue = [&](int c) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int id = max(__builtin_amdgcn_readlane(my_id, 2 * c + b), 0);
-      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * SL::bytes;
+      const int64_t half0 = (int64_t)__builtin_amdgcn_readlane(my_row[0], 2 * c + b) * SL::row_bytes;
+      const int64_t half1 = (int64_t)__builtin_amdgcn_readlane(my_row[1], 2 * c + b) * SL::row_bytes;
 #pragma unroll
       for (int i = 0; i < SL::loads; ++i) {
-        bk[b][i] = ld16(kc + slab + (i * kWave + lane) * 16);
-        bv[b][i] = ld16(vc + slab + (i * kWave + lane) * 16);
+        constexpr int LH = SL::loads / 2;  // loads per half
+        const int64_t off = (i < LH ? half0 : half1) + ((i % LH) * kWave + lane) * 16;
+        bk[b][i] = ld16(kc + off);
+        bv[b][i] = ld16(vc + off);
       }
     }
   };
@@ -198,10 +208,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float kscale = KIND == KIND_FP8
-                               ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                               __builtin_bit_cast(int, my_ks), 2 * c + t))
-                               : 1.f;
+      // this lane's tokens 4 g .. 4 g + 3 of tile t lie in half g / 2
+      float kscale = 1.f;
+      if constexpr (KIND == KIND_FP8) {
+        const float k0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[0]), 2 * c + t));
+        const float k1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[1]), 2 * c + t));
+        kscale = g < 2 ? k0 : k1;
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tok = t0 + 16 * t + 4 * g + j;
@@ -224,8 +237,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       const uint32_t r0 = pack_bf16(p[0], p[1]), r1 = pack_bf16(p[2], p[3]);
       ls = dot2_bf16(r1, kOnes, dot2_bf16(r0, kOnes, ls));  // the sum adds the rounded weights
       if constexpr (KIND == KIND_FP8) {
-        const float vscale = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                                           __builtin_bit_cast(int, my_vs), 2 * c + t));
+        const float v0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs[0]), 2 * c + t));
+        const float v1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_vs[1]), 2 * c + t));
+        const float vscale = g < 2 ? v0 : v1;
         pw[t][0] = pack_bf16(p[0] * vscale, p[1] * vscale);
         pw[t][1] = pack_bf16(p[2] * vscale, p[3] * vscale);
       } else {

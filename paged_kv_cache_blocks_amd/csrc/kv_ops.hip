@@ -196,15 +196,17 @@ __global__ __launch_bounds__(1024) void kv_append_fp8_kernel(uint8_t* __restrict
                                                             int32_t max_blocks, const int32_t* __restrict__ ctx_lens,
                                                             const int32_t* __restrict__ cu_new,
                                                             const TIn* __restrict__ k_new,
-                                                            const TIn* __restrict__ v_new, int32_t n_kv) {
-  constexpr int B = 16, VPL = D / kWave;
+                                                            const TIn* __restrict__ v_new, int32_t n_kv,
+                                                            int32_t log2_bs) {
+  constexpr int VPL = D / kWave;
+  const int B = 1 << log2_bs;
   const int lane = threadIdx.x & (kWave - 1);
   const int pair = (int)blockIdx.z * (int)(blockDim.x / kWave) + (int)(threadIdx.x / kWave);
   if (pair >= 2 * n_kv) return;
   const int h = pair >> 1, is_v = pair & 1, s = blockIdx.y;
   const int ctx = ctx_lens[s], t0 = cu_new[s], n = cu_new[s + 1] - t0;
   if (ctx < 0 || n <= 0) return;
-  const int j = ctx / B + (int)blockIdx.x;  // logical block
+  const int j = (ctx >> log2_bs) + (int)blockIdx.x;  // logical block
   if (j * B >= ctx + n || j >= max_blocks) return;
   const int32_t raw = table[(int64_t)s * max_blocks + j];
   if (raw < 0 || raw >= num_blocks) return;
@@ -262,6 +264,19 @@ __global__ __launch_bounds__(1024) void kv_append_fp8_kernel(uint8_t* __restrict
   if (lane == 0) *sc = nw;
 }
 
+// CSR page table -> 2-D table: row s holds kv_indices[kv_indptr[s] ..
+// kv_indptr[s+1]) followed by -1 up to max_blocks entries (a row with more
+// pages keeps its first max_blocks).  Grid: x over entries, y = sequence.
+__global__ __launch_bounds__(256) void csr_to_table_kernel(const int32_t* __restrict__ indptr,
+                                                           const int32_t* __restrict__ indices, int32_t max_blocks,
+                                                           int32_t* __restrict__ table) {
+  const int s = blockIdx.y;
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= max_blocks) return;
+  const int b = indptr[s], n = indptr[s + 1] - b;
+  table[(int64_t)s * max_blocks + j] = j < n ? indices[b + j] : -1;
+}
+
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
                                const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,
                                hipStream_t stream) {
@@ -316,10 +331,12 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
 hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
                                  const int32_t* table, int32_t max_blocks, const int32_t* ctx_lens,
                                  const int32_t* cu_new, int32_t batch, int32_t max_new, const void* k_new,
-                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, hipStream_t stream) {
+                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, int32_t log2_bs,
+                                 hipStream_t stream) {
   if (batch == 0 || max_new == 0) return hipSuccess;
-  // n consecutive rows starting anywhere in a block touch at most (n + 14) / 16 + 1 blocks
-  const int gx = (max_new + 14) / 16 + 1;
+  // n consecutive rows starting anywhere in a block of B touch at most (n + B - 2) / B + 1 blocks
+  const int B = 1 << log2_bs;
+  const int gx = (max_new + B - 2) / B + 1;
   const int pairs = 2 * n_kv, waves = pairs < 16 ? pairs : 16;
   const dim3 grid((unsigned)gx, (unsigned)batch, (unsigned)((pairs + waves - 1) / waves));
   const dim3 block((unsigned)(waves * kWave));
@@ -328,12 +345,20 @@ hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, fl
 #define PKV_APPEND_FP8(DD, T)                                                                                   \
   hipLaunchKernelGGL((kv_append_fp8_kernel<DD, T>), grid, block, 0, stream, kc, vc, k_scale, v_scale,          \
                      num_blocks, table, max_blocks, ctx_lens, cu_new, static_cast<const T*>(k_new),             \
-                     static_cast<const T*>(v_new), n_kv)
+                     static_cast<const T*>(v_new), n_kv, log2_bs)
   if (d == 128 && new_bytes == 2) PKV_APPEND_FP8(128, uint16_t);
   else if (d == 128) PKV_APPEND_FP8(128, float);
   else if (new_bytes == 2) PKV_APPEND_FP8(64, uint16_t);
   else PKV_APPEND_FP8(64, float);
 #undef PKV_APPEND_FP8
+  return hipGetLastError();
+}
+
+hipError_t launch_csr_to_table(const int32_t* indptr, const int32_t* indices, int32_t batch, int32_t max_blocks,
+                               int32_t* table, hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  const dim3 grid((unsigned)((max_blocks + 255) / 256), (unsigned)batch);
+  hipLaunchKernelGGL(csr_to_table_kernel, grid, dim3(256), 0, stream, indptr, indices, max_blocks, table);
   return hipGetLastError();
 }
 

@@ -49,8 +49,21 @@ int elem_bytes(pkv_dtype t) {
 
 bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3FN; }
 
-constexpr int kBlockSize = 16;
 constexpr int kMaxPartition = 4096;
+
+// log2 of a supported block size (8, 16, 32, 64, 128, 256), else -1
+int log2_block_size(int32_t bs) {
+  for (int l = 3; l <= 8; ++l)
+    if (bs == (1 << l)) return l;
+  return -1;
+}
+
+// the attention kernels address cache rows of one KV head with 32-bit indices
+pkv_status check_row_space(int64_t num_blocks, int32_t n_kv, int32_t block_size) {
+  if ((double)num_blocks * n_kv * block_size > 4294967296.0)
+    return fail(PKV_ERR_UNSUPPORTED, "num_blocks x n_kv_heads x block_size beyond 2^32 rows");
+  return PKV_OK;
+}
 constexpr int kQueueMaxWgsPerCu = 2;
 constexpr int kQueueSplit = -1;  // partition_tokens value that asks for the work-queue split
 
@@ -118,7 +131,8 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
   if (st != PKV_OK) return st;
   if (!valid_dtype(kv_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
   if (batch < 1 || max_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be positive");
-  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  if (log2_block_size(block_size) < 0)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (8, 16, 32, 64, 128 or 256)", block_size);
   if (d != 64 && d != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d unsupported (64 or 128)", d);
   const int group = n_q / n_kv;
   const int gw = pkv::decode_heads_per_wg(group);
@@ -172,7 +186,7 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
     const int occ = std::min(queue_wgs_per_cu(kv_dtype, d, gw, batch), kQueueMaxWgsPerCu);
     const int64_t resident = (int64_t)cus * occ;
     const int64_t pairs = (int64_t)batch * hk;
-    const int64_t max_blocks_total = pairs * max_blocks;
+    const int64_t max_blocks_total = pairs * ((max_tokens + 15) / 16);  // 16-token tiles
     int64_t n_wg = std::min(resident, (max_blocks_total + 7) / 8);
     if (n_wg < 1) n_wg = 1;
     plan->n_wg = (int32_t)n_wg;
@@ -289,7 +303,8 @@ pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float
     return fail(PKV_ERR_INVALID_ARG, "null pointer");
   if (num_blocks < 1 || max_blocks_per_seq < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
     return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
-  if (block_size != 16) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 16)", block_size);
+  const int log2_bs = log2_block_size(block_size);
+  if (log2_bs < 0) return fail(PKV_ERR_UNSUPPORTED, "block_size %d (supported: 8, 16, 32, 64, 128, 256)", block_size);
   if (d_head != 64 && d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d (supported: 64, 128)", d_head);
   if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "table too wide");
   if (batch > 65535 || 2 * n_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
@@ -298,8 +313,20 @@ pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float
   return hip_status(pkv::launch_kv_append_fp8(k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                                               max_blocks_per_seq, context_lens, cu_new_lens, batch, max_new_len,
                                               k_new, v_new, new_dtype == PKV_BF16 ? 2 : 4, n_kv_heads, d_head,
-                                              (hipStream_t)stream),
+                                              log2_bs, (hipStream_t)stream),
                     "kv_append_fp8 launch");
+}
+
+pkv_status pkv_csr_to_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int32_t batch,
+                                  int32_t max_blocks_per_seq, int32_t* block_table_out, void* stream) {
+  if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (!kv_indptr || !kv_indices || !block_table_out) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  if (batch > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  return hip_status(pkv::launch_csr_to_table(kv_indptr, kv_indices, batch, max_blocks_per_seq, block_table_out,
+                                             (hipStream_t)stream),
+                    "csr_to_table launch");
 }
 
 pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
@@ -362,14 +389,17 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
   return ok();
 }
 
-pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
-                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
-                                             const float* k_scale, const float* v_scale,
-                                             const int32_t* block_table, int32_t max_blocks_per_seq,
-                                             const int32_t* seq_lens, int32_t batch, int64_t num_blocks,
-                                             int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
-                                             int32_t block_size, float scale, int32_t partition_tokens,
-                                             void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// decode over a 2-D table (indptr == nullptr) or CSR rows
+pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const void* k_cache,
+                       const void* v_cache, pkv_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                       const int32_t* block_table, const int32_t* indptr, int32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, int32_t batch, int64_t num_blocks, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale, int32_t partition_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   // head ratio first, before anything else (validate before mutate)
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
   if (st != PKV_OK) return st;
@@ -380,8 +410,11 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks must be positive");
   if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
   if (batch < 1 || max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "batch and max_blocks_per_seq must be positive");
-  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  const int log2_bs = log2_block_size(block_size);
+  if (log2_bs < 0) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (8, 16, 32, 64, 128 or 256)", block_size);
   if (d_head != 64 && d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "d_head %d unsupported (64 or 128)", d_head);
+  st = check_row_space(num_blocks, n_kv_heads, block_size);
+  if (st != PKV_OK) return st;
   const bool combo_ok = (q_dtype == PKV_F32 && kv_dtype == PKV_F32) || (q_dtype == PKV_BF16 && kv_dtype == PKV_BF16) ||
                         (q_dtype == PKV_BF16 && kv_dtype == PKV_FP8_E4M3FN);
   if (!combo_ok) return fail(PKV_ERR_UNSUPPORTED, "(q, kv) dtype combination (%d, %d) unsupported", q_dtype, kv_dtype);
@@ -410,6 +443,7 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.block_table = block_table;
+  a.indptr = indptr;
   a.seq_lens = seq_lens;
   char* wsp = reinterpret_cast<char*>(workspace);
   a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(wsp + plan.ws_o_off) : nullptr;
@@ -423,6 +457,7 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.num_blocks = num_blocks;
   a.batch = batch;
   a.max_blocks = max_blocks_per_seq;
+  a.log2_bs = log2_bs;
   a.n_q = n_q_heads;
   a.n_kv = n_kv_heads;
   a.group = group;
@@ -433,6 +468,36 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
   a.out_bf16 = out_dtype == PKV_BF16;
   a.scale_log2 = scale * kLog2e;
   return hip_status(pkv::launch_decode(a, (int)kv_dtype, d_head, (hipStream_t)stream), "decode launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                             const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                             const float* k_scale, const float* v_scale,
+                                             const int32_t* block_table, int32_t max_blocks_per_seq,
+                                             const int32_t* seq_lens, int32_t batch, int64_t num_blocks,
+                                             int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                             int32_t block_size, float scale, int32_t partition_tokens,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr,
+                     max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size,
+                     scale, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attn_decode_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                     const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                     const float* k_scale, const float* v_scale, const int32_t* kv_indptr,
+                                     const int32_t* kv_indices, int32_t max_pages_per_seq, const int32_t* seq_lens,
+                                     int32_t batch, int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                                     int32_t d_head, int32_t block_size, float scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!kv_indptr) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, kv_indices, kv_indptr,
+                     max_pages_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size, scale,
+                     0, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
@@ -456,16 +521,16 @@ size_t pkv_paged_attn_prefill_workspace(int32_t num_seqs, int32_t max_q_len, int
   return 0;
 }
 
-pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
-                                        const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
-                                        int32_t total_q, int32_t max_q_len, const void* k_cache,
-                                        const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
-                                        const float* v_scale, const int32_t* block_table,
-                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads,
-                                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale,
-                                        int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype, const int32_t* cu_q_lens,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                        const void* k_cache, const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                        const float* v_scale, const int32_t* block_table, const int32_t* indptr,
+                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                        int32_t d_head, int32_t block_size, float scale, int32_t causal, void* stream) {
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
   if (st != PKV_OK) return st;
   if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
@@ -476,8 +541,11 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
     return fail(PKV_ERR_INVALID_ARG, "null pointer");
   if (num_blocks < 1 || max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
   if (num_blocks > (int64_t)1 << 31) return fail(PKV_ERR_UNSUPPORTED, "num_blocks beyond int32 block ids");
-  if (block_size != kBlockSize) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (16 only)", block_size);
+  const int log2_bs = log2_block_size(block_size);
+  if (log2_bs < 0) return fail(PKV_ERR_UNSUPPORTED, "block_size %d unsupported (8, 16, 32, 64, 128 or 256)", block_size);
   if (d_head != 128) return fail(PKV_ERR_UNSUPPORTED, "prefill supports d_head 128 only");
+  st = check_row_space(num_blocks, n_kv_heads, block_size);
+  if (st != PKV_OK) return st;
   if (q_dtype != PKV_BF16 || kv_dtype == PKV_F32)
     return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 q and bf16 or fp8 KV");
   if (kv_dtype == PKV_FP8_E4M3FN && (!k_scale || !v_scale))
@@ -500,11 +568,13 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   a.k_scale = k_scale;
   a.v_scale = v_scale;
   a.block_table = block_table;
+  a.indptr = indptr;
   a.num_blocks = num_blocks;
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.max_q_len = max_q_len;
   a.max_blocks = max_blocks_per_seq;
+  a.log2_bs = log2_bs;
   a.n_q = n_q_heads;
   a.n_kv = n_kv_heads;
   a.group = group;
@@ -513,6 +583,39 @@ pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const vo
   a.kv_fp8 = kv_dtype == PKV_FP8_E4M3FN;
   a.scale_log2 = scale * kLog2e;
   return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_paged_attn_prefill_chunk(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                        const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                        const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                                        const float* v_scale, const int32_t* block_table,
+                                        int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads,
+                                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale,
+                                        int32_t causal, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return prefill_impl(out, out_dtype, q, q_dtype, cu_q_lens, context_lens, num_seqs, total_q, max_q_len, k_cache,
+                      v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr, max_blocks_per_seq, num_blocks,
+                      n_q_heads, n_kv_heads, d_head, block_size, scale, causal, stream);
+}
+
+pkv_status pkv_paged_attn_prefill_chunk_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                            const int32_t* cu_q_lens, const int32_t* context_lens, int32_t num_seqs,
+                                            int32_t total_q, int32_t max_q_len, const void* k_cache,
+                                            const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
+                                            const float* v_scale, const int32_t* kv_indptr,
+                                            const int32_t* kv_indices, int32_t max_pages_per_seq, int64_t num_blocks,
+                                            int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                            int32_t block_size, float scale, int32_t causal, void* stream) {
+  if (!kv_indptr && total_q > 0 && max_q_len > 0) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  return prefill_impl(out, out_dtype, q, q_dtype, cu_q_lens, context_lens, num_seqs, total_q, max_q_len, k_cache,
+                      v_cache, kv_dtype, k_scale, v_scale, kv_indices, kv_indptr, max_pages_per_seq, num_blocks,
+                      n_q_heads, n_kv_heads, d_head, block_size, scale, causal, stream);
 }
 
 

@@ -16,7 +16,8 @@ struct DecodeArgs {
   const void* v_cache;
   const float* k_scale;
   const float* v_scale;
-  const int32_t* block_table;
+  const int32_t* block_table;  // 2-D [batch][max_blocks], or CSR page ids when indptr is set
+  const int32_t* indptr;       // CSR: sequence s owns block_table[indptr[s] .. indptr[s+1])
   const int32_t* seq_lens;
   float* ws_o;    // [batch][n_q][n_parts][d] partial outputs (unnormalised)
   float* ws_ml;   // [batch][n_q][n_parts][2] running max (log2 units) and sum
@@ -29,7 +30,8 @@ struct DecodeArgs {
   int32_t items_per_wg;  // queue mode: items the batch is cut into per workgroup
   int64_t num_blocks;
   int32_t batch;
-  int32_t max_blocks;
+  int32_t max_blocks;   // table row width (CSR: bound on the pages of one sequence)
+  int32_t log2_bs;      // tokens per cache block = 1 << log2_bs (8 .. 256)
   int32_t n_q;
   int32_t n_kv;
   int32_t group;        // n_q / n_kv
@@ -71,7 +73,10 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
 hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
                                  const int32_t* table, int32_t max_blocks, const int32_t* ctx_lens,
                                  const int32_t* cu_new, int32_t batch, int32_t max_new, const void* k_new,
-                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, hipStream_t stream);
+                                 const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, int32_t log2_bs,
+                                 hipStream_t stream);
+hipError_t launch_csr_to_table(const int32_t* indptr, const int32_t* indices, int32_t batch, int32_t max_blocks,
+                               int32_t* table, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
 
@@ -84,12 +89,14 @@ struct PrefillArgs {
   const void* v_cache;
   const float* k_scale;  // FP8 KV: per (block, KV head)
   const float* v_scale;
-  const int32_t* block_table;
+  const int32_t* block_table;  // as in DecodeArgs
+  const int32_t* indptr;
   int64_t num_blocks;
   int32_t num_seqs;
   int32_t total_q;
   int32_t max_q_len;
   int32_t max_blocks;
+  int32_t log2_bs;
   int32_t n_q;
   int32_t n_kv;
   int32_t group;
@@ -100,5 +107,41 @@ struct PrefillArgs {
 };
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream);
 bool prefill_supported_group(int group);
+
+
+// ---- page-table walk shared by the attention kernels ----
+// A sequence's blocks: a row of the 2-D table, or its CSR slice (at most
+// max_blocks entries).  The kernels work in 16-token tiles made of two 8-token
+// halves; half h of tile q holds tokens 16 q + 8 h .. + 7, all in one cache
+// block for every block size from 8 to 256.
+struct PageRow {
+  const int32_t* ids;
+  int32_t n;  // entries of the row
+};
+
+template <class A>
+__device__ __forceinline__ PageRow page_row(const A& a, int s) {
+  if (a.indptr) {
+    const int b = a.indptr[s], e = a.indptr[s + 1];
+    return {a.block_table + b, min(max(e - b, 0), a.max_blocks)};
+  }
+  return {a.block_table + (int64_t)s * a.max_blocks, a.max_blocks};
+}
+
+// Block id of the block holding sequence token `tok`: entries past the row and
+// ids outside the pool are clamped into it (the rows they lead to are masked).
+template <class A>
+__device__ __forceinline__ int page_block(const A& a, const PageRow& r, int tok) {
+  const int j = tok >> a.log2_bs;
+  const int id = j < r.n ? r.ids[j] : 0;
+  return min(max(id, 0), (int)(a.num_blocks - 1));
+}
+
+// Row index of token `tok` in the [num_blocks][n_kv][B] row space of KV head
+// kvh, block `id` (the host keeps num_blocks * n_kv * B below 2^32).
+template <class A>
+__device__ __forceinline__ uint32_t page_row_index(const A& a, int id, int kvh, int tok) {
+  return (((uint32_t)id * (uint32_t)a.n_kv + (uint32_t)kvh) << a.log2_bs) | (uint32_t)(tok & ((1 << a.log2_bs) - 1));
+}
 
 }  // namespace pkv

@@ -14,7 +14,8 @@
 //   A workgroup owns 128 packed query rows of one sequence and one KV head:
 //   row r = (token r / G, head r % G), so the G heads that share the KV head
 //   reuse every K/V tile.  Each wave owns 32 rows (two 16-row MFMA tiles).
-//   Per 64-key tile (four 16-token cache blocks looked up in the table):
+//   Per 64-key tile (eight 8-key halves, each inside one cache block of 8 ..
+//   256 tokens, looked up in the 2-D or CSR table):
 //     K and V slabs -> LDS (16-byte loads, issued one tile ahead);
 //     S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (K from LDS, Q in registers),
 //     so each lane holds four keys of one query row;
@@ -37,7 +38,7 @@ namespace pkv {
 namespace {
 
 constexpr int D = 128;
-constexpr int BS = 16;          // tokens per cache block
+constexpr int BS = 16;          // keys per wave part of a tile (two 8-key halves, each in one cache block)
 constexpr int KT = 64;          // keys per tile
 constexpr int ROWS = 128;       // packed query rows per workgroup
 constexpr int NT = 2;           // 16-row MFMA tiles per wave
@@ -47,7 +48,7 @@ constexpr int STAGE_B = 2 * TILE_B;  // K tile then V tile
 constexpr int kStages = 2;      // tiles in flight through LDS
 constexpr int kXcds = 8;        // XCDs the dispatcher spreads workgroup ids over
 constexpr int kMaxSortSeqs = 256;  // batches up to this size are ordered longest first
-constexpr int BLK8_B = BS * D;     // one block's K (or V) codes, FP8
+constexpr int BLK8_B = BS * D;     // FP8 codes of one wave part (16 keys) of K or V
 constexpr int STG8_B = (KT / BS) * 2 * BLK8_B;  // one tile's K and V codes
 static_assert(STAGE_B + 2 * STG8_B <= kStages * STAGE_B, "FP8 tile + staging must fit the bf16 stages");
 
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // bf16 KV: kStages tiles (K then V).  FP8 KV: one bf16 tile at the start,
   // then two staging buffers of codes, per wave [K block][V block].
   __shared__ __align__(16) char smem[kStages * STAGE_B];
-  __shared__ float blk_scale[2][KT / BS];  // FP8: K and V scale of the tile's blocks
+  __shared__ float blk_scale[2][2 * KT / BS];  // FP8: K and V scale of each 8-token half of the tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   if (sorted) {
     const int t = threadIdx.x;
     if (t < a.num_seqs) {
-      const int cs = min(max(a.ctx_lens[t], 0), a.max_blocks * BS);
+      const int cs = min(max(a.ctx_lens[t], 0), page_row(a, t).n << a.log2_bs);
       const int qb = min(max(a.cu_q[t], 0), a.total_q), qe = min(max(a.cu_q[t + 1], qb), a.total_q);
       seq_key[t] = cs + (qe - qb);
     }
@@ -148,10 +149,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int qs = min(max(a.cu_q[s], 0), a.total_q);
   const int q_len = min(a.cu_q[s + 1], a.total_q) - qs;
   if (q0 >= q_len) return;
-  const int ctx = min(max(a.ctx_lens[s], 0), a.max_blocks * BS);  // keeps every tile inside the table
+  const PageRow prow = page_row(a, s);
+  const int ctx = min(max(a.ctx_lens[s], 0), prow.n << a.log2_bs);  // keeps every tile inside the table
   const int total = ctx + q_len;        // keys that exist for this sequence
   const int last_q = min(q0 + tq, q_len) - 1;
-  const int kv_end = a.causal ? ctx + last_q + 1 : total;  // keys any row of the tile sees
+  // keys any row of the tile sees (none when the table row is empty)
+  const int kv_end = prow.n == 0 ? 0 : a.causal ? ctx + last_q + 1 : total;
   const int n_tiles = (kv_end + KT - 1) / KT;
   const int diag0 = ctx + q0;           // keys >= diag0 are masked for some row
 
@@ -190,61 +193,74 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     l_run[nt] = 0.f;
   }
 
-  // ---- tile loads: wave w brings block w of the tile (16 keys) straight into
-  // LDS, 4 KiB of K and 4 KiB of V in four 1-KiB instructions each; its block
-  // id is fetched one tile ahead of the loads that use it
+  // ---- tile loads: wave w brings keys 16 w .. 16 w + 15 of the tile straight
+  // into LDS, 4 KiB of K and 4 KiB of V in four 1-KiB instructions each; the
+  // block ids of its two halves are fetched one tile ahead of the loads
   const char* const kc = reinterpret_cast<const char*>(a.k_cache);
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
-  const int32_t* trow = a.block_table + (int64_t)s * a.max_blocks;
-  const int n_lblocks = (kv_end + BS - 1) / BS;  // logical blocks any row of the tile sees
+
+  const int n_lblocks = (kv_end + BS - 1) / BS;  // 16-key parts any row of the workgroup sees
   // The raw table entry is fetched one tile ahead and checked only when its
   // loads are issued, so nothing waits on the fetch in between.
+  // A tile part (16 keys) is two 8-key halves, each inside one cache block.
+  // Only the entry index is clamped here (to the row, which is not empty when
+  // there are tiles); the ids are checked when their loads are issued, so the
+  // wave does not wait on this fetch in between.
   auto fetch_id = [&](int kt) {
-    const int lb = kt * (KT / BS) + w;
-    return trow[min(lb, a.max_blocks - 1)];
+    const int tok = (kt * (KT / BS) + w) * BS;
+    const int last = prow.n - 1;
+    return int2{prow.ids[min(tok >> a.log2_bs, last)], prow.ids[min((tok + 8) >> a.log2_bs, last)]};
   };
   // Per-lane source offsets inside a block, one per instruction k: lane l
   // brings key row r = 4k + l / 16 and the global piece that lands in slot
   // l % 16 of that row (r < 16, so the swizzle takes r as is).
+  // (Instructions 0, 1 bring the first half's rows, 2, 3 the second's;
+  // offsets are relative to the half's first row.)
   uint32_t src_off[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = 4 * k + (lane >> 4);
-    src_off[k] = r * ROWB + (((lane & 15) ^ swz_f(r)) << 4);
+    src_off[k] = (r & 7) * ROWB + (((lane & 15) ^ swz_f(r)) << 4);
   }
   const uint32_t lds0 = lds_addr(smem) + BS * w * ROWB;  // this wave's first tile row
   // FP8: this wave's staging slot and the scales of the block it loads
   const uint32_t stg0 = lds_addr(smem) + STAGE_B + w * 2 * BLK8_B;
-  float ks_load = 0.f, vs_load = 0.f;  // scales of the block last issued (0 when none)
-  auto issue = [&](int kt, int raw_id) {
+  float ks_load[2] = {0.f, 0.f}, vs_load[2] = {0.f, 0.f};  // scales of the halves last issued (0 when none)
+  auto issue = [&](int kt, int2 raw_id) {
     const int lb = kt * (KT / BS) + w;
     if (FP8) {
-      ks_load = 0.f;
-      vs_load = 0.f;
+      ks_load[0] = ks_load[1] = vs_load[0] = vs_load[1] = 0.f;
     }
-    if (lb >= n_lblocks || lb >= a.max_blocks) return;  // nothing to load for this wave
-    const int id = min(max(__builtin_amdgcn_readfirstlane(raw_id), 0), (int)(a.num_blocks - 1));
+    if (lb >= n_lblocks) return;  // nothing to load for this wave
+    const int nb1 = (int)(a.num_blocks - 1);
+    const int id[2] = {min(max(__builtin_amdgcn_readfirstlane(raw_id.x), 0), nb1),
+                       min(max(__builtin_amdgcn_readfirstlane(raw_id.y), 0), nb1)};
+    int64_t half[2];  // byte offset of each half's first row (KV head kvh)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      half[h] = (int64_t)page_row_index(a, id[h], kvh, lb * BS + 8 * h) * (FP8 ? D : ROWB);
     if (FP8) {
-      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * BLK8_B;
       const uint32_t dst = stg0 + (kt & 1) * STG8_B;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        lds_dma16(kc + slab, k * 1024 + 16 * lane, dst + k * 1024);
-        lds_dma16(vc + slab, k * 1024 + 16 * lane, dst + BLK8_B + k * 1024);
+        lds_dma16(kc + half[k], 16 * lane, dst + k * 1024);
+        lds_dma16(vc + half[k], 16 * lane, dst + BLK8_B + k * 1024);
       }
-      ks_load = a.k_scale[(int64_t)id * a.n_kv + kvh];
-      vs_load = a.v_scale[(int64_t)id * a.n_kv + kvh];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        ks_load[h] = a.k_scale[(int64_t)id[h] * a.n_kv + kvh];
+        vs_load[h] = a.v_scale[(int64_t)id[h] * a.n_kv + kvh];
+      }
     } else {
-      const int64_t slab = ((int64_t)id * a.n_kv + kvh) * (BS * ROWB);
       const uint32_t dst = lds0 + (kt % kStages) * STAGE_B;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        lds_dma16(kc + slab, src_off[k], dst + 4 * k * ROWB);
-        lds_dma16(vc + slab, src_off[k], dst + TILE_B + 4 * k * ROWB);
+        lds_dma16(kc + half[k >> 1], src_off[k], dst + 4 * k * ROWB);
+        lds_dma16(vc + half[k >> 1], src_off[k], dst + TILE_B + 4 * k * ROWB);
       }
     }
   };
-  int id_next = 0;
+  int2 id_next = int2{0, 0};
   if (n_tiles > 0) {
     issue(0, fetch_id(0));
     if (n_tiles > 1) id_next = fetch_id(1);
@@ -255,7 +271,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const char* const k_lds = smem + (FP8 ? 0 : (kt % kStages) * STAGE_B);
     const char* const v_lds = k_lds + TILE_B;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads of tile kt have landed
-    const float ks_tile = ks_load, vs_tile = vs_load;  // FP8: scales of this wave's block of tile kt
+    // FP8: scales of this wave's halves of tile kt
+    const float ks_tile0 = ks_load[0], ks_tile1 = ks_load[1], vs_tile0 = vs_load[0], vs_tile1 = vs_load[1];
     if (!FP8 && kt * KT + KT > kv_end) {
       // the keys this workgroup sees end inside this tile: V rows past them
       // (rows no load wrote, or past the sequence end) may hold anything, NaN
@@ -272,6 +289,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       issue(kt + 1, id_next);
       if (kt + 2 < n_tiles) id_next = fetch_id(kt + 2);
     }
+    // FP8: this lane's K and V scale per 16-key part t of the tile: its keys
+    // 4 g .. 4 g + 3 of each part lie in the part's half g / 2
     float ksc[KT / BS], vsc[KT / BS];
     if (FP8) {
       // widen this wave's block of codes into rows 16w .. 16w+15 of the bf16
@@ -298,14 +317,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
                keep ? u32x4{bw[4 * i], bw[4 * i + 1], bw[4 * i + 2], bw[4 * i + 3]} : u32x4{0, 0, 0, 0});
       }
       if (lane == 0) {
-        blk_scale[0][w] = ks_tile;
-        blk_scale[1][w] = vs_tile;
+        blk_scale[0][2 * w] = ks_tile0;
+        blk_scale[0][2 * w + 1] = ks_tile1;
+        blk_scale[1][2 * w] = vs_tile0;
+        blk_scale[1][2 * w + 1] = vs_tile1;
       }
       __syncthreads();  // the bf16 tile and its scales are complete
+      const int hs = g >> 1;
 #pragma unroll
       for (int t = 0; t < KT / BS; ++t) {
-        ksc[t] = blk_scale[0][t];
-        vsc[t] = blk_scale[1][t];
+        const float k0 = blk_scale[0][2 * t], k1 = blk_scale[0][2 * t + 1];
+        const float v0 = blk_scale[1][2 * t], v1 = blk_scale[1][2 * t + 1];
+        ksc[t] = hs ? k1 : k0;
+        vsc[t] = hs ? v1 : v0;
       }
     }
 
@@ -385,8 +409,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         if (FP8) {
           // weights enter the value product scaled by their block's V scale
           ls += (p4[0] + p4[1]) + (p4[2] + p4[3]);
-          pk[t][0] = pack_bf16(p4[0] * vsc[t], p4[1] * vsc[t]);
-          pk[t][1] = pack_bf16(p4[2] * vsc[t], p4[3] * vsc[t]);
+          const float vs = vsc[t];
+          pk[t][0] = pack_bf16(p4[0] * vs, p4[1] * vs);
+          pk[t][1] = pack_bf16(p4[2] * vs, p4[3] * vs);
         } else {
           pk[t][0] = pack_bf16(p4[0], p4[1]);
           pk[t][1] = pack_bf16(p4[2], p4[3]);

@@ -332,6 +332,61 @@ def check_paged_equals_contiguous(orc):
     assert nb >= 5
 
 
+def check_block_sizes_and_csr(orc):
+    """The same sequences paged into blocks of 8, 16 and 64 tokens, through a
+    2-D table or as CSR rows, give bitwise-equal decode and prefill outputs
+    ([KVP] Problem 4: block = p // B, offset = p % B; [MEM] "Walking the
+    table"), equal to attention over the unpaged rows within rounding."""
+    r = np.random.default_rng(21)
+    n_q, n_kv, d = 4, 2, 8
+    lens = [1, 7, 8, 9, 40, 100]
+    rows_k = [r.standard_normal((L, n_kv, d)) for L in lens]
+    rows_v = [r.standard_normal((L, n_kv, d)) for L in lens]
+    q = r.standard_normal((len(lens), n_q, d)).astype(np.float32)
+    scale = 0.3
+    outs, pre = [], []
+    for B in (8, 16, 64):
+        need = [-(-L // B) for L in lens]
+        nb = sum(need) + 3
+        perm = r.permutation(nb)
+        k = np.full((nb, n_kv, B, d), np.nan, np.float32)
+        v = np.full((nb, n_kv, B, d), np.nan, np.float32)
+        table = np.full((len(lens), max(need)), -1, np.int32)
+        cur = 0
+        for s, L in enumerate(lens):
+            ids = perm[cur:cur + need[s]]
+            cur += need[s]
+            table[s, :need[s]] = ids
+            for p in range(L):
+                k[ids[p // B], :, p % B] = rows_k[s][p]
+                v[ids[p // B], :, p % B] = rows_v[s][p]
+        out = orc.paged_decode(q, "f32", k, v, "f32", None, None, table, lens, n_q, n_kv, scale)
+        indptr = np.concatenate([[0], np.cumsum(need)]).astype(np.int32)
+        indices = np.concatenate([table[s, :need[s]] for s in range(len(lens))]).astype(np.int32)
+        csr_rows = [orc.csr_pages(indptr, indices, s) for s in range(len(lens))]
+        out_csr = orc.paged_decode(q, "f32", k, v, "f32", None, None, csr_rows, lens, n_q, n_kv, scale)
+        assert np.array_equal(out, out_csr)
+        outs.append(out)
+        # prefill: the last 3 tokens of each sequence as the chunk
+        ql = np.minimum(3, lens)
+        ctx = np.array(lens) - ql
+        cu = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        qp = np.random.default_rng(5).standard_normal((int(cu[-1]), n_q, d)).astype(np.float32)
+        pre.append(orc.paged_prefill(qp, "f32", cu, ctx, k, v, "f32", None, None, csr_rows, n_q, n_kv, scale))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    for o in pre[1:]:
+        assert np.array_equal(o, pre[0])
+    # and the unpaged computation agrees
+    for s, L in enumerate(lens):
+        for h in range(n_q):
+            kv = h // (n_q // n_kv)
+            sc = rows_k[s][:, kv, :].astype(np.float32).astype(np.float64) @ q[s, h].astype(np.float64) * scale
+            w = np.exp(sc - sc.max())
+            want = (w / w.sum()) @ rows_v[s][:, kv, :].astype(np.float32).astype(np.float64)
+            assert np.allclose(outs[0][s, h], want, rtol=1e-12, atol=1e-12)
+
+
 def check_cache_equals_recompute(orc):
     """T steps of append-then-attend through the paged cache equal full causal
     attention recomputed from all inputs at each step (synthetic projections)."""
@@ -514,7 +569,7 @@ ALL_CHECKS = [
     check_sizing, check_csr_walk, check_waste, check_append_gather, check_e4m3, check_bf16,
     check_bruteforce_decode, check_sdpa_decode, check_sdpa_prefill, check_prefill_reductions,
     check_paged_equals_contiguous, check_cache_equals_recompute, check_head_grouping, check_special_cases,
-    check_online_softmax, check_demo_shapes, check_poison_ignored,
+    check_online_softmax, check_demo_shapes, check_poison_ignored, check_block_sizes_and_csr,
 ]
 
 

@@ -75,7 +75,9 @@ def test_decode_validation_before_launch(pkv):
     assert _decode(lib, n_kv=0) == pkv.ERR_INVALID_ARG
     assert _decode(lib, q=None) == pkv.ERR_INVALID_ARG
     assert _decode(lib, d=96) == pkv.ERR_UNSUPPORTED
-    assert _decode(lib, bs=32) == pkv.ERR_UNSUPPORTED
+    assert _decode(lib, bs=24) == pkv.ERR_UNSUPPORTED               # block sizes: powers of two 8 .. 256
+    assert _decode(lib, bs=512) == pkv.ERR_UNSUPPORTED
+    assert _decode(lib, bs=4) == pkv.ERR_UNSUPPORTED
     assert _decode(lib, q_dtype=0) == pkv.ERR_UNSUPPORTED          # f32 q with bf16 KV
     assert _decode(lib, kv_dtype=2) == pkv.ERR_INVALID_ARG         # fp8 without scales
     assert _decode(lib, scale=0.0) == pkv.ERR_INVALID_ARG
@@ -85,6 +87,32 @@ def test_decode_validation_before_launch(pkv):
     assert need > 0
     assert _decode(lib, max_blocks=256, part=256, ws=0x1000, ws_n=need - 1) == pkv.ERR_WORKSPACE
     assert _decode(lib, max_blocks=256, part=256, ws=0x1001, ws_n=need) == pkv.ERR_INVALID_ARG  # misaligned
+
+
+def test_csr_entry_points_validate(pkv):
+    lib = pkv.load()
+    # decode: no indptr; unsupported block size; row space beyond 2^32
+    args = [0x1000, 0, 0x2000, 1, 0x3000, 0x4000, 1, None, None, 0x5000, 0x6000, 4, 0x7000, 2, 64, 8, 2, 128, 16,
+            0.088, None, 0, None]
+    a = list(args); a[9] = None
+    assert lib.pkv_paged_attn_decode_csr(*a) == pkv.ERR_INVALID_ARG
+    a = list(args); a[18] = 12
+    assert lib.pkv_paged_attn_decode_csr(*a) == pkv.ERR_UNSUPPORTED
+    a = list(args); a[14] = 1 << 28; a[18] = 256
+    assert lib.pkv_paged_attn_decode_csr(*a) == pkv.ERR_UNSUPPORTED
+    # prefill: fp8 without scales, block size, empty chunk is a no-op
+    pargs = [0x1000, 0, 0x2000, 1, 0x3000, 0x4000, 2, 64, 32, 0x5000, 0x6000, 1, None, None, 0x7000, 0x8000, 4, 32,
+             8, 2, 128, 16, 0.088, 1, None]
+    a = list(pargs); a[11] = 2
+    assert lib.pkv_paged_attn_prefill_chunk_csr(*a) == pkv.ERR_INVALID_ARG
+    a = list(pargs); a[21] = 48
+    assert lib.pkv_paged_attn_prefill_chunk_csr(*a) == pkv.ERR_UNSUPPORTED
+    a = list(pargs); a[7] = 0
+    assert lib.pkv_paged_attn_prefill_chunk_csr(*a) == pkv.OK
+    # expansion: empty batch is a no-op, null pointers are rejected
+    assert lib.pkv_csr_to_block_table(None, None, 0, 4, None, None) == pkv.OK
+    assert lib.pkv_csr_to_block_table(None, 0x1000, 2, 4, 0x2000, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_csr_to_block_table(0x1000, 0x1000, 2, 0, 0x2000, None) == pkv.ERR_INVALID_ARG
 
 
 def test_decode_workspace_sizes(pkv):
@@ -109,8 +137,8 @@ def test_other_entry_points_validate(pkv):
     assert fa(*args) == pkv.OK                       # max_new_len 0: no-op
     args = list(good); args[13] = 2
     assert fa(*args) == pkv.ERR_UNSUPPORTED          # new rows already FP8
-    args = list(good); args[16] = 8
-    assert fa(*args) == pkv.ERR_UNSUPPORTED          # block size 8
+    args = list(good); args[16] = 12
+    assert fa(*args) == pkv.ERR_UNSUPPORTED          # block size 12
     args = list(good); args[15] = 96
     assert fa(*args) == pkv.ERR_UNSUPPORTED          # d 96
     args = list(good); args[11] = 0x8004

@@ -27,6 +27,9 @@ MUTATIONS = [
     ("attention.py", "V = V * gather_scales(v_scale,", "V = V * gather_scales(k_scale,"),
     ("attention.py", "L = int(seq_lens[seq])", "L = int(seq_lens[seq]) - 1"),
     ("paging.py", "offset = pos % block_size", "offset = block_size - 1 - pos % block_size"),
+    ("paging.py", "    block_size = cache.shape[2]\n    rows = []", "    block_size = 16\n    rows = []"),
+    ("paging.py", "return list(kv_indices[kv_indptr[request]:kv_indptr[request + 1]])",
+     "return list(kv_indices[kv_indptr[request]:kv_indptr[request + 1] + 1])"),
     ("paging.py", "physical_block = int(block_table[seq][pos // block_size])",
      "physical_block = int(block_table[seq][pos // block_size]) + 1"),
     ("paging.py", "rows.append(cache[block, :, p % block_size, :])", "rows.append(cache[block, :, (p + 1) % block_size, :])"),
