@@ -15,7 +15,8 @@ Sources (three web pages):
     "MHA, MQA, and GQA", "Method 3: PagedAttention", "Walking the table",
     "FlashAttention" (numerically stable softmax, causal -inf mask).
     "Prefix sharing" (a shared prefix stored once); Problem 4 of the first
-    page for block sharing with reference counts and copy-on-write.
+    page for block sharing with reference counts and copy-on-write, and for
+    preemption by swapping blocks to CPU memory.
   * "The KV Cache from First Principles" -- "The redundancy" (the query
     attends positions 1..t including itself), "Implementation" (query head h
     uses KV head h // (n_q / n_kv); the head-ratio check runs before the cache
@@ -31,6 +32,7 @@ from .attention import (head_to_kv_head, softmax_attention_rows, paged_decode, p
                         decode_one, prefill_one)
 from .sharing import BlockPool, PoolExhausted, copy_blocks
 from .quant import encode_e4m3fn, append_block_fp8, kv_append_fp8
+from .swap import swap_image, swap_in
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_to_f64", "f32_to_f64", "decode_storage",
@@ -40,4 +42,5 @@ __all__ = [
     "decode_one", "prefill_one",
     "BlockPool", "PoolExhausted", "copy_blocks",
     "encode_e4m3fn", "append_block_fp8", "kv_append_fp8",
+    "swap_image", "swap_in",
 ]

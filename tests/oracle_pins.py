@@ -799,3 +799,86 @@ def check_fp8_append_invariants(orc):
 
 
 ALL_CHECKS += [check_e4m3_encode, check_fp8_append_fixture, check_fp8_append_one_shot, check_fp8_append_invariants]
+
+# ---------------------------------------------------------------------------
+# preemption by swap
+# ---------------------------------------------------------------------------
+
+def _swap_fixture_caches():
+    k16 = np.zeros((3, 1, 2, 2), np.uint16)
+    for b in range(3):
+        k16[b, 0] = [[0x0001 + 0x10 * b, 0x0002 + 0x10 * b], [0x0003 + 0x10 * b, 0x0004 + 0x10 * b]]
+    v16 = k16 + np.uint16(0x0100)
+    k8 = np.zeros((2, 2, 1, 2), np.uint8)
+    for b in range(2):
+        for h in range(2):
+            k8[b, h, 0] = [0x10 * b + 2 * h, 0x10 * b + 2 * h + 1]
+    v8 = k8 | np.uint8(0x80)
+    ks = np.array([[1, 2], [3, 4]], np.float32)
+    vs = np.array([[0.5, 0.25], [8, 16]], np.float32)
+    return k16, v16, k8, v8, ks, vs
+
+
+def check_swap_fixture(orc):
+    """Host images of the hand-worked example, byte for byte, and swapping
+    them back in restores the blocks."""
+    g = _golden("swap_image.json")
+    k16, v16, k8, v8, ks, vs = _swap_fixture_caches()
+    img = orc.swap_image(k16, v16, g["bf16"]["ids"])
+    assert [f"{b:02x}" for b in img] == g["bf16"]["image"]
+    img8 = orc.swap_image(k8, v8, g["fp8"]["ids"], ks, vs)
+    assert [f"{b:02x}" for b in img8] == g["fp8"]["image"]
+    k2, v2, _, _ = orc.swap_in(np.zeros_like(k16), np.zeros_like(v16), img, [0, 1])
+    assert np.array_equal(k2[0], k16[2]) and np.array_equal(k2[1], k16[0]) and np.all(k2[2] == 0)
+    assert np.array_equal(v2[0], v16[2]) and np.array_equal(v2[1], v16[0])
+    k3, v3, ks3, vs3 = orc.swap_in(np.zeros_like(k8), np.zeros_like(v8), img8, [0], np.zeros_like(ks),
+                                   np.zeros_like(vs))
+    assert np.array_equal(k3[0], k8[1]) and np.array_equal(v3[0], v8[1])
+    assert np.array_equal(ks3[0], ks[1]) and np.array_equal(vs3[0], vs[1]) and np.all(ks3[1] == 0)
+
+
+def check_swap_equals_block_copy(orc):
+    """Swapping blocks A out and into blocks B moves exactly what the block
+    copy of pairs (A[i], B[i]) moves, for every element type."""
+    r = np.random.default_rng(31)
+    for kind, d in (("f32", 4), ("bf16", 8), ("fp8", 16)):
+        dt = synth.STORAGE_DTYPE[kind]
+        nb, n_kv, B = 10, 2, 4
+        k = r.integers(0, 256, size=(nb, n_kv, B, d * np.dtype(dt).itemsize), dtype=np.uint8).view(dt)
+        v = r.integers(0, 256, size=(nb, n_kv, B, d * np.dtype(dt).itemsize), dtype=np.uint8).view(dt)
+        ks = r.random((nb, n_kv)).astype(np.float32) if kind == "fp8" else None
+        vs = r.random((nb, n_kv)).astype(np.float32) if kind == "fp8" else None
+        src, dst = [7, 2, 5], [0, 9, 3]
+        img = orc.swap_image(k, v, src, ks, vs)
+        got = orc.swap_in(k, v, img, dst, ks, vs)
+        want = orc.copy_blocks(k, v, list(zip(src, dst)), ks, vs)
+        for a, b in zip(got, want):
+            if a is not None:
+                assert np.array_equal(np.ascontiguousarray(a).view(np.uint8), np.ascontiguousarray(b).view(np.uint8))
+
+
+def check_swap_preemption_decode(orc):
+    """Preempt a sequence (swap its blocks out, let other data overwrite them),
+    bring it back into other blocks and point its table there: its decode
+    output is bitwise what it was before ([KVP] Problem 4: blocks are reached
+    only through the table)."""
+    c = _decode_case(config=97, layer=0, n_q=4, n_kv=2, d=16, seq_lens=[5, 40, 23], kv_dtype="fp8", num_blocks=12)
+    before = _run_decode(orc, c)
+    s = 1
+    n = -(-int(c.seq_lens[s]) // 16)
+    ids = [int(b) for b in c.block_table[s, :n]]
+    img = orc.swap_image(c.k_cache, c.v_cache, ids, c.k_scale, c.v_scale)
+    k, v, ks, vs = c.k_cache.copy(), c.v_cache.copy(), c.k_scale.copy(), c.v_scale.copy()
+    k[ids] = 0x7F  # the freed blocks are reused: NaN codes
+    v[ids] = 0x7F
+    used = set(int(b) for b in c.block_table.reshape(-1) if b >= 0)
+    fresh = [b for b in range(12) if b not in used][:n]
+    assert len(fresh) == n
+    k, v, ks, vs = orc.swap_in(k, v, img, fresh, ks, vs)
+    table = c.block_table.copy()
+    table[s, :n] = fresh
+    after = _run_decode(orc, c, k_cache=k, v_cache=v, block_table=table, k_scale=ks, v_scale=vs)
+    assert np.array_equal(before, after)
+
+
+ALL_CHECKS += [check_swap_fixture, check_swap_equals_block_copy, check_swap_preemption_decode]

@@ -51,6 +51,12 @@ MUTATIONS = [
     ("sharing.py", "            self.ref[b] += 1", "            self.ref[b] += 2"),
     ("sharing.py", "        k[dst] = k_cache[src]", "        k[dst] = v_cache[src]"),
     ("sharing.py", "            vs[dst] = v_scale[src]", "            vs[dst] = k_scale[src]"),
+    ("swap.py", "    parts += [_raw(v_cache[int(b)]).reshape(-1) for b in ids]",
+     "    parts += [_raw(k_cache[int(b)]).reshape(-1) for b in ids]"),
+    ("swap.py", "    parts = [_raw(k_cache[int(b)]).reshape(-1) for b in ids]",
+     "    parts = [_raw(k_cache[int(b)]).reshape(-1) for b in ids[::-1]]"),
+    ("swap.py", "        parts += [_raw(v_scale[int(b)]).reshape(-1) for b in ids]\n", ""),
+    ("swap.py", "        off += n * size\n", "        off += size\n"),
     ("quant.py", "        codes[:n_old] = encode_e4m3fn(vals / new)\n", ""),
     ("quant.py", "np.float32(m / _F448)", "np.float32(m / np.float32(256.0))"),
     ("quant.py", "(codes[hi] % 2 == 0)", "(codes[hi] % 2 == 1)"),
