@@ -419,6 +419,55 @@ def traffic_from_profile(workload_key):
 
 # ---------------------------------------------------------------------------
 
+def swap_bench(cfg, args):
+    """Swap N blocks of one layer of a decode workload out to pinned host
+    memory and back (preemption by swap); image bytes / time per direction,
+    beside a plain pinned copy of the same size."""
+    import torch
+    import paged_kv_cache_blocks_amd as pkv
+    w = DecodeWorkload(cfg, 1, "copy", args.block_size)
+    table = w.block_table_np
+    ids_np = table[table >= 0][:args.swap_blocks].astype(np.int32)
+    n = len(ids_np)
+    ids = torch.from_numpy(ids_np).cuda()
+    code = pkv.dtype_code(w.k[0])
+    nbytes = pkv.swap_image_bytes(n, code, w.n_kv, w.d, w.bs)
+    staging = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    host = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    kw = dict(k_scale=w.ks[0], v_scale=w.vs[0])
+    k0, v0 = w.k[0].clone(), w.v[0].clone()
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) / 1e3
+
+    reps = max(args.steps, 5)
+    t_out = timed(lambda: pkv.swap_out(w.k[0], w.v[0], ids, staging, host, **kw), reps)
+    t_in = timed(lambda: pkv.swap_in(w.k[0], w.v[0], ids, staging, host, **kw), reps)
+    t_d2h = timed(lambda: host.copy_(staging, non_blocking=True), reps)
+    t_h2d = timed(lambda: staging.copy_(host, non_blocking=True), reps)
+    torch.cuda.synchronize()
+    # out then in to the same blocks leaves every byte as it was (NaN-poisoned slots included)
+    same = bool(torch.equal(w.k[0].view(torch.uint8), k0.view(torch.uint8)) and
+                torch.equal(w.v[0].view(torch.uint8), v0.view(torch.uint8)))
+    return {"metric": "preemption by swap: host-link GB/s (out, in)", "value": round(nbytes / t_out / 1e9, 2),
+            "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+            "config": {"workload": w.name, "blocks": n, "block_size": w.bs, "image_bytes": nbytes,
+                       "kv_dtype": w.kind},
+            "swap_out_GBps": round(nbytes / t_out / 1e9, 2), "swap_in_GBps": round(nbytes / t_in / 1e9, 2),
+            "swap_out_us": round(t_out * 1e6, 1), "swap_in_us": round(t_in * 1e6, 1),
+            "plain_copy_d2h_GBps": round(nbytes / t_d2h / 1e9, 2), "plain_copy_h2d_GBps": round(nbytes / t_h2d / 1e9, 2),
+            "round_trip_bit_exact": same}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -429,6 +478,8 @@ def main():
     ap.add_argument("--cpu-sample-layers", type=int, default=8)
     ap.add_argument("--fp8-append", choices=["copy", "quantize"], default="copy",
                     help="FP8 workload: copy ready-made codes, or quantise bf16 rows on append")
+    ap.add_argument("--swap-blocks", type=int, default=0,
+                    help="time swapping this many blocks of one decode layer out to pinned host memory and back")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64, 128, 256],
                     help="decode workloads: tokens per cache block (the same sequences, re-paged)")
     ap.add_argument("--csr", action="store_true", help="decode workloads: pass the page table in CSR form")
@@ -459,6 +510,9 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
+    if args.swap_blocks:
+        print(json.dumps(swap_bench(cfg, args)))
+        return
     t_build = time.perf_counter()
     w = (PrefillWorkload(cfg, args.prefill_kv) if prefill
          else DecodeWorkload(cfg, args.layers, args.fp8_append, args.block_size, args.csr))

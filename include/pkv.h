@@ -208,6 +208,46 @@ pkv_status pkv_copy_blocks(void* k_cache, void* v_cache, pkv_dtype cache_dtype, 
                            int64_t num_blocks, const int32_t* src, const int32_t* dst, int32_t n_pairs,
                            int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
 
+/* ---- Preemption by swap ([KVP] Problem 4, "The idea" and "Trade-offs": when
+ * memory runs out a sequence's blocks can be moved to CPU memory and brought
+ * back later instead of recomputed; a sequence reaches its blocks only
+ * through its table, so they may come back into any free blocks).
+ * Host image of n listed blocks: [K of block 0 .. n-1][V of block 0 .. n-1]
+ * [K scales][V scales], a block's K (or V) being its whole slab
+ * (n_kv_heads x block_size x d_head elements) and the scale sections
+ * (n x n_kv_heads fp32 each) present for FP8 caches only. */
+
+/* Bytes of the host image (and of the staging buffer) for n_blocks blocks;
+ * 0 for invalid arguments. */
+size_t pkv_swap_image_bytes(int32_t n_blocks, pkv_dtype cache_dtype, int32_t n_kv_heads, int32_t d_head,
+                            int32_t block_size);
+
+/* Swap out: packs blocks block_ids[0 .. n_blocks) (device int32; an id
+ * outside [0, num_blocks) leaves its image slot unwritten) into `staging`
+ * (device, 16-byte aligned, >= pkv_swap_image_bytes, else
+ * PKV_ERR_WORKSPACE), then copies the image to `host_image` (host memory the
+ * caller allocated pinned, e.g. hipHostMalloc, for the copy to run
+ * asynchronously on the DMA engines; pageable memory works but the copy may
+ * block), both on `stream`.  The image is complete once the stream reaches
+ * this point; staging and host_image must not be reused before.  The blocks
+ * themselves are unchanged (freeing them is the caller's pool operation).
+ * k_scale / v_scale: given exactly for FP8 caches.  n_blocks == 0 is a
+ * no-op; at most 65535 blocks per call. */
+pkv_status pkv_swap_out(const void* k_cache, const void* v_cache, pkv_dtype cache_dtype, const float* k_scale,
+                        const float* v_scale, int64_t num_blocks, const int32_t* block_ids, int32_t n_blocks,
+                        void* staging, size_t staging_bytes, void* host_image, int32_t n_kv_heads, int32_t d_head,
+                        int32_t block_size, void* stream);
+
+/* Swap in: copies `host_image` (as written by pkv_swap_out for n_blocks
+ * blocks) to `staging`, then writes its i-th block (K, V and FP8 scales) into
+ * device block block_ids[i]; ids outside the pool are skipped.  The listed
+ * blocks may differ from the ones swapped out; the caller points the
+ * sequence's table at them.  Arguments as pkv_swap_out. */
+pkv_status pkv_swap_in(void* k_cache, void* v_cache, pkv_dtype cache_dtype, float* k_scale, float* v_scale,
+                       int64_t num_blocks, const int32_t* block_ids, int32_t n_blocks, void* staging,
+                       size_t staging_bytes, const void* host_image, int32_t n_kv_heads, int32_t d_head,
+                       int32_t block_size, void* stream);
+
 /* Paged decode attention: one query per sequence attends every cached token
  * of its sequence, the current one included ([FP] "The redundancy"; [KVP]
  * Problem 5, "Serving note": decode reads K and V once):

@@ -54,6 +54,11 @@ _SIGS = {
                                           ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _vp], ctypes.c_int),
     "pkv_csr_to_block_table": ([_vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+    "pkv_swap_image_bytes": ([_i32, ctypes.c_int, _i32, _i32, _i32], _sz),
+    "pkv_swap_out": ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, _i32, _vp, _sz, _vp, _i32, _i32, _i32, _vp],
+                     ctypes.c_int),
+    "pkv_swap_in": ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, _i32, _vp, _sz, _vp, _i32, _i32, _i32, _vp],
+                    ctypes.c_int),
     "pkv_pool_create": ([_i64, _vp], ctypes.c_int),
     "pkv_pool_destroy": ([_vp], None),
     "pkv_pool_free_blocks": ([_vp], _i64),
@@ -282,6 +287,39 @@ def copy_blocks(k_cache: torch.Tensor, v_cache: torch.Tensor, src: torch.Tensor,
         raise TypeError("k_cache and v_cache must match")
     _check(load().pkv_copy_blocks(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), nb,
                                   _ptr(src), _ptr(dst), src.numel(), n_kv, d, bs, _stream(stream)))
+
+
+def swap_image_bytes(n_blocks: int, cache_dtype: int, n_kv_heads: int, d_head: int, block_size: int) -> int:
+    return int(load().pkv_swap_image_bytes(n_blocks, cache_dtype, n_kv_heads, d_head, block_size))
+
+
+def _swap_args(k_cache, v_cache, block_ids, staging, host_image, k_scale, v_scale):
+    _need(block_ids, torch.int32, "block_ids")
+    if not host_image.is_pinned():
+        raise ValueError("host_image must be pinned host memory")
+    if not host_image.is_contiguous() or staging.dtype != torch.uint8 or host_image.dtype != torch.uint8:
+        raise TypeError("staging and host_image must be contiguous uint8 tensors")
+    nb, n_kv, bs, d = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache must match")
+    return nb, n_kv, bs, d
+
+
+def swap_out(k_cache, v_cache, block_ids, staging, host_image, *, k_scale=None, v_scale=None, stream=None) -> None:
+    """Pack blocks block_ids into the device staging buffer and copy the image
+    to host_image (a pinned uint8 tensor of swap_image_bytes(...) bytes)."""
+    nb, n_kv, bs, d = _swap_args(k_cache, v_cache, block_ids, staging, host_image, k_scale, v_scale)
+    _check(load().pkv_swap_out(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), nb,
+                               _ptr(block_ids), block_ids.numel(), _ptr(staging), staging.numel(),
+                               host_image.data_ptr(), n_kv, d, bs, _stream(stream)))
+
+
+def swap_in(k_cache, v_cache, block_ids, staging, host_image, *, k_scale=None, v_scale=None, stream=None) -> None:
+    """Copy host_image to the staging buffer and write its blocks into block_ids."""
+    nb, n_kv, bs, d = _swap_args(k_cache, v_cache, block_ids, staging, host_image, k_scale, v_scale)
+    _check(load().pkv_swap_in(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), _ptr(k_scale), _ptr(v_scale), nb,
+                              _ptr(block_ids), block_ids.numel(), _ptr(staging), staging.numel(),
+                              host_image.data_ptr(), n_kv, d, bs, _stream(stream)))
 
 
 def paged_attn_decode_plan(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,

@@ -277,6 +277,38 @@ __global__ __launch_bounds__(256) void csr_to_table_kernel(const int32_t* __rest
   table[(int64_t)s * max_blocks + j] = j < n ? indices[b + j] : -1;
 }
 
+// Swap image of n listed blocks: [K slabs][V slabs][K scales][V scales] (the
+// scale sections for FP8 only), block i of the list at position i of each
+// section.  Pack (to_image = 1) copies listed blocks into the image, unpack
+// the image into listed blocks; a listed id outside the pool is skipped.
+// One thread moves 16 bytes; grid x over a slab's 16-byte pieces, y = list
+// position, z = 0 for K, 1 for V; the first n_kv threads of x-block 0 move
+// the block's scales.
+__global__ __launch_bounds__(256) void swap_kernel(char* __restrict__ k_cache, char* __restrict__ v_cache,
+                                                   float* __restrict__ k_scale, float* __restrict__ v_scale,
+                                                   int64_t num_blocks, const int32_t* __restrict__ ids, int32_t n,
+                                                   char* __restrict__ image, int64_t block_bytes, int32_t n_kv,
+                                                   int32_t to_image) {
+  const int i = blockIdx.y, z = blockIdx.z;
+  const int id = ids[i];
+  if (id < 0 || id >= num_blocks) return;
+  char* const cache = z ? v_cache : k_cache;
+  char* const slab = cache + (int64_t)id * block_bytes;
+  char* const img = image + ((int64_t)z * n + i) * block_bytes;
+  const int64_t piece = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (piece * 16 < block_bytes) {
+    if (to_image) st16(img + piece * 16, ld16(slab + piece * 16));
+    else st16(slab + piece * 16, ld16(img + piece * 16));
+  }
+  if (k_scale && blockIdx.x == 0 && (int)threadIdx.x < n_kv) {
+    float* const sc = (z ? v_scale : k_scale) + (int64_t)id * n_kv + threadIdx.x;
+    float* const isc = reinterpret_cast<float*>(image + 2 * (int64_t)n * block_bytes) + ((int64_t)z * n + i) * n_kv +
+                       threadIdx.x;
+    if (to_image) *isc = *sc;
+    else *sc = *isc;
+  }
+}
+
 hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
                                const int32_t* positions, int32_t n, int32_t block_size, int64_t* out,
                                hipStream_t stream) {
@@ -359,6 +391,17 @@ hipError_t launch_csr_to_table(const int32_t* indptr, const int32_t* indices, in
   if (batch == 0) return hipSuccess;
   const dim3 grid((unsigned)((max_blocks + 255) / 256), (unsigned)batch);
   hipLaunchKernelGGL(csr_to_table_kernel, grid, dim3(256), 0, stream, indptr, indices, max_blocks, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_swap(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                       const int32_t* ids, int32_t n, void* image, int64_t block_bytes, int32_t n_kv, int to_image,
+                       hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t pieces = block_bytes / 16;
+  const dim3 grid((unsigned)((pieces + 255) / 256), (unsigned)n, 2u);
+  hipLaunchKernelGGL(swap_kernel, grid, dim3(256), 0, stream, static_cast<char*>(k_cache), static_cast<char*>(v_cache),
+                     k_scale, v_scale, num_blocks, ids, n, static_cast<char*>(image), block_bytes, n_kv, to_image);
   return hipGetLastError();
 }
 

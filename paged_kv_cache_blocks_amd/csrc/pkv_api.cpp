@@ -317,6 +317,81 @@ pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float
                     "kv_append_fp8 launch");
 }
 
+size_t pkv_swap_image_bytes(int32_t n_blocks, pkv_dtype cache_dtype, int32_t n_kv_heads, int32_t d_head,
+                            int32_t block_size) {
+  if (n_blocks < 0 || n_kv_heads < 1 || d_head < 1 || block_size < 1 || !valid_dtype(cache_dtype)) return 0;
+  const size_t block_bytes = (size_t)n_kv_heads * block_size * d_head * elem_bytes(cache_dtype);
+  const size_t scales = cache_dtype == PKV_FP8_E4M3FN ? (size_t)n_kv_heads * sizeof(float) : 0;
+  return (size_t)n_blocks * 2 * (block_bytes + scales);
+}
+
+}  // extern "C"
+
+namespace {
+
+// checks shared by swap out and swap in
+pkv_status check_swap(const void* k_cache, const void* v_cache, pkv_dtype cache_dtype, const float* k_scale,
+                      const float* v_scale, int64_t num_blocks, const int32_t* block_ids, int32_t n_blocks,
+                      const void* staging, size_t staging_bytes, const void* host_image, int32_t n_kv_heads,
+                      int32_t d_head, int32_t block_size, int64_t* block_bytes) {
+  if (n_blocks < 0) return fail(PKV_ERR_INVALID_ARG, "n_blocks must be >= 0");
+  if (!valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown dtype");
+  if (!k_cache || !v_cache || !block_ids || !staging || !host_image) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (num_blocks < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if ((cache_dtype == PKV_FP8_E4M3FN) != (k_scale != nullptr) || (k_scale != nullptr) != (v_scale != nullptr))
+    return fail(PKV_ERR_INVALID_ARG, "k_scale and v_scale are given exactly for FP8 caches");
+  *block_bytes = (int64_t)n_kv_heads * block_size * d_head * elem_bytes(cache_dtype);
+  if (*block_bytes % 16 != 0) return fail(PKV_ERR_UNSUPPORTED, "a block must be a multiple of 16 bytes");
+  if (n_blocks > 65535) return fail(PKV_ERR_UNSUPPORTED, "at most 65535 blocks per call");
+  if (((uintptr_t)staging) & 15) return fail(PKV_ERR_INVALID_ARG, "staging must be 16-byte aligned");
+  const size_t need = pkv_swap_image_bytes(n_blocks, cache_dtype, n_kv_heads, d_head, block_size);
+  if (staging_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "staging of %zu bytes needed, %zu given", need, staging_bytes);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status pkv_swap_out(const void* k_cache, const void* v_cache, pkv_dtype cache_dtype, const float* k_scale,
+                        const float* v_scale, int64_t num_blocks, const int32_t* block_ids, int32_t n_blocks,
+                        void* staging, size_t staging_bytes, void* host_image, int32_t n_kv_heads, int32_t d_head,
+                        int32_t block_size, void* stream) {
+  if (n_blocks == 0) return ok();
+  int64_t block_bytes = 0;
+  pkv_status st = check_swap(k_cache, v_cache, cache_dtype, k_scale, v_scale, num_blocks, block_ids, n_blocks,
+                             staging, staging_bytes, host_image, n_kv_heads, d_head, block_size, &block_bytes);
+  if (st != PKV_OK) return st;
+  const size_t bytes = pkv_swap_image_bytes(n_blocks, cache_dtype, n_kv_heads, d_head, block_size);
+  st = hip_status(pkv::launch_swap(const_cast<void*>(k_cache), const_cast<void*>(v_cache), const_cast<float*>(k_scale),
+                                   const_cast<float*>(v_scale), num_blocks, block_ids, n_blocks, staging, block_bytes,
+                                   n_kv_heads, 1, (hipStream_t)stream),
+                  "swap pack launch");
+  if (st != PKV_OK) return st;
+  return hip_status(hipMemcpyAsync(host_image, staging, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream),
+                    "swap copy to host");
+}
+
+pkv_status pkv_swap_in(void* k_cache, void* v_cache, pkv_dtype cache_dtype, float* k_scale, float* v_scale,
+                       int64_t num_blocks, const int32_t* block_ids, int32_t n_blocks, void* staging,
+                       size_t staging_bytes, const void* host_image, int32_t n_kv_heads, int32_t d_head,
+                       int32_t block_size, void* stream) {
+  if (n_blocks == 0) return ok();
+  int64_t block_bytes = 0;
+  pkv_status st = check_swap(k_cache, v_cache, cache_dtype, k_scale, v_scale, num_blocks, block_ids, n_blocks,
+                             staging, staging_bytes, host_image, n_kv_heads, d_head, block_size, &block_bytes);
+  if (st != PKV_OK) return st;
+  const size_t bytes = pkv_swap_image_bytes(n_blocks, cache_dtype, n_kv_heads, d_head, block_size);
+  st = hip_status(hipMemcpyAsync(staging, host_image, bytes, hipMemcpyHostToDevice, (hipStream_t)stream),
+                  "swap copy to device");
+  if (st != PKV_OK) return st;
+  return hip_status(pkv::launch_swap(k_cache, v_cache, k_scale, v_scale, num_blocks, block_ids, n_blocks, staging,
+                                     block_bytes, n_kv_heads, 0, (hipStream_t)stream),
+                    "swap unpack launch");
+}
+
 pkv_status pkv_csr_to_block_table(const int32_t* kv_indptr, const int32_t* kv_indices, int32_t batch,
                                   int32_t max_blocks_per_seq, int32_t* block_table_out, void* stream) {
   if (batch < 0) return fail(PKV_ERR_INVALID_ARG, "batch must be >= 0");

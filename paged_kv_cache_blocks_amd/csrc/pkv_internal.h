@@ -75,6 +75,9 @@ hipError_t launch_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, fl
                                  const int32_t* cu_new, int32_t batch, int32_t max_new, const void* k_new,
                                  const void* v_new, int32_t new_bytes, int32_t n_kv, int32_t d, int32_t log2_bs,
                                  hipStream_t stream);
+hipError_t launch_swap(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
+                       const int32_t* ids, int32_t n, void* image, int64_t block_bytes, int32_t n_kv, int to_image,
+                       hipStream_t stream);
 hipError_t launch_csr_to_table(const int32_t* indptr, const int32_t* indices, int32_t batch, int32_t max_blocks,
                                int32_t* table, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,

@@ -115,6 +115,29 @@ def test_csr_entry_points_validate(pkv):
     assert lib.pkv_csr_to_block_table(0x1000, 0x1000, 2, 0, 0x2000, None) == pkv.ERR_INVALID_ARG
 
 
+def test_swap_entry_points_validate(pkv):
+    lib = pkv.load()
+    # image: 2 x (n_kv x B x d x bytes) per block, plus 2 x n_kv fp32 scales for FP8
+    assert lib.pkv_swap_image_bytes(3, pkv.BF16, 8, 128, 16) == 3 * 2 * 8 * 16 * 128 * 2
+    assert lib.pkv_swap_image_bytes(3, pkv.FP8_E4M3FN, 8, 128, 16) == 3 * 2 * (8 * 16 * 128 + 8 * 4)
+    assert lib.pkv_swap_image_bytes(-1, pkv.BF16, 8, 128, 16) == 0
+    need = lib.pkv_swap_image_bytes(4, pkv.BF16, 2, 64, 16)
+    base = [0x1000, 0x2000, pkv.BF16, None, None, 64, 0x3000, 4, 0x4000, need, 0x5000, 2, 64, 16, None]
+    for f in (lib.pkv_swap_out, lib.pkv_swap_in):
+        a = list(base); a[7] = 0
+        assert f(*a) == pkv.OK                          # nothing to move
+        a = list(base); a[9] = need - 1
+        assert f(*a) == pkv.ERR_WORKSPACE               # staging too small
+        a = list(base); a[2] = pkv.FP8_E4M3FN
+        assert f(*a) == pkv.ERR_INVALID_ARG             # fp8 without scales
+        a = list(base); a[8] = 0x4008
+        assert f(*a) == pkv.ERR_INVALID_ARG             # misaligned staging
+        a = list(base); a[10] = None
+        assert f(*a) == pkv.ERR_INVALID_ARG             # no host image
+        a = list(base); a[7] = 70000
+        assert f(*a) == pkv.ERR_UNSUPPORTED
+
+
 def test_decode_workspace_sizes(pkv):
     # partition mode: one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
     assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 4, 16, pkv.BF16, 256) == 0
