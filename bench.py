@@ -4,11 +4,13 @@
 
 A step is one pass of the whole hot path over one batch, on inputs already
 resident in HBM:
-  * decode workloads: slot indexing for the batch's current token, kv_append
-    of that token's K/V rows into every layer's cache, then paged decode
-    attention of every layer, back to back (each layer's append precedes its
-    attention; with no model between the layers the two orders do the same
-    work, and back-to-back calls keep launch gaps out of the decode timing);
+  * decode workloads: slot indexing for the batch's current token, the
+    step's work order (the batch ranked by length once, shared by every
+    layer), kv_append of that token's K/V rows into every layer's cache, then
+    paged decode attention of every layer, back to back (each layer's append
+    precedes its attention; with no model between the layers the two orders do
+    the same work, and back-to-back calls keep launch gaps out of the decode
+    timing);
   * prefill workload: slot indexing of the chunk, kv_append of its 8,192
     new rows, chunked-prefill attention.
 With --fp8-append quantize the FP8 workload's append takes the token's rows
@@ -179,6 +181,7 @@ class DecodeWorkload:
         self.positions = (self.seq_lens_t - 1).to(torch.int32)
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
         self.cu_new = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
+        self.order = torch.arange(self.batch, dtype=torch.int32, device=dev)
         self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
                     for _ in range(self.layers)]
         ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, B,
@@ -205,13 +208,18 @@ class DecodeWorkload:
             return
         self.pkv.paged_attn_decode(self.q[layer], self.k[layer], self.v[layer], self.block_table, self.seq_lens_t,
                                    self.n_q, self.n_kv, self.d, self.bs, self.scale, k_scale=self.ks[layer],
-                                   v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws)
+                                   v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws,
+                                   work_order=self.order)
 
     calls_per_event = property(lambda self: self.layers)
 
     def step(self, events=None):
         pkv = self.pkv
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
+        if not self.csr:
+            # one work order per step, shared by every layer's decode (same batch, same lengths)
+            pkv.paged_attn_decode_order(self.seq_lens_t, self.n_q, self.n_kv, self.d, self.max_blocks, self.bs,
+                                        pkv.dtype_code(self.k[0]), out=self.order)
         for layer in range(self.layers):
             if self.quantize_append:
                 pkv.kv_append_fp8(self.k[layer], self.v[layer], self.ks[layer], self.vs[layer], self.block_table,

@@ -332,6 +332,35 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
                                       int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype,
                                       int32_t partition_tokens, int32_t* info);
 
+/* Work order for the decode calls of one step (every layer decodes the same
+ * batch): ranks the sequences by length (longer first, ties by index) and
+ * writes work_order_out (device int32 [batch]), the permutation
+ * pkv_paged_attn_decode_ordered takes.  When every split workgroup of the call
+ * is resident at once (workgroups i and i + half the grid share a CU) the k-th
+ * longest sequence is paired with the k-th shortest; otherwise the longest
+ * come first, so the short ones fill the end.  Balancing is this library's
+ * addition to the pages' split of a sequence across thread blocks ([KVP]
+ * Problem 5, serving note).  Arguments as pkv_paged_attn_decode_plan; one
+ * launch of about batch^2 length comparisons, meant to run once per step. */
+pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t d_head, int32_t max_blocks_per_seq, int32_t block_size,
+                                       pkv_dtype kv_dtype, int32_t* work_order_out, void* stream);
+
+/* Decode as pkv_paged_attn_decode (the library's split) with the sequence
+ * slots of the split grid taken in work_order (device int32 [batch], a
+ * permutation of 0 .. batch - 1; entries are clamped into range, so anything
+ * else computes some sequences twice and leaves others unwritten).  Every
+ * (sequence, head, partition) is computed the same way whichever workgroup
+ * takes it, so the output is bit-identical to pkv_paged_attn_decode's for any
+ * permutation.  The work-queue split ignores the order. */
+pkv_status pkv_paged_attn_decode_ordered(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                         const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                         int32_t block_size, float scale, const int32_t* work_order,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- CSR page tables ([MEM] "Method 3: PagedAttention", "Walking the
  * table"): request s owns pages kv_indices[kv_indptr[s] .. kv_indptr[s+1]),
  * its token p sits in page kv_indices[kv_indptr[s] + p / B] at offset p % B.

@@ -42,6 +42,10 @@ _SIGS = {
     "pkv_paged_attn_decode_partitioned": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                            _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp],
                                           ctypes.c_int),
+    "pkv_paged_attn_decode_ordered": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                       _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp],
+                                      ctypes.c_int),
+    "pkv_paged_attn_decode_order": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32], _sz),
     "pkv_paged_attn_decode_plan": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_chunk": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
@@ -341,8 +345,9 @@ def paged_attn_decode_workspace(batch, n_q_heads, n_kv_heads, d_head, max_blocks
 
 def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_kv_heads, d_head, block_size, scale,
                       *, k_scale=None, v_scale=None, out=None, out_dtype=torch.float32, workspace=None,
-                      partition_tokens: int = 0, stream=None) -> torch.Tensor:
-    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the seq_lens[s] cached tokens of sequence s."""
+                      partition_tokens: int = 0, work_order=None, stream=None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the seq_lens[s] cached tokens of sequence s.
+    work_order (from paged_attn_decode_order) only changes which workgroup takes which sequence."""
     batch = q.shape[0]
     nb = k_cache.shape[0]
     _need(block_table, torch.int32, "block_table")
@@ -355,10 +360,32 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
         workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=q.device)  # the item counter starts at 0
     ws_ptr = _ptr(workspace) if workspace is not None else None
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if work_order is not None:
+        _need(work_order, torch.int32, "work_order")
+        if partition_tokens != 0 or work_order.numel() != batch:
+            raise ValueError("work_order takes the library's split and one entry per sequence")
+        _check(load().pkv_paged_attn_decode_ordered(
+            _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+            _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb,
+            n_q_heads, n_kv_heads, d_head, block_size, float(scale), _ptr(work_order), ws_ptr, ws_n, _stream(stream)))
+        return out
     _check(load().pkv_paged_attn_decode_partitioned(
         _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb, n_q_heads,
         n_kv_heads, d_head, block_size, float(scale), int(partition_tokens), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_order(seq_lens, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
+                            kv_dtype: int = BF16, out=None, stream=None) -> torch.Tensor:
+    """Work order (int32 permutation of the batch) for the decode calls of one step."""
+    _need(seq_lens, torch.int32, "seq_lens")
+    batch = seq_lens.numel()
+    if out is None:
+        out = torch.empty(batch, dtype=torch.int32, device=seq_lens.device)
+    _check(load().pkv_paged_attn_decode_order(_ptr(seq_lens), batch, n_q_heads, n_kv_heads, d_head,
+                                              int(max_blocks_per_seq), block_size, kv_dtype, _ptr(out),
+                                              _stream(stream)))
     return out
 
 

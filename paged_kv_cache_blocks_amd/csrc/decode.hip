@@ -547,7 +547,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int w = threadIdx.x / kWave;
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
-  const int s = (blockIdx.x / hk) % a.batch;
+  int s = (blockIdx.x / hk) % a.batch;  // sequence slot -> sequence (the caller's work order, if any)
+  if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
   const int part = blockIdx.x / (hk * a.batch);
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
@@ -1067,6 +1068,33 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t st
   if (kv_kind == KIND_F32) return d == 64 ? launch_gw<KIND_F32, 64>(a, stream) : launch_gw<KIND_F32, 128>(a, stream);
   if (kv_kind == KIND_BF16) return d == 64 ? launch_gw<KIND_BF16, 64>(a, stream) : launch_gw<KIND_BF16, 128>(a, stream);
   return d == 64 ? launch_gw<KIND_FP8, 64>(a, stream) : launch_gw<KIND_FP8, 128>(a, stream);
+}
+
+// Work order of a batch: thread t ranks sequence t by length against every
+// other (longer first, ties by index; the loads of the whole length array are
+// shared by the wave), then writes t into the slot of its rank.
+__global__ __launch_bounds__(256) void decode_order_kernel(const int32_t* __restrict__ seq_lens, int32_t batch,
+                                                           int32_t pair, int32_t* __restrict__ order) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= batch) return;
+  const int lt = max(seq_lens[t], 0);
+  int r = 0;
+#pragma unroll 8
+  for (int u = 0; u < batch; ++u) {
+    const int lu = max(seq_lens[u], 0);
+    r += (lu > lt) | ((lu == lt) & (u < t));
+  }
+  const int half = (batch + 1) / 2;
+  const int slot = (!pair || r < half) ? r : half + (batch - 1 - r);
+  order[slot] = t;
+}
+
+hipError_t launch_decode_order(const int32_t* seq_lens, int32_t batch, int32_t pair, int32_t* order,
+                               hipStream_t stream) {
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_order_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream, seq_lens, batch,
+                     pair, order);
+  return hipGetLastError();
 }
 
 }  // namespace pkv

@@ -81,7 +81,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
-  const int s = (blockIdx.x / hk) % a.batch;
+  // sequence slot -> sequence: the batch order, or the caller's work order
+  // (pkv_paged_attn_decode_order: long sequences paired with short ones on a
+  // CU, or the longest first); results do not depend on it
+  int s = (blockIdx.x / hk) % a.batch;
+  if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
   const int part = blockIdx.x / (hk * a.batch);
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;

@@ -474,7 +474,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
                        const int32_t* block_table, const int32_t* indptr, int32_t max_blocks_per_seq,
                        const int32_t* seq_lens, int32_t batch, int64_t num_blocks, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale, int32_t partition_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       const int32_t* work_order, void* workspace, size_t workspace_bytes, void* stream) {
   // head ratio first, before anything else (validate before mutate)
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
   if (st != PKV_OK) return st;
@@ -538,6 +538,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
   a.group = group;
   a.head_chunks = plan.head_chunks;
   a.use_mfma = plan.use_mfma;
+  a.work_order = work_order;
   a.part_tokens = plan.part_tokens;
   a.n_parts = plan.n_parts;
   a.out_bf16 = out_dtype == PKV_BF16;
@@ -559,7 +560,45 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
                                              void* workspace, size_t workspace_bytes, void* stream) {
   return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr,
                      max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size,
-                     scale, partition_tokens, workspace, workspace_bytes, stream);
+                     scale, partition_tokens, nullptr, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attn_decode_ordered(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                         const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                         int32_t block_size, float scale, const int32_t* work_order,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!work_order) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr,
+                     max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size,
+                     scale, 0, work_order, workspace, workspace_bytes, stream);
+}
+
+pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                       int32_t d_head, int32_t max_blocks_per_seq, int32_t block_size,
+                                       pkv_dtype kv_dtype, int32_t* work_order_out, void* stream) {
+  if (!seq_lens || !work_order_out) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  DecodePlan plan;
+  pkv_status st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype, 0,
+                              &plan);
+  if (st != PKV_OK) return st;
+  // All split workgroups resident at once: workgroups i and i + half the grid
+  // share a CU, so pair the k-th longest sequence with the k-th shortest.
+  // Otherwise workgroups start as others finish: the longest first.
+  int pair = 0;
+  if (!plan.n_wg) {
+    const int cus = device_cus();
+    if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
+    const int gw = (n_q_heads / n_kv_heads) / plan.head_chunks;
+    const int per_cu = plan.use_mfma ? pkv::decode_mfma_wgs_per_cu(kv_dtype, gw)
+                                     : partition_wgs_per_cu(kv_dtype, d_head, gw);
+    const int64_t wgs = (int64_t)batch * n_kv_heads * plan.head_chunks * plan.n_parts;
+    pair = wgs <= (int64_t)cus * per_cu ? 1 : 0;
+  }
+  return hip_status(pkv::launch_decode_order(seq_lens, batch, pair, work_order_out, (hipStream_t)stream),
+                    "decode order launch");
 }
 
 pkv_status pkv_paged_attn_decode_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
@@ -572,7 +611,7 @@ pkv_status pkv_paged_attn_decode_csr(void* out, pkv_dtype out_dtype, const void*
   if (!kv_indptr) return fail(PKV_ERR_INVALID_ARG, "null pointer");
   return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, kv_indices, kv_indptr,
                      max_pages_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size, scale,
-                     0, workspace, workspace_bytes, stream);
+                     0, nullptr, workspace, workspace_bytes, stream);
 }
 
 pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,

@@ -40,6 +40,7 @@ struct DecodeArgs {
   int32_t n_parts;
   int32_t out_bf16;
   int32_t use_mfma;     // partition mode: the matrix-core split kernel (decode_mfma.hip)
+  const int32_t* work_order;  // partition mode: sequence slot -> sequence (a permutation), or null
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -52,6 +53,11 @@ int decode_queue_items_per_wg();           // items the queue kernel aims for pe
 int decode_queue_max_item_blocks();      // largest item the queue kernel makes
 int decode_queue_wgs_per_cu(int kv_kind, int d, int heads_per_wg, int batch);
 hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t stream);
+// order[slot] = sequence: sequences ranked by length (longer first, ties by
+// index); pair != 0 puts the k-th longest and the k-th shortest in slots s
+// and s + ceil(batch / 2)
+hipError_t launch_decode_order(const int32_t* seq_lens, int32_t batch, int32_t pair, int32_t* order,
+                               hipStream_t stream);
 // matrix-core decode (partition mode only): bf16 / fp8 KV, d = 128, 4, 8 or 16 heads per workgroup
 bool decode_mfma_supported(int kv_kind, int d, int heads_per_wg);
 int decode_mfma_wgs_per_cu(int kv_kind, int heads_per_wg);

@@ -138,6 +138,16 @@ def test_swap_entry_points_validate(pkv):
         assert f(*a) == pkv.ERR_UNSUPPORTED
 
 
+def test_work_order_entry_points_validate(pkv):
+    lib = pkv.load()
+    assert lib.pkv_paged_attn_decode_order(None, 4, 8, 2, 128, 8, 16, pkv.BF16, 0x1000, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_paged_attn_decode_order(0x1000, 4, 6, 4, 128, 8, 16, pkv.BF16, 0x2000, None) == pkv.ERR_INVALID_ARG
+    assert lib.pkv_paged_attn_decode_order(0x1000, 4, 8, 2, 96, 8, 16, pkv.BF16, 0x2000, None) == pkv.ERR_UNSUPPORTED
+    args = [0x1000, 0, 0x2000, 1, 0x3000, 0x4000, 1, None, None, 0x5000, 8, 0x6000, 2, 64, 8, 2, 128, 16, 0.088,
+            None, None, 0, None]
+    assert lib.pkv_paged_attn_decode_ordered(*args) == pkv.ERR_INVALID_ARG   # no order
+
+
 def test_decode_workspace_sizes(pkv):
     # partition mode: one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
     assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 4, 16, pkv.BF16, 256) == 0

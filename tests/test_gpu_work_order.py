@@ -1,0 +1,58 @@
+"""GPU checks of the decode work order: pkv_paged_attn_decode_order writes the
+length ranking (pairing long with short, or longest first), and decode with
+any permutation as work order gives bit-identical outputs to plain decode."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_util import dev, note, oracle_decode, upload_decode, TOL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkv():
+    import paged_kv_cache_blocks_amd as p
+    assert torch.cuda.is_available()
+    return p
+
+
+def _expected(lens):
+    n = len(lens)
+    desc = sorted(range(n), key=lambda t: (-max(int(lens[t]), 0), t))
+    half = (n + 1) // 2
+    pair = [desc[q] if q < half else desc[n - 1 - (q - half)] for q in range(n)]
+    return desc, pair
+
+
+@pytest.mark.parametrize("batch", [1, 2, 7, 64, 256, 1000])
+def test_order_is_the_length_ranking(pkv, batch):
+    r = np.random.default_rng(970 + batch)
+    lens = r.integers(0, 3000, size=batch).astype(np.int32)
+    lens[::5] = lens[0]  # ties
+    note(f"decode order batch={batch}")
+    got = pkv.paged_attn_decode_order(dev(lens), 32, 8, 128, 3000 // 16 + 1, 16, pkv.BF16).cpu().tolist()
+    desc, pair = _expected(lens)
+    assert got == desc or got == pair
+
+
+@pytest.mark.parametrize("kind,d,n_q,n_kv", [("bf16", 128, 32, 8), ("fp8", 128, 64, 8), ("f32", 64, 8, 2)])
+def test_ordered_decode_is_bit_identical(pkv, kind, d, n_q, n_kv):
+    lens = [1, 5000, 17, 300, 9000, 2048, 0, 777, 4097, 64]
+    c = synth.make_decode_case(config=971, layer=0, n_q=n_q, n_kv=n_kv, d=d, seq_lens=lens, kv_dtype=kind)
+    t = upload_decode(c)
+    def run(order=None):
+        out = pkv.paged_attn_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"], n_q, n_kv, d,
+                                    16, c.scale, k_scale=t["k_scale"], v_scale=t["v_scale"], work_order=order)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+    note(f"ordered decode {kind}")
+    plain = run()
+    lib_order = pkv.paged_attn_decode_order(t["seq_lens"], n_q, n_kv, d, c.block_table.shape[1], 16,
+                                            pkv.dtype_code(t["k_cache"]))
+    rand = torch.from_numpy(np.random.default_rng(5).permutation(len(lens)).astype(np.int32)).cuda()
+    for o in (lib_order, rand):
+        assert np.array_equal(run(o).view(np.uint32), plain.view(np.uint32))
+    want = oracle_decode(c)
+    assert np.allclose(plain.astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
