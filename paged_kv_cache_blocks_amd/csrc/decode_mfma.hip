@@ -99,7 +99,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int n_my = n_chunks > w ? (n_chunks - w + kW - 1) / kW : 0;
 
   // Where this wave's tiles live: lane i holds tile (i & 1) of the wave's
-  // chunk i >> 1 (partition chunk w + 4 (i >> 1)) as the cache row index of
+  // chunk i >> 1 (partition chunk w + 4 (i >> 1)), so a partition has at most
+  // 4 x 32 chunks of 32 tokens (the host caps it at 4096), as the cache row index of
   // each half's first row; fp8 scales of each half's block ride along.  A
   // tile past the partition keeps row 0: it is loaded all the same, so the
   // loads need no branch, and its rows, being past the end, are masked (K)

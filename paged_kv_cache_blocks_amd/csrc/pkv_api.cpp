@@ -49,6 +49,8 @@ int elem_bytes(pkv_dtype t) {
 
 bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3FN; }
 
+// Longest partition: the matrix-core kernel keeps the row indices of a
+// partition's tiles in its waves' lanes (4 waves x 32 chunks x 32 tokens).
 constexpr int kMaxPartition = 4096;
 
 // log2 of a supported block size (8, 16, 32, 64, 128, 256), else -1
@@ -149,9 +151,18 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
   plan->use_mfma = 0;
   int32_t part = partition_tokens;
   if (part == 0 && mfma) {
-    // fewest equal partitions of at most kMaxPartition tokens; the matrix-core
-    // kernel has no work-queue form, so this holds whatever the residency
-    const int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
+    // Fewest equal partitions of at most kMaxPartition tokens, but at least
+    // enough that every resident workgroup slot gets a workgroup (a single
+    // long sequence otherwise left most CUs idle).  The matrix-core kernel
+    // has no work-queue form.  Without a device the fill rule is skipped
+    // (sizes only).
+    int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
+    const int cus = device_cus();
+    if (cus > 0) {
+      const int64_t resident = (int64_t)cus * pkv::decode_mfma_wgs_per_cu(kv_dtype, gw);
+      const int64_t pairs = (int64_t)batch * hk;
+      n_parts = std::max<int64_t>(n_parts, std::min<int64_t>((resident + pairs - 1) / pairs, (max_tokens + 255) / 256));
+    }
     part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + 255) / 256 * 256);
   } else if (part == 0) {
     // Library's choice.  Cut each (sequence, KV head chunk) into the fewest

@@ -52,7 +52,30 @@ def test_ordered_decode_is_bit_identical(pkv, kind, d, n_q, n_kv):
     lib_order = pkv.paged_attn_decode_order(t["seq_lens"], n_q, n_kv, d, c.block_table.shape[1], 16,
                                             pkv.dtype_code(t["k_cache"]))
     rand = torch.from_numpy(np.random.default_rng(5).permutation(len(lens)).astype(np.int32)).cuda()
-    for o in (lib_order, rand):
-        assert np.array_equal(run(o).view(np.uint32), plain.view(np.uint32))
+    ident = torch.arange(len(lens), dtype=torch.int32, device="cuda")
+    ordered = run(lib_order)
+    # the order only moves work between workgroups: the same bits for every permutation
+    for o in (rand, ident):
+        assert np.array_equal(run(o).view(np.uint32), ordered.view(np.uint32))
     want = oracle_decode(c)
-    assert np.allclose(plain.astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
+    assert np.array_equal(plain.view(np.uint32), ordered.view(np.uint32))  # same split, same bits
+    for got in (plain, ordered):
+        assert np.allclose(got.astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_single_long_sequence_fills_the_device(pkv, kind):
+    """One 20000-token sequence: the split spreads it over every resident
+    workgroup slot (not just a few 4096-token partitions) and still matches
+    the oracle."""
+    c = synth.make_decode_case(config=972, layer=0, n_q=32, n_kv=8, d=128, seq_lens=[20000], kv_dtype=kind)
+    plan = pkv.paged_attn_decode_plan(1, 32, 8, 128, c.block_table.shape[1], 16, pkv.BF16 if kind == "bf16"
+                                      else pkv.FP8_E4M3FN)
+    note(f"single long sequence {kind}: {plan}")
+    assert plan["workgroups"] >= 256 and plan["n_parts"] > 5
+    t = upload_decode(c)
+    out = pkv.paged_attn_decode(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seq_lens"], 32, 8, 128, 16,
+                                c.scale, k_scale=t["k_scale"], v_scale=t["v_scale"])
+    torch.cuda.synchronize()
+    want = oracle_decode(c)
+    assert np.allclose(out.cpu().numpy().astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
