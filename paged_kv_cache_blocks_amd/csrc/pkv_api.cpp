@@ -163,7 +163,8 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
       const int64_t pairs = (int64_t)batch * hk;
       n_parts = std::max<int64_t>(n_parts, std::min<int64_t>((resident + pairs - 1) / pairs, (max_tokens + 255) / 256));
     }
-    part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + 255) / 256 * 256);
+    // partitions in whole 32-token chunks, the matrix-core kernel's unit
+    part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + 31) / 32 * 32);
   } else if (part == 0) {
     // Library's choice.  Cut each (sequence, KV head chunk) into the fewest
     // equal partitions of at most kMaxPartition tokens; if all of those
