@@ -195,8 +195,9 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, const BlockIds&
 #pragma unroll
     for (int i = 0; i < Gm::NLK; ++i) {
       const int64_t off = (i < LH ? half0 : half1) + (int64_t)((i % LH) * kWave + lane) * Gm::LW;
-      r.bk[b][i] = *reinterpret_cast<const LV*>(kc + off);
-      r.bv[b][i] = *reinterpret_cast<const LV*>(vc + off);
+      // read once: non-temporal loads (see ld16_stream)
+      r.bk[b][i] = __builtin_nontemporal_load(reinterpret_cast<const LV*>(kc + off));
+      r.bv[b][i] = __builtin_nontemporal_load(reinterpret_cast<const LV*>(vc + off));
     }
   }
 }

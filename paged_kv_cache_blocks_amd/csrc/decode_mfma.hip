@@ -18,8 +18,8 @@
 // at the end through LDS.  Each tile is two 8-token halves, each inside one
 // cache block whatever the block size (8 .. 256) and table format.  Per chunk
 // a wave:
-//   loads the K and V rows of its two tiles with coalesced 16-byte loads
-//   (issued one chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
+//   loads the K and V rows of its two tiles with coalesced, non-temporal
+//   16-byte loads (issued one chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
 //   its own LDS region in the swizzled row layout (V rows past the end of the
 //   sequence are written as zeros: their zero weights must not meet a NaN);
 //   S^T = K q^T: 2 token tiles x 4 d steps, K fragments from LDS, q^T in
@@ -155,8 +155,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       for (int i = 0; i < SL::loads; ++i) {
         constexpr int LH = SL::loads / 2;  // loads per half
         const int64_t off = (i < LH ? half0 : half1) + ((i % LH) * kWave + lane) * 16;
-        bk[b][i] = ld16(kc + off);
-        bv[b][i] = ld16(vc + off);
+        bk[b][i] = ld16_stream(kc + off);
+        bv[b][i] = ld16_stream(vc + off);
       }
     }
   };
