@@ -20,10 +20,13 @@ ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 # Packed FP32 instructions are kept out of the generated code on purpose.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wno-unused-function"]
-# The prefill kernel keeps its MFMA accumulators in ordinary VGPRs: it needs
-# fewer than 256 registers that way, which leaves room for two waves per SIMD,
-# and the softmax reads the score tiles without accumulator-register copies.
-EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# The prefill and matrix-core decode kernels keep their MFMA accumulators in
+# ordinary VGPRs: they need fewer than 256 registers that way, which leaves
+# room for two waves per SIMD, and the softmax and the output rescale read the
+# tiles without accumulator-register copies (about 100 copy instructions per
+# 32-token decode chunk otherwise).
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc():

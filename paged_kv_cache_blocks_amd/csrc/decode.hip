@@ -587,17 +587,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 }
 
 // Merge the partitions of one (sequence, query head): the rescale rule of the
-// online softmax applied to whole partitions.  One wave per (sequence, head):
-// lane j takes partition j of each group of 64 for the max and the weights,
-// and every lane accumulates its output columns over the partitions with each
-// weight broadcast from its lane.
+// online softmax applied to whole partitions.  One wave per (sequence, head),
+// up to kCombineHeads heads of one sequence per workgroup (a sequence with a
+// single partition costs one small workgroup, not one per head): lane j takes
+// partition j of each group of 64 for the max and the weights, and every lane
+// accumulates its output columns over the partitions with each weight
+// broadcast from its lane.
+constexpr int kCombineHeads = 16;
 template <int D>
-__global__ __launch_bounds__(64) void combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave * kCombineHeads) void combine_kernel(DecodeArgs a) {
   constexpr int COLS = D / kWave;
-  const int hq = blockIdx.x, s = blockIdx.y, lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
+  const int hq = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int s = blockIdx.y;
   const int L = clamp_len(a, s);
   const int nv = (L + a.part_tokens - 1) / a.part_tokens;
-  if (nv == 1) return;  // the split kernel wrote this sequence's output itself
+  if (nv == 1 || hq >= a.n_q) return;  // one partition: the split kernel wrote this sequence's output itself
   const int64_t base = ((int64_t)s * a.n_q + hq) * a.n_parts;
   const float* ml = a.ws_ml + base * 2;
   const float* op = a.ws_o + base * D;
@@ -1051,7 +1056,9 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
     e = hipGetLastError();
   }
   if (e != hipSuccess || a.n_parts == 1) return e;
-  hipLaunchKernelGGL((combine_kernel<D>), dim3(a.n_q, a.batch), dim3(64), 0, stream, a);
+  const int heads = a.n_q < kCombineHeads ? a.n_q : kCombineHeads;
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((a.n_q + heads - 1) / heads, a.batch), dim3(kWave * heads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

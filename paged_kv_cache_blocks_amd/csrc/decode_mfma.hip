@@ -146,28 +146,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
 
   u32x4 bk[2][SL::loads], bv[2][SL::loads];
+  // Loads take a scalar base (the half's first row, read from its lane) plus
+  // this lane's 32-bit offset, so the per-load address work is scalar.
+  const uint32_t lane_off = (uint32_t)lane * 16;
   auto issue = [&](int c) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int64_t half0 = (int64_t)__builtin_amdgcn_readlane(my_row[0], 2 * c + b) * SL::row_bytes;
-      const int64_t half1 = (int64_t)__builtin_amdgcn_readlane(my_row[1], 2 * c + b) * SL::row_bytes;
+      const uint64_t half0 = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_row[0], 2 * c + b) * SL::row_bytes;
+      const uint64_t half1 = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(my_row[1], 2 * c + b) * SL::row_bytes;
 #pragma unroll
       for (int i = 0; i < SL::loads; ++i) {
         constexpr int LH = SL::loads / 2;  // loads per half
-        const int64_t off = (i < LH ? half0 : half1) + ((i % LH) * kWave + lane) * 16;
-        bk[b][i] = ld16_stream(kc + off);
-        bv[b][i] = ld16_stream(vc + off);
+        const uint64_t h = i < LH ? half0 : half1;
+        const uint32_t off = (uint32_t)((i % LH) * kWave * 16) + lane_off;
+        bk[b][i] = ld16_stream(kc + h + off);
+        bv[b][i] = ld16_stream(vc + h + off);
       }
     }
   };
 
-  const float sl = a.scale_log2;
-  if (n_my > 0) issue(0);
-  for (int c = 0; c < n_my; ++c) {
-    const int t0 = (w + kW * c) * kCT;  // first token of the chunk (partition-relative)
-
-    // ---- stage K and V of the chunk into LDS (bf16 rows, swizzled) ----
-    wave_lds_sync();  // this wave's reads of the previous chunk are done
+  // Stage the chunk's K and V rows into LDS (bf16 rows, swizzled).  Only a
+  // chunk that runs past the partition's end (TAIL) writes its V rows there
+  // as zeros; the others store every row as loaded.
+  auto stage = [&](int t0, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -175,13 +177,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         if constexpr (KIND == KIND_BF16) {
           const int r = kB * b + 4 * i + (lane >> 4);  // chunk row
           const int pc = lane & 15;
-          const bool live = t0 + r < plen;
+          const bool live = !TAIL || t0 + r < plen;
           st16(k_lds + swz(r, pc), bk[b][i]);
           st16(v_lds + swz(r, pc), live ? bv[b][i] : u32x4{0, 0, 0, 0});
         } else {
           const int r = kB * b + 8 * i + (lane >> 3);
           const int p8 = lane & 7;
-          const bool live = t0 + r < plen;
+          const bool live = !TAIL || t0 + r < plen;
           uint32_t kb[8], vb[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -195,6 +197,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         }
       }
     }
+  };
+
+  const float sl = a.scale_log2;
+  if (n_my > 0) issue(0);
+  for (int c = 0; c < n_my; ++c) {
+    const int t0 = (w + kW * c) * kCT;  // first token of the chunk (partition-relative)
+    const bool tail = t0 + kCT > plen;  // wave-uniform: only a partition's last chunk
+
+    wave_lds_sync();  // this wave's reads of the previous chunk are done
+    if (tail) stage(t0, std::true_type{});
+    else stage(t0, std::false_type{});
     // the registers are free again: fetch the next chunk while this one computes
     if (c + 1 < n_my) issue(c + 1);
     wave_lds_sync();
@@ -211,22 +224,27 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // ---- online softmax for head column n over tokens t0 + 16 t + 4 g + j ----
     float sc[2][4];
     float mx = -INFINITY;
+    auto scores = [&](auto tail_tag) {
+      constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      // this lane's tokens 4 g .. 4 g + 3 of tile t lie in half g / 2
-      float kscale = 1.f;
-      if constexpr (KIND == KIND_FP8) {
-        const float k0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[0]), 2 * c + t));
-        const float k1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[1]), 2 * c + t));
-        kscale = g < 2 ? k0 : k1;
-      }
+      for (int t = 0; t < 2; ++t) {
+        // this lane's tokens 4 g .. 4 g + 3 of tile t lie in half g / 2
+        float kscale = 1.f;
+        if constexpr (KIND == KIND_FP8) {
+          const float k0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[0]), 2 * c + t));
+          const float k1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_ks[1]), 2 * c + t));
+          kscale = g < 2 ? k0 : k1;
+        }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = t0 + 16 * t + 4 * g + j;
-        sc[t][j] = tok < plen ? st[t][j] * (sl * kscale) : -INFINITY;
-        mx = fmaxf(mx, sc[t][j]);
+        for (int j = 0; j < 4; ++j) {
+          const int tok = t0 + 16 * t + 4 * g + j;
+          sc[t][j] = (!TAIL || tok < plen) ? st[t][j] * (sl * kscale) : -INFINITY;
+          mx = fmaxf(mx, sc[t][j]);
+        }
       }
-    }
+    };
+    if (tail) scores(std::true_type{});
+    else scores(std::false_type{});
     mx = max_xor32(max_xor16(mx));
     const float m_new = (mx > m_run + kSlack) ? mx : m_run;  // m_run = -inf takes mx
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
