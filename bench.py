@@ -18,6 +18,12 @@ in bf16 and quantises them into the cache (kv_append_fp8: per-block scale
 update, re-encoding when a scale grows) instead of copying ready-made codes.
 The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
 8 KV heads, d 128, lengths uniform in [1024, 2048], 32 layers, bf16 KV).
+Decode steps of several layers are recorded once into two HIP graphs (prep,
+attention) after the eager warm-up and replayed in the timed steps, so the
+host's launch work is off the clock (--graph off launches every kernel from
+Python; a one-layer step does so by default, a graph replay costing more than
+its few direct launches); the bounded-sample parity check reads the outputs of
+the replayed steps.
 
 Prints one JSON line.  `value` is achieved GB/s (algorithmic bytes / wall
 time of the K timed steps); `roofline` describes the decode call (split-K
@@ -213,7 +219,8 @@ class DecodeWorkload:
 
     calls_per_event = property(lambda self: self.layers)
 
-    def step(self, events=None):
+    def prep(self):
+        """Slot mapping, work order and every layer's append for the batch's current token."""
         pkv = self.pkv
         pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
         if not self.csr:
@@ -226,10 +233,44 @@ class DecodeWorkload:
                                   self.positions, self.cu_new, 1, self.k_new[layer], self.v_new[layer])
             else:
                 pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
-        if events is not None:
-            events[0].record()
+
+    def attend(self):
         for layer in range(self.layers):
             self.decode_call(layer)
+
+    def step(self, events=None):
+        self.prep()
+        if events is not None:
+            events[0].record()
+        self.attend()
+        if events is not None:
+            events[1].record()
+
+    def capture(self):
+        """Record the step's launches in two HIP graphs (prep, attention), so a
+        timed step replays them without per-launch host work.  Every step
+        appends the same token into the same slot, so replays compute what the
+        eager step computes."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.prep()
+            self.attend()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.g_prep, self.g_attend = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g_prep):
+            self.prep()
+        with torch.cuda.graph(self.g_attend):
+            self.attend()
+        torch.cuda.synchronize()
+
+    def graph_step(self, events=None):
+        self.g_prep.replay()
+        if events is not None:
+            events[0].record()
+        self.g_attend.replay()
         if events is not None:
             events[1].record()
 
@@ -494,6 +535,10 @@ def main():
     ap.add_argument("--prefill-kv", choices=["bf16", "fp8"], default="bf16",
                     help="prefill workload: KV cache element type (fp8: the chunk is quantised on append)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="decode workloads: replay each step from HIP graphs (auto: when the step has several "
+                         "layers; a graph replay costs more than a few direct launches, so a one-layer step "
+                         "launches its kernels directly)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -529,12 +574,19 @@ def main():
     for _ in range(args.warmup):
         w.step()
     torch.cuda.synchronize()
+    graphs = not prefill and (args.graph == "on" or (args.graph == "auto" and w.layers >= 4))
+    step = w.step
+    if graphs:
+        w.capture()
+        for _ in range(args.warmup):
+            w.graph_step()
+        step = w.graph_step
 
     events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        w.step(events[k])
+        step(events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     call_ms = [e0.elapsed_time(e1) / w.calls_per_event for e0, e1 in events]
@@ -569,7 +621,8 @@ def main():
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "kernel": w.kernel_desc(),
-                        "timing": f"HIP events around each step's {w.layers} back-to-back decode calls, / {w.layers}",
+                        "timing": f"HIP events around each step's {w.layers} back-to-back decode calls"
+                                  + (" (replayed from a HIP graph)" if graphs else "") + f", / {w.layers}",
                         "avg_call_us": round(avg_call_s * 1e6, 3), "bytes_per_call": w.layer_bytes}}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
