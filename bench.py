@@ -187,7 +187,9 @@ class DecodeWorkload:
         self.positions = (self.seq_lens_t - 1).to(torch.int32)
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
         self.cu_new = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
-        self.order = torch.arange(self.batch, dtype=torch.int32, device=dev)
+        self.order = torch.empty(pkv.paged_attn_decode_order_entries(self.batch, self.n_q, self.n_kv, self.d,
+                                                                     self.max_blocks, B, pkv.dtype_code(self.k[0])),
+                                 dtype=torch.int32, device=dev)
         self.out = [torch.empty((self.batch, self.n_q, self.d), dtype=torch.float32, device=dev)
                     for _ in range(self.layers)]
         ws = pkv.paged_attn_decode_workspace(self.batch, self.n_q, self.n_kv, self.d, self.max_blocks, B,

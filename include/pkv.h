@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 
 typedef enum {
   PKV_OK = 0,
@@ -333,26 +333,44 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
                                       int32_t partition_tokens, int32_t* info);
 
 /* Work order for the decode calls of one step (every layer decodes the same
- * batch): ranks the sequences by length (longer first, ties by index) and
- * writes work_order_out (device int32 [batch]), the permutation
- * pkv_paged_attn_decode_ordered takes.  When every split workgroup of the call
- * is resident at once (workgroups i and i + half the grid share a CU) the k-th
- * longest sequence is paired with the k-th shortest; otherwise the longest
- * come first, so the short ones fill the end.  Balancing is this library's
- * addition to the pages' split of a sequence across thread blocks ([KVP]
- * Problem 5, serving note).  Arguments as pkv_paged_attn_decode_plan; one
- * launch of about batch^2 length comparisons, meant to run once per step. */
+ * batch), the order pkv_paged_attn_decode_ordered takes; work_order_out is
+ * device int32 with pkv_paged_attn_decode_order_entries() entries.
+ *  - When the library's split gives each sequence one partition (or the work
+ *    queue), the entries are a permutation of 0 .. batch - 1: the sequences
+ *    ranked by length (longer first, ties by index).  When every split
+ *    workgroup is resident at once (workgroups i and i + half the grid share
+ *    a CU) the k-th longest sequence is paired with the k-th shortest;
+ *    otherwise the longest come first, so the short ones fill the end.
+ *  - When the split has several partitions per sequence (and at most 8192
+ *    (sequence, partition) units), the entries list the units u = sequence *
+ *    n_parts + partition, ranked by their token counts (more first, ties by
+ *    index), followed by -1 for every unit without tokens: a long sequence's
+ *    later partitions then start with the other long work, and the empty
+ *    units come last.
+ * Balancing is this library's addition to the pages' split of a sequence
+ * across thread blocks ([KVP] Problem 5, serving note).  Arguments as
+ * pkv_paged_attn_decode_plan; one launch of about entries^2 comparisons,
+ * meant to run once per step. */
 pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                                        int32_t d_head, int32_t max_blocks_per_seq, int32_t block_size,
                                        pkv_dtype kv_dtype, int32_t* work_order_out, void* stream);
 
-/* Decode as pkv_paged_attn_decode (the library's split) with the sequence
- * slots of the split grid taken in work_order (device int32 [batch], a
- * permutation of 0 .. batch - 1; entries are clamped into range, so anything
- * else computes some sequences twice and leaves others unwritten).  Every
- * (sequence, head, partition) is computed the same way whichever workgroup
- * takes it, so the output is bit-identical to pkv_paged_attn_decode's for any
- * permutation.  The work-queue split ignores the order. */
+/* Entries of the work order for these arguments (host call): batch, or batch
+ * * partitions per sequence when the order lists (sequence, partition) units;
+ * 0 for invalid arguments or when the split needs a device and none is
+ * present. */
+int32_t pkv_paged_attn_decode_order_entries(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                            int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype);
+
+/* Decode as pkv_paged_attn_decode (the library's split) with the split
+ * grid's work taken in work_order (device int32, as pkv_paged_attn_decode_order
+ * writes it: a permutation of the sequences, or the list of (sequence,
+ * partition) units followed by -1s; entries are clamped into range, so
+ * anything else computes some work twice and leaves other outputs unwritten
+ * or unmerged).  Every (sequence, head, partition) is computed the same way
+ * whichever workgroup takes it, so the output is bit-identical to
+ * pkv_paged_attn_decode's for any such order.  The work-queue split ignores
+ * the order. */
 pkv_status pkv_paged_attn_decode_ordered(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
                                          const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
                                          const float* k_scale, const float* v_scale, const int32_t* block_table,

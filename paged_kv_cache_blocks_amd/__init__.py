@@ -46,6 +46,7 @@ _SIGS = {
                                        _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp],
                                       ctypes.c_int),
     "pkv_paged_attn_decode_order": ([_vp, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "pkv_paged_attn_decode_order_entries": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int], _i32),
     "pkv_paged_attn_decode_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32], _sz),
     "pkv_paged_attn_decode_plan": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _i32, _vp], ctypes.c_int),
     "pkv_paged_attn_prefill_chunk": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
@@ -362,8 +363,10 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
     ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if work_order is not None:
         _need(work_order, torch.int32, "work_order")
-        if partition_tokens != 0 or work_order.numel() != batch:
-            raise ValueError("work_order takes the library's split and one entry per sequence")
+        n = paged_attn_decode_order_entries(batch, n_q_heads, n_kv_heads, d_head, block_table.shape[1], block_size,
+                                            dtype_code(k_cache))
+        if partition_tokens != 0 or work_order.numel() != n:
+            raise ValueError(f"work_order takes the library's split and {n} entries (paged_attn_decode_order)")
         _check(load().pkv_paged_attn_decode_ordered(
             _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
             _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb,
@@ -376,13 +379,29 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
     return out
 
 
+def paged_attn_decode_order_entries(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
+                                    kv_dtype: int = BF16) -> int:
+    """int32 entries of the work order for these arguments (batch, or batch x partitions)."""
+    n = load().pkv_paged_attn_decode_order_entries(batch, n_q_heads, n_kv_heads, d_head, int(max_blocks_per_seq),
+                                                   block_size, kv_dtype)
+    if n <= 0:
+        raise PkvError(ERR_INVALID_ARG, "no work order for these arguments: " + load().pkv_last_error().decode())
+    return n
+
+
 def paged_attn_decode_order(seq_lens, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size=16,
                             kv_dtype: int = BF16, out=None, stream=None) -> torch.Tensor:
-    """Work order (int32 permutation of the batch) for the decode calls of one step."""
+    """Work order for the decode calls of one step: the sequences ranked by
+    length, or, when the split has several partitions per sequence, the
+    (sequence, partition) units ranked by tokens followed by -1s."""
     _need(seq_lens, torch.int32, "seq_lens")
     batch = seq_lens.numel()
+    n = paged_attn_decode_order_entries(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size,
+                                        kv_dtype)
     if out is None:
-        out = torch.empty(batch, dtype=torch.int32, device=seq_lens.device)
+        out = torch.empty(n, dtype=torch.int32, device=seq_lens.device)
+    elif out.numel() != n or out.dtype != torch.int32:
+        raise ValueError(f"the work order takes {n} int32 entries")
     _check(load().pkv_paged_attn_decode_order(_ptr(seq_lens), batch, n_q_heads, n_kv_heads, d_head,
                                               int(max_blocks_per_seq), block_size, kv_dtype, _ptr(out),
                                               _stream(stream)))

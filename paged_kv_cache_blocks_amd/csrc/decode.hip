@@ -548,9 +548,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int w = threadIdx.x / kWave;
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
-  int s = (blockIdx.x / hk) % a.batch;  // sequence slot -> sequence (the caller's work order, if any)
-  if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
-  const int part = blockIdx.x / (hk * a.batch);
+  int s, part;  // the unit this workgroup serves: see the matrix-core kernel
+  if (a.work_order && a.order_units) {
+    const int u = __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x / hk]);
+    if (u < 0) return;
+    const int uc = min(u, a.batch * a.n_parts - 1);
+    s = uc / a.n_parts;
+    part = uc % a.n_parts;
+  } else {
+    s = (blockIdx.x / hk) % a.batch;  // sequence slot -> sequence (the caller's work order, if any)
+    if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
+    part = blockIdx.x / (hk * a.batch);
+  }
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int p0 = part * a.part_tokens;
@@ -1095,6 +1104,39 @@ __global__ __launch_bounds__(256) void decode_order_kernel(const int32_t* __rest
   const int half = (batch + 1) / 2;
   const int slot = (!pair || r < half) ? r : half + (batch - 1 - r);
   order[slot] = t;
+}
+
+// Unit order of a split decode: thread t ranks unit t = (sequence t / n_parts,
+// partition t % n_parts) by its token count against every other unit (more
+// tokens first, ties by index) and writes t into the slot of its rank, or -1
+// when the unit has no tokens (those rank last).
+__global__ __launch_bounds__(256) void decode_unit_order_kernel(const int32_t* __restrict__ seq_lens, int32_t batch,
+                                                                int32_t n_parts, int32_t part_tokens,
+                                                                int32_t* __restrict__ order) {
+  const int n = batch * n_parts;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n) return;
+  auto tokens = [&](int u) {
+    const int L = max(seq_lens[u / n_parts], 0);
+    return min(max(L - (u % n_parts) * part_tokens, 0), part_tokens);
+  };
+  const int lt = tokens(t);
+  int r = 0;
+#pragma unroll 4
+  for (int u = 0; u < n; ++u) {
+    const int lu = tokens(u);
+    r += (lu > lt) | ((lu == lt) & (u < t));
+  }
+  order[r] = lt > 0 ? t : -1;
+}
+
+hipError_t launch_decode_unit_order(const int32_t* seq_lens, int32_t batch, int32_t n_parts, int32_t part_tokens,
+                                    int32_t* order, hipStream_t stream) {
+  const int n = batch * n_parts;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_unit_order_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, seq_lens,
+                     batch, n_parts, part_tokens, order);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_order(const int32_t* seq_lens, int32_t batch, int32_t pair, int32_t* order,

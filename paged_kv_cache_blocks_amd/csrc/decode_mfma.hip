@@ -81,12 +81,25 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int n = lane & 15, g = lane >> 4;
   const int hk = a.n_kv * a.head_chunks;
   const int kvc = blockIdx.x % hk;
-  // sequence slot -> sequence: the batch order, or the caller's work order
-  // (pkv_paged_attn_decode_order: long sequences paired with short ones on a
-  // CU, or the longest first); results do not depend on it
-  int s = (blockIdx.x / hk) % a.batch;
-  if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
-  const int part = blockIdx.x / (hk * a.batch);
+  // The unit (sequence, partition) of this workgroup; results do not depend
+  // on which workgroup takes which unit.  With a unit order (split calls,
+  // pkv_paged_attn_decode_order) entry blockIdx / hk names the unit, longest
+  // first, and -1 marks a unit without tokens, so real second partitions start
+  // early and the empty ones come last.  Otherwise the grid is partition by
+  // partition, its sequence slots mapped through the caller's sequence order if
+  // any (long sequences paired with short ones on a CU, or the longest first).
+  int s, part;
+  if (a.work_order && a.order_units) {
+    const int u = __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x / hk]);
+    if (u < 0) return;
+    const int uc = min(u, a.batch * a.n_parts - 1);
+    s = uc / a.n_parts;
+    part = uc % a.n_parts;
+  } else {
+    s = (blockIdx.x / hk) % a.batch;
+    if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
+    part = blockIdx.x / (hk * a.batch);
+  }
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int p0 = part * a.part_tokens;

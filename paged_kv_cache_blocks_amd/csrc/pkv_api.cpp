@@ -244,6 +244,15 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
   return PKV_OK;
 }
 
+// A split call's work order lists its (sequence, partition) units, longest
+// first (a unit order), when it has several partitions per sequence and few
+// enough units for the order kernel's all-pairs ranking; otherwise it lists
+// the sequences.
+constexpr int64_t kMaxOrderUnits = 8192;
+bool order_units(const DecodePlan& p, int32_t batch) {
+  return !p.n_wg && p.n_parts > 1 && (int64_t)batch * p.n_parts <= kMaxOrderUnits;
+}
+
 const float kLog2e = 1.4426950408889634f;
 
 }  // namespace
@@ -551,6 +560,7 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
   a.head_chunks = plan.head_chunks;
   a.use_mfma = plan.use_mfma;
   a.work_order = work_order;
+  a.order_units = (work_order && order_units(plan, batch)) ? 1 : 0;
   a.part_tokens = plan.part_tokens;
   a.n_parts = plan.n_parts;
   a.out_bf16 = out_dtype == PKV_BF16;
@@ -596,6 +606,10 @@ pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, i
   pkv_status st = plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype, 0,
                               &plan);
   if (st != PKV_OK) return st;
+  if (order_units(plan, batch))
+    return hip_status(pkv::launch_decode_unit_order(seq_lens, batch, plan.n_parts, plan.part_tokens, work_order_out,
+                                                    (hipStream_t)stream),
+                      "decode order launch");
   // All split workgroups resident at once: workgroups i and i + half the grid
   // share a CU, so pair the k-th longest sequence with the k-th shortest.
   // Otherwise workgroups start as others finish: the longest first.
@@ -611,6 +625,15 @@ pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, i
   }
   return hip_status(pkv::launch_decode_order(seq_lens, batch, pair, work_order_out, (hipStream_t)stream),
                     "decode order launch");
+}
+
+int32_t pkv_paged_attn_decode_order_entries(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                            int32_t max_blocks_per_seq, int32_t block_size, pkv_dtype kv_dtype) {
+  DecodePlan plan;
+  if (plan_decode(batch, n_q_heads, n_kv_heads, d_head, max_blocks_per_seq, block_size, (int)kv_dtype, 0, &plan) !=
+      PKV_OK)
+    return 0;
+  return order_units(plan, batch) ? batch * plan.n_parts : batch;
 }
 
 pkv_status pkv_paged_attn_decode_csr(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,

@@ -41,6 +41,7 @@ struct DecodeArgs {
   int32_t out_bf16;
   int32_t use_mfma;     // partition mode: the matrix-core split kernel (decode_mfma.hip)
   const int32_t* work_order;  // partition mode: sequence slot -> sequence (a permutation), or null
+  int32_t order_units;        // work_order is a unit list (entry i: sequence * n_parts + partition, or -1)
   float scale_log2;     // softmax scale * log2(e)
 };
 
@@ -58,6 +59,10 @@ hipError_t launch_decode(const DecodeArgs& a, int kv_kind, int d, hipStream_t st
 // and s + ceil(batch / 2)
 hipError_t launch_decode_order(const int32_t* seq_lens, int32_t batch, int32_t pair, int32_t* order,
                                hipStream_t stream);
+// order[rank] = unit (sequence * n_parts + partition) by token count, more
+// first; units without tokens rank last as -1
+hipError_t launch_decode_unit_order(const int32_t* seq_lens, int32_t batch, int32_t n_parts, int32_t part_tokens,
+                                    int32_t* order, hipStream_t stream);
 // matrix-core decode (partition mode only): bf16 / fp8 KV, d = 128, 4, 8 or 16 heads per workgroup
 bool decode_mfma_supported(int kv_kind, int d, int heads_per_wg);
 int decode_mfma_wgs_per_cu(int kv_kind, int heads_per_wg);

@@ -38,7 +38,8 @@ def test_graph_replay_matches_eager(pkv, kind):
     seq_ids = torch.arange(batch, dtype=torch.int32, device="cuda")
     positions = (sl - 1).to(torch.int32)
     slots = [torch.empty(batch, dtype=torch.int64, device="cuda") for _ in range(2)]
-    order = torch.empty(batch, dtype=torch.int32, device="cuda")
+    order = torch.empty(pkv.paged_attn_decode_order_entries(batch, n_q, n_kv, d, tables[0].shape[1], B, kvd),
+                        dtype=torch.int32, device="cuda")
     mb = tables[0].shape[1]
     ws = torch.zeros(max(pkv.paged_attn_decode_workspace(batch, n_q, n_kv, d, mb, B, kvd), 256),
                      dtype=torch.uint8, device="cuda")

@@ -1,6 +1,8 @@
 """GPU checks of the decode work order: pkv_paged_attn_decode_order writes the
-length ranking (pairing long with short, or longest first), and decode with
-any permutation as work order gives bit-identical outputs to plain decode."""
+length ranking (pairing long with short, or longest first) or, for a split
+with several partitions per sequence, the (sequence, partition) units ranked by
+tokens followed by -1s; decode with any such order gives bit-identical outputs
+to plain decode."""
 import numpy as np
 import pytest
 import torch
@@ -26,15 +28,30 @@ def _expected(lens):
     return desc, pair
 
 
-@pytest.mark.parametrize("batch", [1, 2, 7, 64, 256, 1000])
-def test_order_is_the_length_ranking(pkv, batch):
-    r = np.random.default_rng(970 + batch)
-    lens = r.integers(0, 3000, size=batch).astype(np.int32)
+def _expected_units(lens, n_parts, part_tokens):
+    tok = {s * n_parts + p: min(max(int(lens[s]) - p * part_tokens, 0), part_tokens)
+           for s in range(len(lens)) for p in range(n_parts)}
+    ranked = sorted(tok, key=lambda u: (-tok[u], u))
+    return [u if tok[u] > 0 else -1 for u in ranked]
+
+
+@pytest.mark.parametrize("batch,max_len", [(1, 3000), (2, 3000), (7, 3000), (64, 3000), (256, 3000), (1000, 3000),
+                                           (64, 9000), (256, 8192)])
+def test_order_is_the_length_ranking(pkv, batch, max_len):
+    r = np.random.default_rng(970 + batch + max_len)
+    lens = r.integers(0, max_len, size=batch).astype(np.int32)
     lens[::5] = lens[0]  # ties
-    note(f"decode order batch={batch}")
-    got = pkv.paged_attn_decode_order(dev(lens), 32, 8, 128, 3000 // 16 + 1, 16, pkv.BF16).cpu().tolist()
-    desc, pair = _expected(lens)
-    assert got == desc or got == pair
+    mb = max_len // 16 + 1
+    note(f"decode order batch={batch} max_len={max_len}")
+    got = pkv.paged_attn_decode_order(dev(lens), 32, 8, 128, mb, 16, pkv.BF16).cpu().tolist()
+    plan = pkv.paged_attn_decode_plan(batch, 32, 8, 128, mb, 16, pkv.BF16)
+    if len(got) == batch:
+        desc, pair = _expected(lens)
+        assert got == desc or got == pair
+    else:
+        # several partitions per sequence: the unit order
+        assert plan["n_parts"] > 1 and len(got) == batch * plan["n_parts"]
+        assert got == _expected_units(lens, plan["n_parts"], plan["partition_tokens"])
 
 
 @pytest.mark.parametrize("kind,d,n_q,n_kv", [("bf16", 128, 32, 8), ("fp8", 128, 64, 8), ("f32", 64, 8, 2)])
@@ -51,10 +68,13 @@ def test_ordered_decode_is_bit_identical(pkv, kind, d, n_q, n_kv):
     plain = run()
     lib_order = pkv.paged_attn_decode_order(t["seq_lens"], n_q, n_kv, d, c.block_table.shape[1], 16,
                                             pkv.dtype_code(t["k_cache"]))
-    rand = torch.from_numpy(np.random.default_rng(5).permutation(len(lens)).astype(np.int32)).cuda()
-    ident = torch.arange(len(lens), dtype=torch.int32, device="cuda")
+    n = lib_order.numel()  # sequences, or (sequence, partition) units
+    assert n == len(lens) or n % len(lens) == 0
+    rand = torch.from_numpy(np.random.default_rng(5).permutation(n).astype(np.int32)).cuda()
+    ident = torch.arange(n, dtype=torch.int32, device="cuda")
     ordered = run(lib_order)
-    # the order only moves work between workgroups: the same bits for every permutation
+    # the order only moves work between workgroups: the same bits for every
+    # permutation (a unit list may name empty units too: they exit)
     for o in (rand, ident):
         assert np.array_equal(run(o).view(np.uint32), ordered.view(np.uint32))
     want = oracle_decode(c)
