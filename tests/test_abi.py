@@ -148,6 +148,21 @@ def test_work_order_entry_points_validate(pkv):
     assert lib.pkv_paged_attn_decode_ordered(*args) == pkv.ERR_INVALID_ARG   # no order
 
 
+def test_work_order_entries(pkv):
+    """Size of the work order: one entry per sequence when each sequence is one
+    partition, one per (sequence, partition) unit when the matrix-core split
+    cuts sequences into several (without a device the split is planned from
+    the sizes alone); 0 for invalid arguments."""
+    lib = pkv.load()
+    assert lib.pkv_paged_attn_decode_order_entries(64, 32, 8, 128, 128, 16, pkv.BF16) == 64          # 2048 tokens
+    assert lib.pkv_paged_attn_decode_order_entries(256, 64, 8, 128, 512, 16, pkv.FP8_E4M3FN) == 512  # 8192: 2 parts
+    assert lib.pkv_paged_attn_decode_order_entries(8, 64, 8, 128, 2048, 16, pkv.BF16) == 64          # 32768: 8 parts
+    assert lib.pkv_paged_attn_decode_order_entries(2048, 64, 8, 128, 512, 16, pkv.BF16) == 4096     # 2 parts
+    assert lib.pkv_paged_attn_decode_order_entries(8192, 64, 8, 128, 512, 16, pkv.BF16) == 8192     # > 8192 units
+    assert lib.pkv_paged_attn_decode_order_entries(4, 6, 4, 128, 8, 16, pkv.BF16) == 0              # head ratio
+    assert lib.pkv_paged_attn_decode_order_entries(4, 8, 2, 96, 8, 16, pkv.BF16) == 0               # d_head
+
+
 def test_decode_workspace_sizes(pkv):
     # partition mode: one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
     assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 4, 16, pkv.BF16, 256) == 0
