@@ -470,6 +470,49 @@ def traffic_from_profile(workload_key):
 
 # ---------------------------------------------------------------------------
 
+def read_probe_bench():
+    """Read bandwidth a plain kernel gets on this GPU: a 2 GiB buffer read in
+    grid-stride order, and randomly placed slabs (4 KiB: one (block, KV head)
+    slab of a bf16 paged cache; 16 KiB) of its first 430 MB, the size of one
+    8B-shaped decode call, with ordinary and non-temporal loads.  Best of 5
+    event-timed launches after one warm-up."""
+    import torch
+    import paged_kv_cache_blocks_amd as pkv
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    region = 430 * 10 ** 6
+    rows = []
+
+    def timed(fn):
+        fn()
+        best = float("inf")
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) / 1e3)
+        return best
+
+    for nt in (False, True):
+        for wgs in (1024, 2048, 4096):
+            t = timed(lambda: pkv.read_probe(buf, sink, None, 4096, wgs, nt))
+            rows.append({"pattern": "sequential", "bytes": nbytes, "workgroups": wgs, "nontemporal": nt,
+                         "GB/s": round(nbytes / t / 1e9, 1)})
+    for slab in (4096, 16384):
+        n = region // slab
+        perm = torch.from_numpy(np.random.default_rng(7).permutation(n).astype(np.int32)).cuda()
+        for nt in (False, True):
+            for wgs in (512, 1024):
+                per = n // wgs
+                t = timed(lambda: pkv.read_probe(buf, sink, perm, slab, wgs, nt))
+                rows.append({"pattern": f"random {slab // 1024} KiB slabs", "bytes": per * wgs * slab,
+                             "workgroups": wgs, "nontemporal": nt, "GB/s": round(per * wgs * slab / t / 1e9, 1)})
+    return {"read_probe": rows, "peak_GB/s": HBM_PEAK_GBS}
+
+
 def swap_bench(cfg, args):
     """Swap N blocks of one layer of a decode workload out to pinned host
     memory and back (preemption by swap); image bytes / time per direction,
@@ -541,6 +584,9 @@ def main():
                     help="decode workloads: replay each step from HIP graphs (auto: when the step has several "
                          "layers; a graph replay costs more than a few direct launches, so a one-layer step "
                          "launches its kernels directly)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="run only the library's read probe: the HBM read bandwidth of a plain kernel, sequential and "
+                         "over randomly placed slabs, with ordinary and non-temporal loads")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="run only a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -552,6 +598,10 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench needs a GPU"
     torch.cuda.set_device(0)
+
+    if args.read_probe:
+        print(json.dumps(read_probe_bench()))
+        return
 
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb * 2 ** 20 // 4

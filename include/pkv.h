@@ -148,6 +148,21 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
  * caller zeroes first), every sequence with seq_lens[s] < 0 or
  * > max_blocks_per_seq * B and every table entry a sequence uses (logical
  * block < ceil(seq_len / B)) that lies outside [0, num_blocks). */
+/* Read probe, a measurement aid outside the attention path: the bandwidth a
+ * plain kernel gets from HBM, to set beside the decode figures.  Reads the
+ * device buffer buf (bytes, a multiple of 16) with 16-byte loads on
+ * `workgroups` workgroups of 256 threads: with slab_list == NULL every byte in
+ * grid-stride order; otherwise the slabs of slab_bytes (a multiple of 4096)
+ * named by slab_list (device int32 [n_list], entries clamped into the buffer),
+ * workgroup w reading entries w * (n_list / workgroups) onward one slab after
+ * another, the pattern of one (block, KV head) slab of a paged cache.
+ * nontemporal != 0 sets the nt bit on the loads.  sink (device uint32) is
+ * written only in the practically impossible case that the folded data equals
+ * a fixed pattern.  Errors: INVALID_ARG for null pointers, sizes out of range
+ * or fewer list entries than workgroups; HIP for launch failures. */
+pkv_status pkv_read_probe(const void* buf, int64_t bytes, const int32_t* slab_list, int32_t n_list,
+                          int32_t slab_bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink, void* stream);
+
 pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                             int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
                             void* stream);

@@ -37,6 +37,7 @@ _SIGS = {
                           _vp],
                          ctypes.c_int),
     "pkv_check_tables": ([_vp, _i32, _vp, _i32, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "pkv_read_probe": ([_vp, _i64, _vp, _i32, _i32, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_paged_attn_decode": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp,
                                _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp], ctypes.c_int),
     "pkv_paged_attn_decode_partitioned": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
@@ -484,3 +485,16 @@ def paged_attn_prefill_chunk(q, cu_q_lens, context_lens, max_q_len, k_cache, v_c
         _ptr(block_table), block_table.shape[1], k_cache.shape[0], n_q_heads, n_kv_heads, d_head, block_size,
         float(scale), 1 if causal else 0, None, 0, _stream(stream)))
     return out
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, slab_list: Optional[torch.Tensor] = None, slab_bytes: int = 4096,
+               workgroups: int = 512, nontemporal: bool = True, stream=None) -> None:
+    """Stream buf (grid-stride, or the listed slabs) with 16-byte loads: a
+    measurement aid for the read bandwidth a plain kernel gets."""
+    nbytes = buf.numel() * buf.element_size()
+    n_list = 0
+    if slab_list is not None:
+        _need(slab_list, torch.int32, "slab_list")
+        n_list = slab_list.numel()
+    _check(load().pkv_read_probe(_ptr(buf), nbytes, _ptr(slab_list), n_list, slab_bytes, workgroups,
+                                 1 if nontemporal else 0, _ptr(sink), _stream(stream)))

@@ -405,4 +405,69 @@ hipError_t launch_swap(void* k_cache, void* v_cache, float* k_scale, float* v_sc
   return hipGetLastError();
 }
 
+// ---- read probe (measurement aid, not part of the attention path) ----
+// Streams a buffer with 16-byte loads and keeps only a token of what it read,
+// so its duration gives the read bandwidth the memory system delivers to a
+// plain kernel: either every 16-byte piece in grid-stride order, or slabs of
+// slab_bytes (a multiple of 4 KiB) named by a list, each workgroup reading its
+// share of the list one slab after another (the access pattern of one
+// (block, KV head) slab of a paged cache).  nt selects non-temporal loads.
+template <int NT>
+__device__ __forceinline__ u32x4 probe_ld(const char* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int NT>
+__global__ __launch_bounds__(256) void read_probe_kernel(const char* __restrict__ buf, int64_t bytes,
+                                                         const int32_t* __restrict__ slabs, int32_t per_wg,
+                                                         int32_t slab_bytes, int64_t n_slabs,
+                                                         uint32_t* __restrict__ sink) {
+  uint32_t acc = 0;
+  if (!slabs) {
+    const int64_t n16 = bytes / 16;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) {
+      const u32x4 v = probe_ld<NT>(buf + i * 16);
+      acc ^= v[0] ^ v[3];
+    }
+  } else {
+    // four slabs at a time, so each thread keeps four loads in flight
+    const int32_t* my = slabs + (int64_t)blockIdx.x * per_wg;
+    auto slab_at = [&](int j) { return buf + min(max((int64_t)my[j], (int64_t)0), n_slabs - 1) * slab_bytes; };
+    int j = 0;
+    for (; j + 4 <= per_wg; j += 4) {
+      const char* sp[4] = {slab_at(j), slab_at(j + 1), slab_at(j + 2), slab_at(j + 3)};
+      for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
+        u32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = probe_ld<NT>(sp[q] + o);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc ^= v[q][0] ^ v[q][3];
+      }
+    }
+    for (; j < per_wg; ++j) {
+      const char* slab = slab_at(j);
+      for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
+        const u32x4 v = probe_ld<NT>(slab + o);
+        acc ^= v[0] ^ v[3];
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;  // keeps the loads; practically never stores
+}
+
+hipError_t launch_read_probe(const void* buf, int64_t bytes, const int32_t* slabs, int32_t n_list, int32_t slab_bytes,
+                             int32_t workgroups, int32_t nt, uint32_t* sink, hipStream_t stream) {
+  const int32_t per_wg = slabs ? n_list / workgroups : 0;
+  const int64_t n_slabs = slab_bytes > 0 ? bytes / slab_bytes : 0;
+  const char* b = reinterpret_cast<const char*>(buf);
+  if (nt)
+    hipLaunchKernelGGL(read_probe_kernel<1>, dim3(workgroups), dim3(256), 0, stream, b, bytes, slabs, per_wg,
+                       slab_bytes, n_slabs, sink);
+  else
+    hipLaunchKernelGGL(read_probe_kernel<0>, dim3(workgroups), dim3(256), 0, stream, b, bytes, slabs, per_wg,
+                       slab_bytes, n_slabs, sink);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

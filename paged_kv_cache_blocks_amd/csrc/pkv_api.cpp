@@ -445,6 +445,20 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
                     "gather launch");
 }
 
+pkv_status pkv_read_probe(const void* buf, int64_t bytes, const int32_t* slab_list, int32_t n_list,
+                          int32_t slab_bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (bytes < 16 || bytes % 16 != 0 || workgroups < 1) return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if (slab_list) {
+    if (slab_bytes < 4096 || slab_bytes % 4096 != 0 || slab_bytes > bytes)
+      return fail(PKV_ERR_INVALID_ARG, "slab_bytes must be a multiple of 4096 within the buffer");
+    if (n_list < workgroups) return fail(PKV_ERR_INVALID_ARG, "fewer slabs than workgroups");
+  }
+  return hip_status(pkv::launch_read_probe(buf, bytes, slab_list, n_list, slab_bytes, workgroups, nontemporal ? 1 : 0,
+                                           sink, (hipStream_t)stream),
+                    "read probe launch");
+}
+
 pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                             int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
                             void* stream) {

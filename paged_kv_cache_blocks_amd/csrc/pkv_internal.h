@@ -91,6 +91,8 @@ hipError_t launch_swap(void* k_cache, void* v_cache, float* k_scale, float* v_sc
                        hipStream_t stream);
 hipError_t launch_csr_to_table(const int32_t* indptr, const int32_t* indices, int32_t batch, int32_t max_blocks,
                                int32_t* table, hipStream_t stream);
+hipError_t launch_read_probe(const void* buf, int64_t bytes, const int32_t* slabs, int32_t n_list, int32_t slab_bytes,
+                             int32_t workgroups, int32_t nt, uint32_t* sink, hipStream_t stream);
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
 

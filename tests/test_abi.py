@@ -163,6 +163,17 @@ def test_work_order_entries(pkv):
     assert lib.pkv_paged_attn_decode_order_entries(4, 8, 2, 96, 8, 16, pkv.BF16) == 0               # d_head
 
 
+def test_read_probe_validates(pkv):
+    lib = pkv.load()
+    f = lib.pkv_read_probe
+    assert f(None, 4096, None, 0, 4096, 8, 1, 0x1000, None) == pkv.ERR_INVALID_ARG        # no buffer
+    assert f(0x1000, 4096, None, 0, 4096, 8, 1, None, None) == pkv.ERR_INVALID_ARG        # no sink
+    assert f(0x1000, 4100, None, 0, 4096, 8, 1, 0x2000, None) == pkv.ERR_INVALID_ARG      # not 16-byte pieces
+    assert f(0x1000, 1 << 20, 0x3000, 64, 1000, 8, 1, 0x2000, None) == pkv.ERR_INVALID_ARG  # slab size
+    assert f(0x1000, 1 << 20, 0x3000, 4, 4096, 8, 1, 0x2000, None) == pkv.ERR_INVALID_ARG   # fewer slabs than WGs
+    assert f(0x1000, 1 << 20, None, 0, 4096, 0, 1, 0x2000, None) == pkv.ERR_INVALID_ARG     # no workgroups
+
+
 def test_decode_workspace_sizes(pkv):
     # partition mode: one partition -> none; otherwise batch * n_q * parts * (d + 2) floats (d part rounded to 256 B)
     assert pkv.paged_attn_decode_workspace(2, 8, 2, 64, 4, 16, pkv.BF16, 256) == 0
