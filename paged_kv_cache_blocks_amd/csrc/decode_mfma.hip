@@ -13,15 +13,18 @@
 // softmax.
 //
 // Work decomposition (as the VALU kernel's partition mode): one workgroup per
-// (sequence, KV head chunk, partition); its four waves take 32-token chunks
+// (sequence, KV head chunk, partition), in the caller's work order if given
+// (sequences, or (sequence, partition) units); its four waves take 32-token chunks
 // (two 16-token tiles) round robin and keep their own running state, merged
 // at the end through LDS.  Each tile is two 8-token halves, each inside one
 // cache block whatever the block size (8 .. 256) and table format.  Per chunk
 // a wave:
 //   loads the K and V rows of its two tiles with coalesced, non-temporal
-//   16-byte loads (issued one chunk ahead), converts fp8 codes to bf16 (exact), and writes them into
-//   its own LDS region in the swizzled row layout (V rows past the end of the
-//   sequence are written as zeros: their zero weights must not meet a NaN);
+//   16-byte loads (issued one chunk ahead, from a scalar base per half),
+//   converts fp8 codes to bf16 (exact), and writes them into its own LDS
+//   region in the swizzled row layout (on a partition's last chunk, V rows
+//   past its end are written as zeros: their zero weights must not meet a
+//   NaN, and only that chunk masks scores);
 //   S^T = K q^T: 2 token tiles x 4 d steps, K fragments from LDS, q^T in
 //   registers; the fp8 K scale of each half's block multiplies its scores;
 //   online softmax per head column (in-lane max over the lane's 8 tokens,
