@@ -16,8 +16,13 @@ resident in HBM:
 With --fp8-append quantize the FP8 workload's append takes the token's rows
 in bf16 and quantises them into the cache (kv_append_fp8: per-block scale
 update, re-encoding when a scale grows) instead of copying ready-made codes.
-The default workload is the Llama3-8B-shaped decode (batch 64, 32 query heads,
-8 KV heads, d 128, lengths uniform in [1024, 2048], 32 layers, bf16 KV).
+The default workload is the 70B-shaped long-context decode (batch 8, every
+sequence 32768 tokens, 64 query heads, 8 KV heads, d 128, 80 layers, bf16 KV:
+about 86 GB of cache), the largest of the workloads that fits one GPU;
+--workload picks another (the 8B-shaped decode, the fp8 serving mix, the tiny
+fp32 case, the prefill chunk).  The tiny and prefill workloads are timed
+cold: an untimed 512 MiB write before every step keeps their small working
+sets out of the caches, and the medians of per-step events are reported.
 Decode steps of several layers are recorded once into two HIP graphs (prep,
 attention) after the eager warm-up and replayed in the timed steps, so the
 host's launch work is off the clock (--graph off launches every kernel from
@@ -26,11 +31,12 @@ its few direct launches); the bounded-sample parity check reads the outputs of
 the replayed steps.
 
 Prints one JSON line.  `value` is achieved GB/s (algorithmic bytes / wall
-time of the K timed steps); `roofline` describes the decode call (split-K
-kernel + merge when split), timed with HIP events on the launch stream around
-each step's block of decode calls and divided by the calls; `cpu_baseline`
-times the float64 CPU oracle on a bounded sample of the same workload on the
-host cores and checks the sampled GPU outputs against it.
+time of the K timed steps; TFLOP/s for prefill); `roofline` describes the
+attention call (split-K kernel + merge when split), timed with HIP events on
+the launch stream around each step's block of decode calls and divided by the
+calls; `cpu_baseline` times the float64 CPU oracle on whole layers of the same
+workload on the host cores (and one layer on one core), and `parity` gives the
+GPU outputs' errors against it over those layers.
 """
 import argparse
 import hashlib
@@ -374,13 +380,45 @@ class PrefillWorkload:
 
 
 # ---------------------------------------------------------------------------
-# CPU oracle baseline (bounded sample of the same workload)
+# CPU oracle: baseline timing and whole-layer parity (same device bytes)
 # ---------------------------------------------------------------------------
 
 _CPU = {}
 
 
-def _oracle_task(args):
+def cpu_workers() -> int:
+    """Worker processes for the oracle: every core this process may run on,
+    capped at OMP_NUM_THREADS when that is set (the GPU machine gives one GPU's
+    job a 16-thread share of its host and says so there; its affinity mask may
+    show more cores than that share)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host(t):
+    import torch
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _decode_task(args):
     layer, s = args
     import oracle
     from threadpoolctl import threadpool_limits
@@ -392,55 +430,134 @@ def _oracle_task(args):
     return layer, s, o
 
 
-def cpu_baseline(w: DecodeWorkload, sample_layers: int):
-    """Time the oracle over `sample_layers` layers x all sequences on a process
-    pool; return the baseline record and the max-abs error of the GPU outputs
-    on that sample."""
+def _prefill_task(s):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    w = _CPU
+    with threadpool_limits(limits=1):
+        o = oracle.prefill_one(w["q"], "bf16", w["cu"], w["ctx"], w["k"], w["v"], w["kind"], w["ks"], w["vs"],
+                               w["table"], w["n_q"], w["n_kv"], w["scale"], s, causal=True)
+    return s, o
+
+
+def _pool_map(fn, tasks, workers):
+    """fn over tasks on a fork pool of `workers` processes (in-process for
+    one worker); returns (results, wall seconds of the map)."""
     import multiprocessing as mp
-    import torch
-
-    def host(t):
-        if t is None:
-            return None
-        t = t.cpu()
-        if t.dtype == torch.bfloat16:
-            return t.view(torch.int16).numpy().view(np.uint16)
-        return t.numpy()
-
-    n = min(sample_layers, w.layers)
-    _CPU.clear()
-    _CPU.update(dict(q=[host(w.q[i]) for i in range(n)], k=[host(w.k[i]) for i in range(n)],
-                     v=[host(w.v[i]) for i in range(n)], ks=[host(w.ks[i]) for i in range(n)],
-                     vs=[host(w.vs[i]) for i in range(n)], table=w.block_table_np, lens=w.seq_lens,
-                     n_q=w.n_q, n_kv=w.n_kv, scale=w.scale, kind=w.kind,
-                     q_dtype="f32" if w.kind == "f32" else "bf16"))
-    gpu = [w.out[i].cpu().numpy().astype(np.float64) for i in range(n)]
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
-    tasks = [(i, s) for i in range(n) for s in range(w.batch)]
-    ctx = mp.get_context("fork")
-    with ctx.Pool(workers) as pool:
+    if workers <= 1:
         t0 = time.perf_counter()
-        res = pool.map(_oracle_task, tasks, chunksize=max(1, len(tasks) // (workers * 4)))
+        res = [fn(t) for t in tasks]
+        return res, time.perf_counter() - t0
+    with mp.get_context("fork").Pool(workers) as pool:
+        t0 = time.perf_counter()
+        res = pool.map(fn, tasks, chunksize=max(1, len(tasks) // (workers * 4)))
         dt = time.perf_counter() - t0
         pool.close()  # let the workers exit on their own rather than be terminated
         pool.join()
-    err = 0.0
+    return res, dt
+
+
+def _load_decode_layers(w, layers):
+    _CPU.clear()
+    _CPU.update(dict(q={i: _host(w.q[i]) for i in layers}, k={i: _host(w.k[i]) for i in layers},
+                     v={i: _host(w.v[i]) for i in layers}, ks={i: _host(w.ks[i]) for i in layers},
+                     vs={i: _host(w.vs[i]) for i in layers}, table=w.block_table_np, lens=w.seq_lens,
+                     n_q=w.n_q, n_kv=w.n_kv, scale=w.scale, kind=w.kind,
+                     q_dtype="f32" if w.kind == "f32" else "bf16"))
+
+
+def oracle_decode_layers(w, layers, workers=None):
+    """Oracle outputs of whole layers (every sequence, every query head),
+    computed from the bytes now in the device caches: {layer: [batch, n_q, d]
+    float64}, and the wall seconds of the oracle map."""
+    layers = list(layers)
+    _load_decode_layers(w, layers)
+    tasks = [(i, s) for i in layers for s in range(w.batch)]
+    res, dt = _pool_map(_decode_task, tasks, cpu_workers() if workers is None else workers)
+    outs = {i: np.zeros((w.batch, w.n_q, w.d)) for i in layers}
     for layer, s, o in res:
-        err = max(err, float(np.max(np.abs(gpu[layer][s] - o))))
+        outs[layer][s] = o
+    return outs, dt
+
+
+def _load_prefill(w):
+    _CPU.clear()
+    _CPU.update(dict(q=_host(w.q), cu=w.cu.cpu().numpy(), ctx=w.ctx, k=_host(w.k), v=_host(w.v), ks=_host(w.ks),
+                     vs=_host(w.vs), kind=w.kind, table=w.block_table.cpu().numpy(), n_q=w.n_q, n_kv=w.n_kv,
+                     scale=w.scale))
+
+
+def oracle_prefill_seqs(w, seqs, workers=None):
+    """Oracle outputs of whole sequences of the prefill chunk (every query
+    token and head), from the bytes now in the device cache (the chunk
+    appended): {seq: [q_len, n_q, d]}, and the wall seconds."""
+    _load_prefill(w)
+    res, dt = _pool_map(_prefill_task, list(seqs), cpu_workers() if workers is None else workers)
+    return dict(res), dt
+
+
+def parity_figures(got, want):
+    """max-abs error and the largest per-row relative rms error (rows: one
+    sequence or token and one head; rms(err) / rms(reference))."""
+    d = got - want
+    g = d.reshape(-1, d.shape[-1])
+    ref = want.reshape(-1, want.shape[-1])
+    den = np.sqrt(np.mean(ref ** 2, axis=1))
+    rel = np.sqrt(np.mean(g ** 2, axis=1))[den > 0] / den[den > 0]
+    return float(np.max(np.abs(d))), float(rel.max()) if rel.size else 0.0
+
+
+DEFAULT_CPU_LAYERS = {"tiny-f32": 1, "llama8b-bf16": 8, "llama70b-32k-bf16": 8, "llama70b-fp8-mix": 4}
+
+
+def cpu_baseline(w: DecodeWorkload, sample_layers: int = None):
+    """The oracle as it stands, timed on the host: whole layers (every
+    sequence and head) on a fork pool of cpu_workers() processes, plus one
+    whole layer on one core.  Returns the baseline record and the GPU-vs-oracle
+    error figures over the sampled layers."""
+    n = min(sample_layers or DEFAULT_CPU_LAYERS.get(w.name, 2), w.layers)
+    workers = cpu_workers()
+    layers = list(range(n))
+    outs, dt = oracle_decode_layers(w, layers, workers)
+    err = rel = 0.0
+    for i in layers:
+        e, r = parity_figures(w.out[i].cpu().numpy().astype(np.float64), outs[i])
+        err, rel = max(err, e), max(rel, r)
+    _, dt1 = oracle_decode_layers(w, [0], 1)
     nbytes = n * w.layer_bytes
-    cpu_model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
+    model = cpu_model()
     rec = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": workers, "kind": "oracle",
-           "sample": f"{n} layer(s) x {w.batch} sequences of the same workload (all query heads), float64 NumPy "
-                     f"oracle on a {workers}-process pool, {dt:.2f} s wall; {cpu_model}",
-           "seconds": round(dt, 3), "tokens_per_s_per_layer": round(w.batch * n / dt, 2)}
-    return rec, err
+           "sample": f"{n} whole layer(s) of the same workload ({w.batch} sequences, all {w.n_q} query heads), "
+                     f"float64 NumPy oracle on {workers} processes x 1 BLAS thread, {dt:.2f} s wall; one layer on "
+                     f"one core {dt1:.2f} s; CPU: {model}",
+           "seconds": round(dt, 3), "seconds_per_layer": round(dt / n, 3), "one_core_seconds_per_layer": round(dt1, 3),
+           "tokens_per_s_per_layer": round(w.batch * n / dt, 2), "cpu_model": model}
+    return rec, err, rel
+
+
+def cpu_baseline_prefill(w):
+    """The oracle on the whole prefill chunk (all 16 sequences, every token and
+    head) on cpu_workers() processes, and on one core for one sequence (the
+    median context).  Returns the record and the error figures of the GPU
+    output over the whole chunk."""
+    workers = cpu_workers()
+    seqs = list(range(len(w.ctx)))
+    outs, dt = oracle_prefill_seqs(w, seqs, workers)
+    got = w.out.cpu().numpy().astype(np.float64)
+    cu = w.cu.cpu().numpy()
+    want = np.concatenate([outs[s] for s in seqs])
+    err, rel = parity_figures(got[cu[0]:cu[-1]], want)
+    mid = int(np.argsort(w.ctx)[len(w.ctx) // 2])
+    _, dt1 = oracle_prefill_seqs(w, [mid], 1)
+    flops1 = prefill_flops([w.ctx[mid]], w.q_len, w.n_q, w.d)
+    model = cpu_model()
+    rec = {"value": round(w.flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+           "sample": f"the whole chunk ({len(seqs)} sequences x {w.q_len} tokens, all {w.n_q} query heads), float64 "
+                     f"NumPy oracle on {workers} processes x 1 BLAS thread, {dt:.2f} s wall; sequence {mid} "
+                     f"(context {int(w.ctx[mid])}) on one core {dt1:.2f} s; CPU: {model}",
+           "seconds": round(dt, 3), "one_core_seconds_one_sequence": round(dt1, 3),
+           "one_core_TFLOP/s": round(flops1 / dt1 / 1e12, 6), "cpu_model": model}
+    return rec, err, rel
 
 
 # ---------------------------------------------------------------------------
@@ -565,11 +682,17 @@ def swap_bench(cfg, args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 100 for the cold-cache tiny and prefill workloads, else 30)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama8b-bf16", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="llama70b-32k-bf16", choices=list(WORKLOADS))
     ap.add_argument("--layers", type=int, default=None, help="override the layer count (profiling only)")
-    ap.add_argument("--cpu-sample-layers", type=int, default=8)
+    ap.add_argument("--cpu-sample-layers", type=int, default=None,
+                    help="whole layers the CPU oracle runs on all cores (default by workload: 1 tiny, 8 for the 8B "
+                         "shape and the 70B 32K decode, 4 for the fp8 mix)")
+    ap.add_argument("--flush-mb", type=int, default=512,
+                    help="cold-cache protocol (tiny and prefill workloads): MiB written before every timed step, "
+                         "untimed, so no step finds the previous one's data in the L2 / last-level cache")
     ap.add_argument("--fp8-append", choices=["copy", "quantize"], default="copy",
                     help="FP8 workload: copy ready-made codes, or quantise bf16 rows on append")
     ap.add_argument("--swap-blocks", type=int, default=0,
@@ -615,6 +738,8 @@ def main():
 
     cfg = WORKLOADS[args.workload]
     prefill = synth.CONFIGS[cfg]["kind"] == "prefill"
+    if args.steps is None:
+        args.steps = 100 if (prefill or args.workload == "tiny-f32") else 30
     if args.swap_blocks:
         print(json.dumps(swap_bench(cfg, args)))
         return
@@ -634,33 +759,62 @@ def main():
             w.graph_step()
         step = w.graph_step
 
-    events = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(args.steps)]
+    # Tiny and prefill workloads use the cold-cache protocol: every timed step
+    # is preceded by an untimed write of --flush-mb MiB (more than the 256 MB
+    # last-level cache), the step is bracketed by events, and the median step
+    # and attention-call times are reported.  Their whole working set would
+    # otherwise stay cached from one step to the next.
+    cold = prefill or w.name == "tiny-f32"
+    flush = torch.empty(args.flush_mb << 18, dtype=torch.float32, device="cuda") if cold else None
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        if cold:
+            flush.fill_(float(k))
+            events[k][2].record()
         step(events[k])
+        if cold:
+            events[k][3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    call_ms = [e0.elapsed_time(e1) / w.calls_per_event for e0, e1 in events]
-    avg_call_s = float(np.mean(call_ms)) / 1e3
-    ms_per_step = wall / args.steps * 1e3
+    call_ms = [ev[0].elapsed_time(ev[1]) / w.calls_per_event for ev in events]
+    if cold:
+        step_ms = [ev[2].elapsed_time(ev[3]) for ev in events]
+        call_s = float(np.median(call_ms)) / 1e3
+        step_s = float(np.median(step_ms)) / 1e3
+        timing = (f"cold cache: {args.flush_mb} MiB written (untimed) before each of {args.steps} steps; medians of "
+                  f"HIP events around each step and each attention call")
+    else:
+        call_s = float(np.mean(call_ms)) / 1e3
+        step_s = wall / args.steps
+        timing = None
+    avg_call_s = call_s
+    ms_per_step = step_s * 1e3
 
     if prefill:
-        tflops = w.flops / (wall / args.steps) / 1e12
+        tflops = w.flops / step_s / 1e12
         achieved = w.flops / avg_call_s / 1e12
         rec = {"metric": "chunked prefill over a paged cache: achieved TFLOP/s (bf16 MFMA)", "value": round(tflops, 3),
                "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
                "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
-               "config": w.describe(),
+               "config": w.describe(), "timing": timing, "wall_s_with_flushes": round(wall, 4),
                "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                            "kernel": "prefill_kernel", "avg_call_us": round(avg_call_s * 1e6, 2)},
-               "new_tokens_per_s": round(len(w.ctx) * w.q_len / (wall / args.steps), 1)}
+                            "kernel": "prefill_kernel", "avg_call_us": round(avg_call_s * 1e6, 2),
+                            "flops_per_call": w.flops},
+               "new_tokens_per_s": round(len(w.ctx) * w.q_len / step_s, 1)}
+        print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (median)", file=sys.stderr, flush=True)
+        if not args.no_cpu_baseline:
+            base, err, rel = cpu_baseline_prefill(w)
+            rec["cpu_baseline"] = base
+            rec["parity"] = {"max_abs_err": err, "max_row_rel_err": rel,
+                             "over": "the whole chunk: every sequence, token and head"}
         print(json.dumps(rec))
         return
 
-    gbs = w.step_bytes / (wall / args.steps) / 1e9
+    gbs = w.step_bytes / step_s / 1e9
     achieved = w.layer_bytes / avg_call_s / 1e9
     traffic = traffic_from_profile(args.workload)
     rec = {"metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -669,18 +823,20 @@ def main():
            "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
            "config": w.describe(),
            "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-           "tokens_per_s_per_layer": round(w.batch / (wall / args.steps / w.layers), 1),
+           "tokens_per_s_per_layer": round(w.batch / (step_s / w.layers), 1),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                         "kernel": w.kernel_desc(),
-                        "timing": f"HIP events around each step's {w.layers} back-to-back decode calls"
-                                  + (" (replayed from a HIP graph)" if graphs else "") + f", / {w.layers}",
+                        "timing": timing or (f"HIP events around each step's {w.layers} back-to-back decode calls"
+                                             + (" (replayed from a HIP graph)" if graphs else "") + f", / {w.layers}"),
                         "avg_call_us": round(avg_call_s * 1e6, 3), "bytes_per_call": w.layer_bytes}}
     print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        base, err = cpu_baseline(w, args.cpu_sample_layers)
+        base, err, rel = cpu_baseline(w, args.cpu_sample_layers)
         rec["cpu_baseline"] = base
-        rec["sampled_parity_max_abs_err"] = err
+        n = min(args.cpu_sample_layers or DEFAULT_CPU_LAYERS.get(w.name, 2), w.layers)
+        rec["parity"] = {"max_abs_err": err, "max_row_rel_err": rel,
+                         "over": f"{n} whole layer(s): every sequence and query head"}
     print(json.dumps(rec))
 
 

@@ -13,8 +13,9 @@
  *    device; pointers marked (host) to host memory.  The caller owns every
  *    buffer, including workspaces, whose sizes the *_workspace() calls give.
  *    The library allocates no device memory and keeps no state between
- *    calls; the one exception is the host-side block pool object below,
- *    which the caller creates and destroys.
+ *    calls beyond cached device properties, the device-check switch and its
+ *    counter (a small file-scope device array per GPU); the host-side block
+ *    pool object below is created and destroyed by the caller.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it and the call returns without synchronising.
  *  - Cache layout, one layer: cache[num_blocks][n_kv_heads][block_size][d_head],
@@ -32,7 +33,8 @@
  *    the failure (thread-local).  Device data (block ids, lengths, slots) is
  *    not validated by the attention calls: ids outside [0, num_blocks) are
  *    clamped into the pool so no access leaves it, but such a result is
- *    meaningless; pkv_check_tables() validates tables on the device.
+ *    meaningless; pkv_set_device_checks() turns on a checked mode that
+ *    validates it on the device first (PKV_ERR_DEVICE_CHECK).
  *  - Slots past a sequence's length and blocks no table names may hold any
  *    bytes, NaN included; they never affect a result.
  */
@@ -46,7 +48,7 @@
 extern "C" {
 #endif
 
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 
 typedef enum {
   PKV_OK = 0,
@@ -54,7 +56,8 @@ typedef enum {
   PKV_ERR_UNSUPPORTED = 2, /* valid but not implemented (d_head, block_size, dtype combination) */
   PKV_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace() size */
   PKV_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
-  PKV_ERR_NO_BLOCKS = 5    /* a block pool has too few free blocks for the request */
+  PKV_ERR_NO_BLOCKS = 5,   /* a block pool has too few free blocks for the request */
+  PKV_ERR_DEVICE_CHECK = 6 /* device checks on: a length, block id or slot on the device is invalid */
 } pkv_status;
 
 /* Element types. FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN), with
@@ -65,6 +68,33 @@ int pkv_abi_version(void);
 const char* pkv_status_string(int status);
 /* Message for the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);
+
+/* Device checks (opt-in, for debugging; [FP] "Implementation" validates the
+ * inputs before the cache is mutated).  The attention and append calls do not
+ * read their device-resident inputs on the host, and their kernels do not
+ * validate them: block ids outside the pool are clamped into it, bad slots
+ * skipped, lengths capped at the table row, so a bad table gives a
+ * meaningless result, never an access outside the pool.  With checks on
+ * (process-wide switch, off by default), every call of pkv_kv_append,
+ * pkv_kv_append_fp8, the pkv_paged_attn_decode* and the
+ * pkv_paged_attn_prefill_chunk* calls first counts on the device, on the
+ * caller's stream:
+ *   - decode: seq_lens[s] < 0 or > the row's capacity (entries x B);
+ *   - prefill / fp8 append: context_lens[s] < 0, a new-token count < 0 or
+ *     above max_q_len / max_new_len, cu_*[0] != 0, cu_q_lens[num_seqs] !=
+ *     total_q, context + new tokens > the row's capacity;
+ *   - every table entry the request covers outside [0, num_blocks); CSR
+ *     offsets that decrease or do not start at 0;
+ *   - kv_append: a slot >= num_blocks * B (negative slots are padding);
+ * then waits for the stream (so calls are synchronous and cannot be captured
+ * into a graph) and, if anything was counted, returns PKV_ERR_DEVICE_CHECK
+ * without launching the call's work: nothing is changed.  The counter is a
+ * file-scope device array of the library, one per GPU; checks from several
+ * threads are serialised.  CSR offsets must still index kv_indices (the
+ * check reads the entries they name). */
+void pkv_set_device_checks(int enable);
+/* 1 if device checks are on, else 0. */
+int pkv_device_checks(void);
 
 /* Per-token KV-cache bytes: 2 (K and V) x n_layers x n_kv_heads x d_head x
  * bytes_per_value ([KVP] Problem 3, "The concepts"; [MEM] "KV cache sizing").
@@ -144,10 +174,6 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
                             const int32_t* seq_lens, const int64_t* cu_seq_lens, int64_t total_tokens,
                             int32_t batch, int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
 
-/* Device-side table check: counts, into *error_count (device int32, which the
- * caller zeroes first), every sequence with seq_lens[s] < 0 or
- * > max_blocks_per_seq * B and every table entry a sequence uses (logical
- * block < ceil(seq_len / B)) that lies outside [0, num_blocks). */
 /* Read probe, a measurement aid outside the attention path: the bandwidth a
  * plain kernel gets from HBM, to set beside the decode figures.  Reads the
  * device buffer buf (bytes, a multiple of 16) with 16-byte loads on
@@ -163,6 +189,12 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
 pkv_status pkv_read_probe(const void* buf, int64_t bytes, const int32_t* slab_list, int32_t n_list,
                           int32_t slab_bytes, int32_t workgroups, int32_t nontemporal, uint32_t* sink, void* stream);
 
+/* Device-side table check, asynchronous and for a 2-D table (the device
+ * checks above do the same per call, synchronously): counts, into
+ * *error_count (device int32, which the caller zeroes first), every sequence
+ * with seq_lens[s] < 0 or > max_blocks_per_seq * B and every table entry a
+ * sequence uses (logical block < ceil(seq_len / B)) that lies outside
+ * [0, num_blocks). */
 pkv_status pkv_check_tables(const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* seq_lens,
                             int32_t batch, int64_t num_blocks, int32_t block_size, int32_t* error_count,
                             void* stream);

@@ -28,7 +28,7 @@ pages print, closed forms, library routines and brute force on tiny inputs.
 from .codecs import bf16_bits_to_f64, e4m3fn_to_f64, f32_to_f64, decode_storage
 from .paging import (slot_of, slot_mapping, kv_append, gather_sequence, csr_pages,
                      kv_bytes_per_token, kv_bytes, waste_tokens)
-from .attention import (head_to_kv_head, softmax_attention_rows, paged_decode, paged_prefill,
+from .attention import (softmax_attention_rows, paged_decode, paged_prefill,
                         decode_one, prefill_one)
 from .sharing import BlockPool, PoolExhausted, copy_blocks
 from .quant import encode_e4m3fn, append_block_fp8, kv_append_fp8
@@ -38,7 +38,7 @@ __all__ = [
     "bf16_bits_to_f64", "e4m3fn_to_f64", "f32_to_f64", "decode_storage",
     "slot_of", "slot_mapping", "kv_append", "gather_sequence", "csr_pages",
     "kv_bytes_per_token", "kv_bytes", "waste_tokens",
-    "head_to_kv_head", "softmax_attention_rows", "paged_decode", "paged_prefill",
+    "softmax_attention_rows", "paged_decode", "paged_prefill",
     "decode_one", "prefill_one",
     "BlockPool", "PoolExhausted", "copy_blocks",
     "encode_e4m3fn", "append_block_fp8", "kv_append_fp8",

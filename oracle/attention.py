@@ -29,20 +29,12 @@ from .codecs import decode_storage
 from .paging import gather_sequence, gather_scales
 
 
-def head_to_kv_head(h: int, n_q: int, n_kv: int) -> int:
-    groups, remainder = divmod(n_q, n_kv)
-    if remainder or groups < 1:
-        raise ValueError("query heads must be a multiple of KV heads")
-    return h // groups
-
-
 def _check_heads(n_q: int, n_kv: int) -> int:
-    if n_kv < 1:
-        raise ValueError("need at least one KV head")
-    groups, remainder = divmod(n_q, n_kv)
-    if remainder or groups < 1:
-        raise ValueError("query heads must be a multiple of KV heads")
-    return groups
+    """Group size G = n_q / n_kv; every KV head must serve the same whole
+    number (at least one) of query heads, checked before any data is read."""
+    if n_kv < 1 or n_q < n_kv or n_q % n_kv != 0:
+        raise ValueError(f"{n_q} query heads cannot be split evenly over {n_kv} KV heads")
+    return n_q // n_kv
 
 
 def softmax_attention_rows(q_rows: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,

@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libpkv.so")
 _lib = None
 
 # status codes and element types (include/pkv.h)
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS = range(6)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_NO_BLOCKS, ERR_DEVICE_CHECK = range(7)
 F32, BF16, FP8_E4M3FN = 0, 1, 2
 
 _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -29,6 +29,8 @@ _SIGS = {
     "pkv_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pkv_last_error": ([], ctypes.c_char_p),
     "pkv_kv_bytes_per_token": ([_i32, _i32, _i32, _i32], _i64),
+    "pkv_set_device_checks": ([ctypes.c_int], None),
+    "pkv_device_checks": ([], ctypes.c_int),
     "pkv_slot_mapping": ([_vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_kv_append": ([_vp, _vp, ctypes.c_int, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
     "pkv_kv_append_fp8": ([_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_int, _i32,
@@ -111,6 +113,15 @@ def _check(status: int):
 
 def abi_version() -> int:
     return load().pkv_abi_version()
+
+
+def set_device_checks(enable: bool) -> None:
+    """Turn the library's device-data checks on or off (process-wide)."""
+    load().pkv_set_device_checks(1 if enable else 0)
+
+
+def device_checks() -> bool:
+    return bool(load().pkv_device_checks())
 
 
 def kv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, bytes_per_value: int) -> int:

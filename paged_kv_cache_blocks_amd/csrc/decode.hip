@@ -248,11 +248,16 @@ __device__ __forceinline__ void run_blocks(const DecodeArgs& a, int s, int kvh, 
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         kscale[2 * b + h] = vscale[2 * b + h] = 1.f;
+        // a half wholly past the range keeps scale 1: its block id may be a
+        // clamped or stale table entry whose scale is anything (NaN included),
+        // and its zero weights must not meet it
         if constexpr (KIND == KIND_FP8) {
-          kscale[2 * b + h] =
-              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.ks[h]), c * CB + b));
-          vscale[2 * b + h] =
-              __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.vs[h]), c * CB + b));
+          if (8 * (2 * b + h) < nvalid) {
+            kscale[2 * b + h] =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.ks[h]), c * CB + b));
+            vscale[2 * b + h] =
+                __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ids.vs[h]), c * CB + b));
+          }
         }
       }
 

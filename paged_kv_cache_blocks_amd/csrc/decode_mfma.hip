@@ -131,9 +131,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const int tok = p0 + kB * pb + 8 * h;
         const int id = page_block(a, pr, tok);
         my_row[h] = page_row_index(a, id, kvh, tok);
+        // a half wholly past the partition keeps scale 1: its table entry may
+        // be clamped or stale, its scale anything (NaN included), and the zero
+        // weights of its masked tokens must not meet it
         if constexpr (KIND == KIND_FP8) {
-          my_ks[h] = a.k_scale[(int64_t)id * a.n_kv + kvh];
-          my_vs[h] = a.v_scale[(int64_t)id * a.n_kv + kvh];
+          if (tok < p0 + plen) {
+            my_ks[h] = a.k_scale[(int64_t)id * a.n_kv + kvh];
+            my_vs[h] = a.v_scale[(int64_t)id * a.n_kv + kvh];
+          }
         }
       }
     }
@@ -363,18 +368,13 @@ static int mfma_wgs_per_cu() {
   return nwg > 0 ? nwg : 1;
 }
 
+// uncached: the C-ABI layer caches it per device
 int decode_mfma_wgs_per_cu(int kv_kind, int heads_per_wg) {
-  static int cache[3][17] = {};
-  int& c = cache[kv_kind][heads_per_wg];
-  if (c == 0) {
-    if (kv_kind == KIND_BF16)
-      c = heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_BF16, 16>()
-          : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_BF16, 8>() : mfma_wgs_per_cu<KIND_BF16, 4>();
-    else
-      c = heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_FP8, 16>()
-          : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_FP8, 8>() : mfma_wgs_per_cu<KIND_FP8, 4>();
-  }
-  return c;
+  if (kv_kind == KIND_BF16)
+    return heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_BF16, 16>()
+           : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_BF16, 8>() : mfma_wgs_per_cu<KIND_BF16, 4>();
+  return heads_per_wg == 16 ? mfma_wgs_per_cu<KIND_FP8, 16>()
+         : heads_per_wg == 8 ? mfma_wgs_per_cu<KIND_FP8, 8>() : mfma_wgs_per_cu<KIND_FP8, 4>();
 }
 
 template <int KIND>

@@ -1,13 +1,16 @@
 // C ABI of libpkv: argument validation, launch-shape choice, error reporting,
 // and the host-side block pool.  Every check runs before any launch, so a
-// failing call leaves the device untouched.  No device allocation; no global
-// state beyond the thread-local message.
+// failing call leaves the device untouched.  No device allocation.  State
+// beyond the thread-local message: cached device properties, the device-check
+// switch, and a small file-scope device array per GPU (the device-check
+// counter), located once per device.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <queue>
@@ -72,7 +75,7 @@ constexpr int kQueueSplit = -1;  // partition_tokens value that asks for the wor
 // heads ratio check, shared by the attention calls
 pkv_status check_heads(int32_t n_q, int32_t n_kv) {
   if (n_kv < 1 || n_q < 1) return fail(PKV_ERR_INVALID_ARG, "head counts must be positive (n_q=%d, n_kv=%d)", n_q, n_kv);
-  if (n_q % n_kv != 0) return fail(PKV_ERR_INVALID_ARG, "query heads must be a multiple of KV heads (n_q=%d, n_kv=%d)", n_q, n_kv);
+  if (n_q % n_kv != 0) return fail(PKV_ERR_INVALID_ARG, "%d query heads do not split evenly over %d KV heads", n_q, n_kv);
   return PKV_OK;
 }
 
@@ -89,43 +92,112 @@ struct DecodePlan {
   size_t ws_bytes;
 };
 
-// Compute units of the current device and workgroups of the work-queue decode
-// kernel per CU: fixed properties of the device and the code object, looked
-// up once per (device, kernel variant).
-int device_cus() {
-  static int cus[64] = {0};
+// Compute units of the current device and workgroups per CU of the decode
+// kernels: fixed properties of the device and the code object, looked up once
+// per (device, kernel variant).  Any thread may fill an entry; all compute the
+// same value, so a relaxed atomic load / store per entry is enough.
+constexpr int kMaxDevices = 64;
+using Cached = std::atomic<int>;
+
+int current_device() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+  return dev;
+}
+
+template <class F>
+int cached(Cached& slot, F compute) {
+  int v = slot.load(std::memory_order_relaxed);
+  if (v == 0) {
+    v = compute();
+    if (v > 0) slot.store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
+}
+
+int device_cus() {
+  static Cached cus[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  return cached(cus[dev], [dev] {
+    int n = 0;
+    return hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess ? n : 0;
+  });
 }
 
 int partition_wgs_per_cu(int kind, int d, int gw) {
-  static int cache[64][3][2][9] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& c = cache[dev][kind][d == 128][gw];
-  if (c == 0) c = pkv::decode_partition_wgs_per_cu(kind, d, gw);
-  return c;
+  static Cached cache[kMaxDevices][3][2][9];
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  return cached(cache[dev][kind][d == 128][gw], [&] { return pkv::decode_partition_wgs_per_cu(kind, d, gw); });
+}
+
+int mfma_wgs_per_cu(int kind, int gw) {
+  static Cached cache[kMaxDevices][3][17];
+  const int dev = current_device();
+  if (dev < 0) return 0;
+  return cached(cache[dev][kind][gw], [&] { return pkv::decode_mfma_wgs_per_cu(kind, gw); });
 }
 
 int queue_wgs_per_cu(int kind, int d, int gw, int batch) {
   // keyed by the batch rounded up to 256 sequences (1 KiB of prefix sums)
   constexpr int kBuckets = pkv::kDecodeMaxQueueBatch / 256;
-  static int cache[64][3][2][9][kBuckets] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static Cached cache[kMaxDevices][3][2][9][kBuckets];
+  const int dev = current_device();
+  if (dev < 0) return 0;
   const int bucket = (batch + 255) / 256 - 1;
-  int& c = cache[dev][kind][d == 128][gw][bucket];
-  if (c == 0) c = pkv::decode_queue_wgs_per_cu(kind, d, gw, (bucket + 1) * 256);
-  return c;
+  return cached(cache[dev][kind][d == 128][gw][bucket],
+                [&] { return pkv::decode_queue_wgs_per_cu(kind, d, gw, (bucket + 1) * 256); });
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// ---- opt-in device-data checks (pkv_set_device_checks) ----
+// The counter the check kernels add to: one int per GPU, in a file-scope
+// device array.  Its device address is looked up once per device with
+// hipGetSymbolAddress (the array's name is not a device address in host code).
+__device__ __align__(256) int32_t g_check_count[1];
+
+std::atomic<int> g_device_checks{0};
+std::mutex g_check_mu;                         // one check sequence at a time
+std::atomic<int32_t*> g_count_ptr[kMaxDevices];  // per device, once found
+
+pkv_status count_ptr(int32_t** out) {
+  const int dev = current_device();
+  if (dev < 0) return fail(PKV_ERR_HIP, "no HIP device for the device checks");
+  int32_t* p = g_count_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* addr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(g_check_count));
+    if (e != hipSuccess) return hip_status(e, "locating the device-check counter");
+    p = static_cast<int32_t*>(addr);
+    g_count_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return PKV_OK;
+}
+
+// Runs `launch_checks(counter)` on the stream between a clear of the counter
+// and a copy of it back, waits for the stream, and returns
+// PKV_ERR_DEVICE_CHECK if anything was counted.  Called before the checked
+// call launches its own work, so a failing call changes nothing.
+template <class F>
+pkv_status run_device_check(hipStream_t stream, const char* what, F launch_checks) {
+  std::lock_guard<std::mutex> lock(g_check_mu);
+  int32_t* cnt = nullptr;
+  pkv_status st = count_ptr(&cnt);
+  if (st != PKV_OK) return st;
+  hipError_t e = pkv::launch_zero_words(cnt, 1, stream);
+  if (e == hipSuccess) e = launch_checks(cnt);
+  int32_t host = 0;
+  if (e == hipSuccess) e = hipMemcpyAsync(&host, cnt, sizeof host, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "device check");
+  if (host != 0) return fail(PKV_ERR_DEVICE_CHECK, "%s: %d bad device entries (lengths, block ids or slots)", what, host);
+  return PKV_OK;
+}
+
+bool device_checks_on() { return g_device_checks.load(std::memory_order_relaxed) != 0; }
 
 pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int32_t max_blocks, int32_t block_size,
                        int kv_dtype, int32_t partition_tokens, DecodePlan* plan) {
@@ -154,15 +226,15 @@ pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int3
     // Fewest equal partitions of at most kMaxPartition tokens, but at least
     // enough that every resident workgroup slot gets a workgroup (a single
     // long sequence otherwise left most CUs idle).  The matrix-core kernel
-    // has no work-queue form.  Without a device the fill rule is skipped
-    // (sizes only).
+    // has no work-queue form.  The split depends on the device, so planning
+    // needs one.
     int64_t n_parts = (max_tokens + kMaxPartition - 1) / kMaxPartition;
     const int cus = device_cus();
-    if (cus > 0) {
-      const int64_t resident = (int64_t)cus * pkv::decode_mfma_wgs_per_cu(kv_dtype, gw);
-      const int64_t pairs = (int64_t)batch * hk;
-      n_parts = std::max<int64_t>(n_parts, std::min<int64_t>((resident + pairs - 1) / pairs, (max_tokens + 255) / 256));
-    }
+    const int per_cu = cus > 0 ? mfma_wgs_per_cu(kv_dtype, gw) : 0;
+    if (cus <= 0 || per_cu <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
+    const int64_t resident = (int64_t)cus * per_cu;
+    const int64_t pairs = (int64_t)batch * hk;
+    n_parts = std::max<int64_t>(n_parts, std::min<int64_t>((resident + pairs - 1) / pairs, (max_tokens + 255) / 256));
     // partitions in whole 32-token chunks, the matrix-core kernel's unit
     part = (int32_t)(((max_tokens + n_parts - 1) / n_parts + 31) / 32 * 32);
   } else if (part == 0) {
@@ -269,11 +341,16 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_NO_BLOCKS: return "PKV_ERR_NO_BLOCKS";
+    case PKV_ERR_DEVICE_CHECK: return "PKV_ERR_DEVICE_CHECK";
   }
   return "PKV_ERR_UNKNOWN";
 }
 
 const char* pkv_last_error(void) { return g_err; }
+
+void pkv_set_device_checks(int enable) { g_device_checks.store(enable ? 1 : 0, std::memory_order_relaxed); }
+
+int pkv_device_checks(void) { return device_checks_on() ? 1 : 0; }
 
 int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head, int32_t bytes_per_value) {
   if (n_layers < 0 || n_kv_heads < 0 || d_head < 0 || bytes_per_value < 0) return -1;
@@ -305,6 +382,12 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
     return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
   const int row_bytes = d_head * elem_bytes(cache_dtype);
   if (row_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "a row of %d bytes is not a multiple of 16", row_bytes);
+  if (device_checks_on()) {
+    const pkv_status st = run_device_check((hipStream_t)stream, "kv_append", [&](int32_t* cnt) {
+      return pkv::launch_check_slots(slot_mapping, num_tokens, num_blocks * block_size, cnt, (hipStream_t)stream);
+    });
+    if (st != PKV_OK) return st;
+  }
   return hip_status(pkv::launch_kv_append(k_cache, v_cache, num_blocks, slot_mapping, k, v, num_tokens, n_kv_heads,
                                           row_bytes, block_size, (hipStream_t)stream),
                     "kv_append launch");
@@ -331,6 +414,14 @@ pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float
   if (batch > 65535 || 2 * n_kv_heads > 65535) return fail(PKV_ERR_UNSUPPORTED, "grid too large");
   if (((uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)k_new | (uintptr_t)v_new) & 15)
     return fail(PKV_ERR_UNSUPPORTED, "caches and new K/V must be 16-byte aligned");
+  if (device_checks_on()) {
+    pkv::SeqCheck c{block_table, nullptr, context_lens, cu_new_lens, num_blocks, max_blocks_per_seq, batch, log2_bs,
+                    pkv::SeqCheck::kAppend, max_new_len, 0};
+    const pkv_status st = run_device_check((hipStream_t)stream, "kv_append_fp8", [&](int32_t* cnt) {
+      return pkv::launch_check_seqs(c, cnt, (hipStream_t)stream);
+    });
+    if (st != PKV_OK) return st;
+  }
   return hip_status(pkv::launch_kv_append_fp8(k_cache, v_cache, k_scale, v_scale, num_blocks, block_table,
                                               max_blocks_per_seq, context_lens, cu_new_lens, batch, max_new_len,
                                               k_new, v_new, new_dtype == PKV_BF16 ? 2 : 4, n_kv_heads, d_head,
@@ -579,6 +670,14 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
   a.n_parts = plan.n_parts;
   a.out_bf16 = out_dtype == PKV_BF16;
   a.scale_log2 = scale * kLog2e;
+  if (device_checks_on()) {
+    pkv::SeqCheck c{block_table, indptr, seq_lens, nullptr, num_blocks, max_blocks_per_seq, batch, log2_bs,
+                    pkv::SeqCheck::kDecode, 0, 0};
+    st = run_device_check((hipStream_t)stream, "decode", [&](int32_t* cnt) {
+      return pkv::launch_check_seqs(c, cnt, (hipStream_t)stream);
+    });
+    if (st != PKV_OK) return st;
+  }
   return hip_status(pkv::launch_decode(a, (int)kv_dtype, d_head, (hipStream_t)stream), "decode launch");
 }
 
@@ -632,8 +731,7 @@ pkv_status pkv_paged_attn_decode_order(const int32_t* seq_lens, int32_t batch, i
     const int cus = device_cus();
     if (cus <= 0) return fail(PKV_ERR_HIP, "no HIP device to plan the decode launch for");
     const int gw = (n_q_heads / n_kv_heads) / plan.head_chunks;
-    const int per_cu = plan.use_mfma ? pkv::decode_mfma_wgs_per_cu(kv_dtype, gw)
-                                     : partition_wgs_per_cu(kv_dtype, d_head, gw);
+    const int per_cu = plan.use_mfma ? mfma_wgs_per_cu(kv_dtype, gw) : partition_wgs_per_cu(kv_dtype, d_head, gw);
     const int64_t wgs = (int64_t)batch * n_kv_heads * plan.head_chunks * plan.n_parts;
     pair = wgs <= (int64_t)cus * per_cu ? 1 : 0;
   }
@@ -745,6 +843,14 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype
   a.out_bf16 = out_dtype == PKV_BF16;
   a.kv_fp8 = kv_dtype == PKV_FP8_E4M3FN;
   a.scale_log2 = scale * kLog2e;
+  if (device_checks_on()) {
+    pkv::SeqCheck c{block_table, indptr, context_lens, cu_q_lens, num_blocks, max_blocks_per_seq, num_seqs, log2_bs,
+                    pkv::SeqCheck::kPrefill, max_q_len, total_q};
+    st = run_device_check((hipStream_t)stream, "prefill", [&](int32_t* cnt) {
+      return pkv::launch_check_seqs(c, cnt, (hipStream_t)stream);
+    });
+    if (st != PKV_OK) return st;
+  }
   return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
 }
 

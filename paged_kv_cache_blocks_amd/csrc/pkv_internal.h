@@ -96,6 +96,27 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, const int32_t* slab
 hipError_t launch_check_tables(const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, int32_t batch,
                                int64_t num_blocks, int32_t block_size, int32_t* err, hipStream_t stream);
 
+// Device-data check of one call's sequences (device_check.hip): each
+// sequence's request must fit its table row and every entry it covers must
+// name a pool block.
+struct SeqCheck {
+  enum Mode : int32_t { kDecode = 0, kPrefill = 1, kAppend = 2 };
+  const int32_t* table;   // 2-D [batch][max_blocks], or CSR page ids
+  const int32_t* indptr;  // CSR offsets [batch + 1], or null
+  const int32_t* lens;    // decode: seq_lens; prefill / append: context lengths
+  const int32_t* cu;      // prefill / append: new-token offsets [batch + 1]
+  int64_t num_blocks;
+  int32_t max_blocks;
+  int32_t batch;
+  int32_t log2_bs;
+  int32_t mode;
+  int32_t max_new;        // prefill: max_q_len; append: max_new_len
+  int32_t total;          // prefill: total_q (cu[batch] must equal it)
+};
+hipError_t launch_check_seqs(const SeqCheck& c, int32_t* err, hipStream_t stream);
+hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t limit, int32_t* err, hipStream_t stream);
+hipError_t launch_zero_words(int32_t* p, int32_t n, hipStream_t stream);
+
 struct PrefillArgs {
   void* out;
   const void* q;

@@ -63,10 +63,12 @@ static_assert(STAGE_B + 2 * STG8_B <= kStages * STAGE_B, "FP8 tile + staging mus
 // LDS bytes such a load writes, would otherwise wait for it before every later
 // LDS read, including reads of the other stage, and expose the load latency on
 // every tile.  The caller waits for these loads itself (vmcnt) before the
-// barrier that hands the stage to the readers.  The compiler keeps nothing in
+// barrier that hands the stage to the readers.  An LDS-DMA load needs one wait
+// state after a scalar write of M0; the compiler inserts it for loads it
+// generates but cannot see into this string, hence the s_nop.  The compiler keeps nothing in
 // M0 across these statements in this kernel (checked in its assembly).
 __device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
@@ -150,11 +152,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int q_len = min(a.cu_q[s + 1], a.total_q) - qs;
   if (q0 >= q_len) return;
   const PageRow prow = page_row(a, s);
-  const int ctx = min(max(a.ctx_lens[s], 0), prow.n << a.log2_bs);  // keeps every tile inside the table
-  const int total = ctx + q_len;        // keys that exist for this sequence
+  // context and keys are capped at the table row's capacity, so no tile
+  // reaches past the row (callers keep ctx + q_len within it)
+  const int cap = prow.n << a.log2_bs;
+  const int ctx = min(max(a.ctx_lens[s], 0), cap);
+  const int total = min(ctx + q_len, cap);  // keys that exist for this sequence
   const int last_q = min(q0 + tq, q_len) - 1;
   // keys any row of the tile sees (none when the table row is empty)
-  const int kv_end = prow.n == 0 ? 0 : a.causal ? ctx + last_q + 1 : total;
+  const int kv_end = prow.n == 0 ? 0 : a.causal ? min(ctx + last_q + 1, total) : total;
   const int n_tiles = (kv_end + KT - 1) / KT;
   const int diag0 = ctx + q0;           // keys >= diag0 are masked for some row
 
@@ -170,7 +175,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const int tok = q0 + r / G;
     row_tok[nt] = tok;
     row_head[nt] = kvh * G + r % G;
-    row_lim[nt] = a.causal ? ctx + tok : total - 1;  // last visible key
+    row_lim[nt] = a.causal ? min(ctx + tok, total - 1) : total - 1;  // last visible key
     const bool ok = tok < q_len;
     const char* qrow = reinterpret_cast<const char*>(a.q) +
                        ((int64_t)(qs + (ok ? tok : 0)) * a.n_q + row_head[nt]) * D * 2;
@@ -246,10 +251,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         lds_dma16(kc + half[k], 16 * lane, dst + k * 1024);
         lds_dma16(vc + half[k], 16 * lane, dst + BLK8_B + k * 1024);
       }
+      // a half wholly past the keys the workgroup sees keeps scale 0: its
+      // table entry may be clamped or stale and its scale anything (NaN
+      // included), which the zero weights of its masked keys must not meet
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        ks_load[h] = a.k_scale[(int64_t)id[h] * a.n_kv + kvh];
-        vs_load[h] = a.v_scale[(int64_t)id[h] * a.n_kv + kvh];
+        const bool live = lb * BS + 8 * h < kv_end;
+        ks_load[h] = live ? a.k_scale[(int64_t)id[h] * a.n_kv + kvh] : 0.f;
+        vs_load[h] = live ? a.v_scale[(int64_t)id[h] * a.n_kv + kvh] : 0.f;
       }
     } else {
       const uint32_t dst = lds0 + (kt % kStages) * STAGE_B;

@@ -71,7 +71,7 @@ def test_decode_validation_before_launch(pkv):
     lib = pkv.load()
     # the head ratio is checked first ("validate before mutate")
     assert _decode(lib, n_q=6, n_kv=4, out=None) == pkv.ERR_INVALID_ARG
-    assert b"multiple of KV heads" in lib.pkv_last_error()
+    assert b"do not split evenly" in lib.pkv_last_error()
     assert _decode(lib, n_kv=0) == pkv.ERR_INVALID_ARG
     assert _decode(lib, q=None) == pkv.ERR_INVALID_ARG
     assert _decode(lib, d=96) == pkv.ERR_UNSUPPORTED
@@ -148,17 +148,20 @@ def test_work_order_entry_points_validate(pkv):
     assert lib.pkv_paged_attn_decode_ordered(*args) == pkv.ERR_INVALID_ARG   # no order
 
 
-def test_work_order_entries(pkv):
-    """Size of the work order: one entry per sequence when each sequence is one
-    partition, one per (sequence, partition) unit when the matrix-core split
-    cuts sequences into several (without a device the split is planned from
-    the sizes alone); 0 for invalid arguments."""
+def test_work_order_entries_need_a_device(pkv):
+    """The matrix-core split (bf16 / fp8 KV at d 128) is planned against the
+    device's resident workgroups, so without a device the order size (and the
+    workspace size) is 0 rather than a guess; invalid arguments give 0 too.
+    The sizes themselves are checked on the GPU (test_gpu_work_order.py)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: the GPU test checks the sizes")
     lib = pkv.load()
-    assert lib.pkv_paged_attn_decode_order_entries(64, 32, 8, 128, 128, 16, pkv.BF16) == 64          # 2048 tokens
-    assert lib.pkv_paged_attn_decode_order_entries(256, 64, 8, 128, 512, 16, pkv.FP8_E4M3FN) == 512  # 8192: 2 parts
-    assert lib.pkv_paged_attn_decode_order_entries(8, 64, 8, 128, 2048, 16, pkv.BF16) == 64          # 32768: 8 parts
-    assert lib.pkv_paged_attn_decode_order_entries(2048, 64, 8, 128, 512, 16, pkv.BF16) == 4096     # 2 parts
-    assert lib.pkv_paged_attn_decode_order_entries(8192, 64, 8, 128, 512, 16, pkv.BF16) == 8192     # > 8192 units
+    assert lib.pkv_paged_attn_decode_order_entries(64, 32, 8, 128, 128, 16, pkv.BF16) == 0
+    assert lib.pkv_paged_attn_decode_order_entries(256, 64, 8, 128, 512, 16, pkv.FP8_E4M3FN) == 0
+    assert lib.pkv_paged_attn_decode_workspace(8, 64, 8, 128, 2048, 16, pkv.BF16, 0) == 0
+    info = (ctypes.c_int32 * 7)()
+    assert lib.pkv_paged_attn_decode_plan(8, 64, 8, 128, 2048, 16, pkv.BF16, 0, info) == pkv.ERR_HIP
     assert lib.pkv_paged_attn_decode_order_entries(4, 6, 4, 128, 8, 16, pkv.BF16) == 0              # head ratio
     assert lib.pkv_paged_attn_decode_order_entries(4, 8, 2, 96, 8, 16, pkv.BF16) == 0               # d_head
 

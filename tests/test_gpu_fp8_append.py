@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, dev, err_report, note
+from gpu_util import assert_parity, dev, note
 
 pytestmark = pytest.mark.gpu
 
@@ -190,7 +190,7 @@ def test_chunked_appends_then_decode(pkv, kind):
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     want = oracle.paged_decode(q, "bf16", k, v, "fp8", ks, vs, table, lens, n_q, n_kv, scale)
-    assert np.allclose(got, want, rtol=TOL["fp8"], atol=TOL["fp8"]), err_report(got, want)
+    assert_parity(got, want, "fp8")
 
 
 def test_skips_and_noops(pkv):

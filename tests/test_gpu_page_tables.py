@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, dev, err_report, host_bits, note, oracle_decode, run_decode
+from gpu_util import assert_parity, dev, host_bits, note, oracle_decode, run_decode
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -38,8 +38,7 @@ def test_decode_block_sizes(pkv, kind, d, n_q, n_kv, B):
     note(f"decode {kind} d={d} {n_q}q/{n_kv}kv B={B}")
     got = run_decode(pkv, c)
     want = oracle_decode(c)
-    rep = err_report(got, want)
-    assert np.allclose(got, want, rtol=TOL[kind], atol=TOL[kind]), rep
+    assert_parity(got, want, kind)
 
 
 @pytest.mark.parametrize("B", [8, 64])
@@ -50,7 +49,7 @@ def test_decode_queue_split_block_sizes(pkv, kind, d, n_q, n_kv, B):
     note(f"decode queue split {kind} d={d} B={B}")
     got = run_decode(pkv, c, partition_tokens=-1)
     want = oracle_decode(c)
-    assert np.allclose(got, want, rtol=TOL[kind], atol=TOL[kind]), err_report(got, want)
+    assert_parity(got, want, kind)
 
 
 def _scatter(rows_per_seq, B, perm):
@@ -116,7 +115,7 @@ def test_prefill_block_sizes(pkv, kind, B):
     got = out.cpu().numpy().astype(np.float64)
     want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, p.k_cache, p.v_cache, kind, p.k_scale,
                                 p.v_scale, p.block_table, p.n_q, p.n_kv, p.scale, causal=True)
-    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= TOL[kind], err_report(got, want)
+    assert_parity(got, want, kind)
 
 
 @pytest.mark.parametrize("B", [8, 64, 256])
@@ -217,7 +216,7 @@ def test_csr_pages_example(pkv):
     assert np.array_equal(table.cpu().numpy(), want_table)
     want = oracle.paged_decode(q, "bf16", k, v, "bf16", None, None, rows, lens, n_q, n_kv, scale)
     g64 = got.cpu().numpy().astype(np.float64)
-    assert np.allclose(g64, want, rtol=TOL["bf16"], atol=TOL["bf16"]), err_report(g64, want)
+    assert_parity(g64, want, "bf16")
     assert np.array_equal(got.cpu().numpy().view(np.uint32), via_table.cpu().numpy().view(np.uint32))
     # prefill: the last 5 tokens of each request are the chunk
     ql = np.minimum(5, lens).astype(np.int32)
@@ -229,7 +228,7 @@ def test_csr_pages_example(pkv):
     torch.cuda.synchronize()
     wantp = oracle.paged_prefill(qp, "bf16", cu, ctx, k, v, "bf16", None, None, rows, n_q, n_kv, scale, causal=True)
     gp = out.cpu().numpy().astype(np.float64)
-    assert np.max(np.abs(gp - wantp)) <= TOL["bf16"], err_report(gp, wantp)
+    assert_parity(gp, wantp, "bf16")
 
 
 @pytest.mark.parametrize("B", [8, 32])
@@ -249,5 +248,5 @@ def test_csr_random_fp8(pkv, B):
     got = out.cpu().numpy().astype(np.float64)
     want = oracle.paged_decode(c.q, "bf16", c.k_cache, c.v_cache, "fp8", c.k_scale, c.v_scale, rows, c.seq_lens,
                                c.n_q, c.n_kv, c.scale)
-    assert np.allclose(got, want, rtol=TOL["fp8"], atol=TOL["fp8"]), err_report(got, want)
+    assert_parity(got, want, "fp8")
     assert np.all(got[0] == 0)

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import TOL, dev, err_report, host_bits, note
+from gpu_util import assert_parity, dev, host_bits, note
 
 pytestmark = pytest.mark.gpu
 
@@ -44,9 +44,7 @@ def test_prefill_ragged(pkv, causal, n_q, n_kv):
     note(f"prefill n_q={n_q} n_kv={n_kv} causal={causal}")
     got = _run(pkv, p, causal)
     want = _oracle(p, causal)
-    rep = err_report(got, want)
-    note("  " + rep)
-    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= 1e-2, rep
+    assert_parity(got, want, "bf16")
 
 
 def test_prefill_chunk_of_one_matches_decode(pkv):
@@ -76,9 +74,7 @@ def test_append_then_attend(pkv):
     assert np.array_equal(host_bits(kc), full.k_cache) and np.array_equal(host_bits(vc), full.v_cache)
     got = _run(pkv, p, k_cache=kc, v_cache=vc)
     want = _oracle(full)
-    rep = err_report(got, want)
-    note("  " + rep)
-    assert np.max(np.abs(got - want)) <= 1e-2, rep
+    assert_parity(got, want, "bf16")
 
 
 def test_prefill_bf16_output(pkv):
@@ -107,9 +103,7 @@ def test_prefill_wide_score_range(pkv, causal):
     note(f"prefill wide score range causal={causal}")
     got = _run(pkv, p, causal)
     want = _oracle(p, causal)
-    rep = err_report(got, want)
-    note("  " + rep)
-    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= 1e-2, rep
+    assert_parity(got, want, "bf16")
 
 
 def test_prefill_sequence_without_new_tokens(pkv):
@@ -120,7 +114,7 @@ def test_prefill_sequence_without_new_tokens(pkv):
     got = _run(pkv, p)
     want = _oracle(p)
     assert got.shape[0] == 53
-    assert np.max(np.abs(got - want)) <= 1e-2, err_report(got, want)
+    assert_parity(got, want, "bf16")
 
 
 # ---- FP8 KV (codes widened to bf16 in LDS, per-block K/V scales)
@@ -148,9 +142,7 @@ def test_prefill_fp8_ragged(pkv, causal, n_q, n_kv):
     got = _run_fp8(pkv, p, causal)
     want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, p.k_cache, p.v_cache, "fp8", p.k_scale,
                                 p.v_scale, p.block_table, p.n_q, p.n_kv, p.scale, causal=causal)
-    rep = err_report(got, want)
-    note("  " + rep)
-    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= TOL["fp8"], rep
+    assert_parity(got, want, "fp8")
 
 
 def test_fp8_append_then_prefill(pkv):
@@ -182,6 +174,4 @@ def test_fp8_append_then_prefill(pkv):
     got = _run_fp8(pkv, p, True, tk, tv, tks, tvs)
     want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, k, v, "fp8", ks, vs, p.block_table, p.n_q,
                                 p.n_kv, p.scale, causal=True)
-    rep = err_report(got, want)
-    note("  " + rep)
-    assert np.all(np.isfinite(got)) and np.max(np.abs(got - want)) <= TOL["fp8"], rep
+    assert_parity(got, want, "fp8")

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import dev, note, oracle_decode, run_decode
+from gpu_util import assert_parity, dev, note, oracle_decode, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +100,7 @@ def test_preempt_and_restore_decodes_the_same_bits(pkv, kind):
     after = run_decode(pkv, c, t)
     assert np.array_equal(before.view(np.uint64), after.view(np.uint64))
     want = oracle_decode(c)
-    assert np.allclose(after, want, rtol=5e-2, atol=5e-2)
+    assert_parity(after, want, c.kv_dtype)
 
 
 def test_swap_in_skips_ids_outside_the_pool(pkv):

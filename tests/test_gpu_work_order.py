@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from gpu_util import dev, note, oracle_decode, upload_decode, TOL
+from gpu_util import assert_parity, dev, note, oracle_decode, upload_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +80,7 @@ def test_ordered_decode_is_bit_identical(pkv, kind, d, n_q, n_kv):
     want = oracle_decode(c)
     assert np.array_equal(plain.view(np.uint32), ordered.view(np.uint32))  # same split, same bits
     for got in (plain, ordered):
-        assert np.allclose(got.astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
+        assert_parity(got.astype(np.float64), want, kind)
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
@@ -98,4 +98,17 @@ def test_single_long_sequence_fills_the_device(pkv, kind):
                                 c.scale, k_scale=t["k_scale"], v_scale=t["v_scale"])
     torch.cuda.synchronize()
     want = oracle_decode(c)
-    assert np.allclose(out.cpu().numpy().astype(np.float64), want, rtol=TOL[kind], atol=TOL[kind])
+    assert_parity(out.cpu().numpy().astype(np.float64), want, kind, "20000 tokens")
+
+
+def test_work_order_entries(pkv):
+    """Size of the work order on the device: one entry per sequence when each
+    sequence is one partition, one per (sequence, partition) unit when the
+    matrix-core split cuts sequences into several (up to 8192 units)."""
+    lib = pkv.load()
+    assert lib.pkv_paged_attn_decode_order_entries(64, 32, 8, 128, 128, 16, pkv.BF16) == 64          # 2048 tokens
+    assert lib.pkv_paged_attn_decode_order_entries(256, 64, 8, 128, 512, 16, pkv.FP8_E4M3FN) == 512  # 8192: 2 parts
+    assert lib.pkv_paged_attn_decode_order_entries(8, 64, 8, 128, 2048, 16, pkv.BF16) == 64          # 32768: 8 parts
+    assert lib.pkv_paged_attn_decode_order_entries(2048, 64, 8, 128, 512, 16, pkv.BF16) == 4096     # 2 parts
+    assert lib.pkv_paged_attn_decode_order_entries(8192, 64, 8, 128, 512, 16, pkv.BF16) == 8192     # > 8192 units
+    assert lib.pkv_paged_attn_decode_order_entries(4, 6, 4, 128, 8, 16, pkv.BF16) == 0              # head ratio
