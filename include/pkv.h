@@ -359,6 +359,30 @@ pkv_status pkv_paged_attn_decode_partitioned(void* out, pkv_dtype out_dtype, con
                                              int32_t block_size, float scale, int32_t partition_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Decode for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): as
+ * pkv_paged_attn_decode_partitioned (partition_tokens: 0 = the library's
+ * split, > 0 fixed partitions, -1 the work-queue split), without a workspace
+ * argument.  The partial results of a split call (and the work-queue split's
+ * item counter) go to a static scratch array of the library, 32 MiB in each
+ * GPU's memory, held from the call's first use on that GPU until the process
+ * ends; this call allocates nothing.  A decode whose workspace
+ * (pkv_paged_attn_decode_workspace) exceeds 32 MiB fails with
+ * PKV_ERR_WORKSPACE before any launch (the 70B-shaped 32K decode needs about
+ * 2 MB, batch 256 of 8192 tokens with 64 query heads about 17 MB).  Every
+ * call on one GPU shares that GPU's scratch, which keeps the last call's
+ * bytes (the item counter is cleared by each call): two such calls whose
+ * work overlaps in time on one GPU (different streams, or threads) race and
+ * give wrong results; order them on one stream.  Results equal
+ * pkv_paged_attn_decode_partitioned's bit for bit.  Other arguments and
+ * errors as pkv_paged_attn_decode. */
+pkv_status pkv_paged_attn_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                         const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                         int32_t block_size, float scale, int32_t partition_tokens, void* stream);
+
 /* Workspace bytes the decode call needs on the current device (partition_tokens
  * as above, 0 = the library's choice).  Returns 0 for invalid arguments, or
  * when the split depends on the device and no device is present. */

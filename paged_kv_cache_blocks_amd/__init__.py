@@ -45,6 +45,8 @@ _SIGS = {
     "pkv_paged_attn_decode_partitioned": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                            _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp],
                                           ctypes.c_int),
+    "pkv_paged_attn_decode_noalloc": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                       _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _i32, _vp], ctypes.c_int),
     "pkv_paged_attn_decode_ordered": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
                                        _i32, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _sz, _vp],
                                       ctypes.c_int),
@@ -388,6 +390,22 @@ def paged_attn_decode(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_k
         _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
         _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), batch, nb, n_q_heads,
         n_kv_heads, d_head, block_size, float(scale), int(partition_tokens), ws_ptr, ws_n, _stream(stream)))
+    return out
+
+
+def paged_attn_decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, n_q_heads, n_kv_heads, d_head, block_size,
+                              scale, *, out, k_scale=None, v_scale=None, partition_tokens: int = 0,
+                              stream=None) -> torch.Tensor:
+    """paged_attn_decode without a workspace: the library's static device
+    scratch holds the split's partial results (pkv_paged_attn_decode_noalloc).
+    `out` must be given: nothing is allocated."""
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_lens, torch.int32, "seq_lens")
+    _check(load().pkv_paged_attn_decode_noalloc(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], _ptr(seq_lens), q.shape[0],
+        k_cache.shape[0], n_q_heads, n_kv_heads, d_head, block_size, float(scale), int(partition_tokens),
+        _stream(stream)))
     return out
 
 

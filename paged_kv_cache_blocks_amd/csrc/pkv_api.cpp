@@ -199,6 +199,35 @@ pkv_status run_device_check(hipStream_t stream, const char* what, F launch_check
 
 bool device_checks_on() { return g_device_checks.load(std::memory_order_relaxed) != 0; }
 
+// ---- decode without a caller workspace (pkv_paged_attn_decode_noalloc) ----
+// The split kernels' partial results, and the work-queue split's counter, go
+// to this file-scope device array instead of a caller's workspace: 32 MiB per
+// GPU, held until the process ends (the 70B-shaped 32K decode needs 2.1 MB,
+// the fp8 serving mix 17 MB).  Host code never passes the array's name to a
+// kernel: its device address is looked up once per device.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+pkv_status scratch_ptr(void** out) {
+  const int dev = current_device();
+  if (dev < 0) return fail(PKV_ERR_HIP, "no HIP device for the static scratch");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      // with device `dev` current: its own copy of the array
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "locating the static scratch");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PKV_OK;
+}
+
 pkv_status plan_decode(int32_t batch, int32_t n_q, int32_t n_kv, int32_t d, int32_t max_blocks, int32_t block_size,
                        int kv_dtype, int32_t partition_tokens, DecodePlan* plan) {
   pkv_status st = check_heads(n_q, n_kv);
@@ -600,7 +629,8 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
                        const int32_t* block_table, const int32_t* indptr, int32_t max_blocks_per_seq,
                        const int32_t* seq_lens, int32_t batch, int64_t num_blocks, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t d_head, int32_t block_size, float scale, int32_t partition_tokens,
-                       const int32_t* work_order, void* workspace, size_t workspace_bytes, void* stream) {
+                       const int32_t* work_order, void* workspace, size_t workspace_bytes, void* stream,
+                       bool static_scratch = false) {
   // head ratio first, before anything else (validate before mutate)
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
   if (st != PKV_OK) return st;
@@ -630,6 +660,14 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
   if (st != PKV_OK) return st;
   if (batch > 65535 || (int64_t)batch * n_kv_heads * plan.head_chunks > 0x7fffffff)
     return fail(PKV_ERR_UNSUPPORTED, "grid too large");
+  if (static_scratch && plan.ws_bytes > 0) {
+    if (plan.ws_bytes > kScratchBytes)
+      return fail(PKV_ERR_WORKSPACE, "this decode needs %zu bytes of workspace; the library's static scratch holds %zu",
+                  plan.ws_bytes, kScratchBytes);
+    st = scratch_ptr(&workspace);
+    if (st != PKV_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (plan.ws_bytes > 0) {
     if (!workspace || workspace_bytes < plan.ws_bytes)
       return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws_bytes,
@@ -677,6 +715,13 @@ pkv_status decode_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype 
       return pkv::launch_check_seqs(c, cnt, (hipStream_t)stream);
     });
     if (st != PKV_OK) return st;
+  }
+  if (static_scratch && plan.n_wg) {
+    // the scratch keeps the previous call's bytes: the work-queue split's item
+    // counter must start at zero (a kernel, not a memset, so that captured
+    // streams record a kernel node)
+    const hipError_t e = pkv::launch_zero_words(reinterpret_cast<int32_t*>(a.dyn_counter), 1, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "scratch counter clear");
   }
   return hip_status(pkv::launch_decode(a, (int)kv_dtype, d_head, (hipStream_t)stream), "decode launch");
 }
@@ -772,6 +817,17 @@ pkv_status pkv_paged_attn_decode(void* out, pkv_dtype out_dtype, const void* q, 
                                            block_table, max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads,
                                            n_kv_heads, d_head, block_size, scale, 0, workspace, workspace_bytes,
                                            stream);
+}
+
+pkv_status pkv_paged_attn_decode_noalloc(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                         const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                         const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                         int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                                         int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
+                                         int32_t block_size, float scale, int32_t partition_tokens, void* stream) {
+  return decode_impl(out, out_dtype, q, q_dtype, k_cache, v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr,
+                     max_blocks_per_seq, seq_lens, batch, num_blocks, n_q_heads, n_kv_heads, d_head, block_size,
+                     scale, partition_tokens, nullptr, nullptr, 0, stream, true);
 }
 
 size_t pkv_paged_attn_prefill_workspace(int32_t num_seqs, int32_t max_q_len, int32_t n_q_heads, int32_t d_head) {
