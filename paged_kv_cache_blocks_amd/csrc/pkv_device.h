@@ -192,4 +192,28 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// ---- direct global -> LDS loads (prefill kernels) ----
+// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4, scalar-base form: address = base + off, with the
+// base and the LDS address the same in every lane and the LDS address in M0).
+// Issued from inline assembly on purpose: the compiler, unable to tell which
+// LDS bytes such a load writes, would otherwise wait for it before every later
+// LDS read, including reads of the other stage, and expose the load latency on
+// every tile.  The caller waits for these loads itself (vmcnt) before the
+// barrier that hands the stage to the readers.  An LDS-DMA load needs one wait
+// state after a scalar write of M0; the compiler inserts it for loads it
+// generates but cannot see into this string, hence the s_nop.  The compiler keeps nothing in
+// M0 across these statements in the prefill kernels (checked in their assembly).
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
+
 }  // namespace pkv

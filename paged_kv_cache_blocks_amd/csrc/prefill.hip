@@ -11,9 +11,10 @@
 // Work decomposition
 //   1-D grid over (query tile, KV head, sequence) work items, placed so the
 //   query tiles of one (sequence, KV head) share an XCD; 256 threads = 4 waves.
-//   A workgroup owns 128 packed query rows of one sequence and one KV head:
-//   row r = (token r / G, head r % G), so the G heads that share the KV head
-//   reuse every K/V tile.  Each wave owns 32 rows (two 16-row MFMA tiles).
+//   A workgroup owns 64 NT packed query rows of one sequence and one KV head
+//   (NT = 2 or 3): row r = (token r / G, head r % G), so the G heads that
+//   share the KV head reuse every K/V tile.  Each wave owns 16 NT rows (NT
+//   16-row MFMA tiles).
 //   Per 64-key tile (eight 8-key halves, each inside one cache block of 8 ..
 //   256 tokens, looked up in the 2-D or CSR table):
 //     K and V slabs -> LDS (16-byte loads, issued one tile ahead);
@@ -40,8 +41,7 @@ namespace {
 constexpr int D = 128;
 constexpr int BS = 16;          // keys per wave part of a tile (two 8-key halves, each in one cache block)
 constexpr int KT = 64;          // keys per tile
-constexpr int ROWS = 128;       // packed query rows per workgroup
-constexpr int NT = 2;           // 16-row MFMA tiles per wave
+constexpr int ROWS = 128;       // packed query rows per workgroup with two row tiles per wave
 constexpr int ROWB = D * 2;      // bytes of one bf16 K or V row
 constexpr int TILE_B = KT * ROWB;  // one K (or V) tile in LDS
 constexpr int STAGE_B = 2 * TILE_B;  // K tile then V tile
@@ -56,29 +56,6 @@ static_assert(STAGE_B + 2 * STG8_B <= kStages * STAGE_B, "FP8 tile + staging mus
 // direct global->LDS loads write 1 KiB of consecutive LDS each.
 
 
-// 16 bytes per lane from global memory straight into LDS at lds + 16 * lane
-// (global_load_lds_dwordx4, scalar-base form: address = base + off, with the
-// base and the LDS address the same in every lane and the LDS address in M0).
-// Issued from inline assembly on purpose: the compiler, unable to tell which
-// LDS bytes such a load writes, would otherwise wait for it before every later
-// LDS read, including reads of the other stage, and expose the load latency on
-// every tile.  The caller waits for these loads itself (vmcnt) before the
-// barrier that hands the stage to the readers.  An LDS-DMA load needs one wait
-// state after a scalar write of M0; the compiler inserts it for loads it
-// generates but cannot see into this string, hence the s_nop.  The compiler keeps nothing in
-// M0 across these statements in this kernel (checked in its assembly).
-__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(off), "s"(base)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-}
-
-
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 constexpr float kRescaleSlack = 8.f;           // log2 units: weights stay <= 256
 
@@ -88,8 +65,8 @@ __device__ __forceinline__ void no_if_conversion() { asm volatile("" ::: "memory
 
 }  // namespace
 
-template <bool FP8>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+template <bool FP8, int NT>
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillArgs a) {
   // bf16 KV: kStages tiles (K then V).  FP8 KV: one bf16 tile at the start,
   // then two staging buffers of codes, per wave [K block][V block].
   __shared__ __align__(16) char smem[kStages * STAGE_B];
@@ -99,7 +76,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in a scalar register
   const int G = a.group;
-  const int tq = ROWS / G;              // tokens per workgroup
+  const int tq = 64 * NT / G;           // tokens per workgroup (64 NT packed rows)
   // Work order.  Sequences are taken longest first (most keys: context plus
   // chunk), so the long workgroups start early and short ones fill the end;
   // within a sequence the later query tiles, which see more keys, go first.
@@ -350,20 +327,34 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       for (int nt = 0; nt < NT; ++nt) st_[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     // K fragments of the next 32-wide d step are read while this step's
     // MFMAs run (two groups of four fragments in flight)
-    u32x4 kf[2][4];
+    if constexpr (NT == 2) {
+      u32x4 kf[2][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) kf[0][t] = ld16(k_lds + swz(16 * t + n, g));
+      for (int t = 0; t < 4; ++t) kf[0][t] = ld16(k_lds + swz(16 * t + n, g));
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      if (ds + 1 < 4) {
+      for (int ds = 0; ds < 4; ++ds) {
+        if (ds + 1 < 4) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) kf[(ds + 1) & 1][t] = ld16(k_lds + swz(16 * t + n, 4 * (ds + 1) + g));
+          for (int t = 0; t < 4; ++t) kf[(ds + 1) & 1][t] = ld16(k_lds + swz(16 * t + n, 4 * (ds + 1) + g));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf[ds & 1][t], qf[nt][ds], st_[t][nt]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's MFMAs
+    } else {
+      // more row tiles: one fragment (16 keys x 32 d) ahead, fewer registers
+      u32x4 kf[2];
+      kf[0] = ld16(k_lds + swz(n, g));
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < 16; ++i) {  // i = 4 ds + t
+        const int ds = i >> 2, t = i & 3;
+        if (i + 1 < 16) kf[(i + 1) & 1] = ld16(k_lds + swz(16 * ((i + 1) & 3) + n, 4 * ((i + 1) >> 2) + g));
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf[ds & 1][t], qf[nt][ds], st_[t][nt]);
+        for (int nt = 0; nt < NT; ++nt) st_[t][nt] = mfma_bf16(kf[i & 1], qf[nt][ds], st_[t][nt]);
+      }
     }
 
     if (FP8) {
@@ -484,16 +475,31 @@ bool prefill_supported_group(int group) {
   return group >= 1 && group <= ROWS && (ROWS % group) == 0;
 }
 
+// Rows per wave.  Each 1-KiB K or V fragment read from LDS feeds one product
+// per 16-row tile the wave owns.  Three row tiles (48 rows per wave, 192 per
+// workgroup; the group size must divide 192) cut the fragment reads per
+// product by a third and still fit two waves per SIMD (256 registers, a few
+// spilled outside the key loop).  Measured on the 16 x 512-token chunk this
+// runs 1-2% faster than two row tiles: the kernel is not bound by LDS
+// bandwidth.  FP8 caches keep two tiles (their conversion pass needs the
+// registers).
+static bool three_row_tiles(const PrefillArgs& a) {
+  return !a.kv_fp8 && (192 % a.group) == 0;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream) {
   (void)d;
-  const int tq = ROWS / a.group;
+  const int nt = three_row_tiles(a) ? 3 : 2;
+  const int tq = 64 * nt / a.group;
   const int64_t n_work = (int64_t)((a.max_q_len + tq - 1) / tq) * a.n_kv * a.num_seqs;
   if (n_work == 0) return hipSuccess;
   if (n_work > 0x7fffffff) return hipErrorInvalidValue;
   if (a.kv_fp8)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)n_work), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<true, 2>), dim3((unsigned)n_work), dim3(256), 0, stream, a);
+  else if (nt == 3)
+    hipLaunchKernelGGL((prefill_kernel<false, 3>), dim3((unsigned)n_work), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)n_work), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<false, 2>), dim3((unsigned)n_work), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
