@@ -507,7 +507,8 @@ def parity_figures(got, want):
     return float(np.max(np.abs(d))), float(rel.max()) if rel.size else 0.0
 
 
-DEFAULT_CPU_LAYERS = {"tiny-f32": 1, "llama8b-bf16": 8, "llama70b-32k-bf16": 8, "llama70b-fp8-mix": 4}
+# whole layers the oracle runs on all cores, by workload id (tiny, 8B, 70B 32K, fp8 mix)
+DEFAULT_CPU_LAYERS = {1: 1, 2: 8, 3: 8, 4: 4}
 
 
 def cpu_baseline(w: DecodeWorkload, sample_layers: int = None):
@@ -515,7 +516,7 @@ def cpu_baseline(w: DecodeWorkload, sample_layers: int = None):
     sequence and head) on a fork pool of cpu_workers() processes, plus one
     whole layer on one core.  Returns the baseline record and the GPU-vs-oracle
     error figures over the sampled layers."""
-    n = min(sample_layers or DEFAULT_CPU_LAYERS.get(w.name, 2), w.layers)
+    n = min(sample_layers or DEFAULT_CPU_LAYERS.get(w.cfg_id, 2), w.layers)
     workers = cpu_workers()
     layers = list(range(n))
     outs, dt = oracle_decode_layers(w, layers, workers)
@@ -834,7 +835,7 @@ def main():
     if not args.no_cpu_baseline:
         base, err, rel = cpu_baseline(w, args.cpu_sample_layers)
         rec["cpu_baseline"] = base
-        n = min(args.cpu_sample_layers or DEFAULT_CPU_LAYERS.get(w.name, 2), w.layers)
+        n = min(args.cpu_sample_layers or DEFAULT_CPU_LAYERS.get(w.cfg_id, 2), w.layers)
         rec["parity"] = {"max_abs_err": err, "max_row_rel_err": rel,
                          "over": f"{n} whole layer(s): every sequence and query head"}
     print(json.dumps(rec))
