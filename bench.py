@@ -56,6 +56,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 MFMA
 METRIC = "paged GQA decode: achieved HBM GB/s (% of peak) and tokens/s per layer"
 
 # workload name -> synth workload id (the id also namespaces the seeds)
@@ -311,7 +312,11 @@ class PrefillWorkload:
         import torch
         import paged_kv_cache_blocks_amd as pkv
         self.pkv, self.torch = pkv, torch
-        self.kind = kv
+        # "fp8-mma": the FP8 cache attended with both products in FP8, queries
+        # and weights as two E4M3 terms ("fp8-mma-single": one term)
+        self.mma = kv.startswith("fp8-mma")
+        self.split = kv == "fp8-mma"
+        self.kind = "fp8" if self.mma else kv
         c = synth.CONFIGS[cfg_id]
         self.name = c["name"]
         self.n_q, self.n_kv, self.d = c["n_q"], c["n_kv"], c["d"]
@@ -326,7 +331,7 @@ class PrefillWorkload:
         self.block_table = torch.from_numpy(table).to(dev)
         shape = (self.num_blocks, self.n_kv, 16, self.d)
         self.ks = self.vs = None
-        if kv == "fp8":
+        if self.kind == "fp8":
             # codes and per-(block, KV head) scales = max |x| / 448 over the block
             cs = []
             for seed in (5001, 5002):
@@ -354,9 +359,13 @@ class PrefillWorkload:
         torch.cuda.synchronize()
 
     def attn_call(self):
-        self.pkv.paged_attn_prefill_chunk(self.q, self.cu, self.ctx_t, self.q_len, self.k, self.v, self.block_table,
-                                          self.n_q, self.n_kv, self.d, 16, self.scale, out=self.out,
-                                          k_scale=self.ks, v_scale=self.vs)
+        args = (self.q, self.cu, self.ctx_t, self.q_len, self.k, self.v, self.block_table, self.n_q, self.n_kv, self.d,
+                16, self.scale)
+        if self.mma:
+            self.pkv.paged_attn_prefill_chunk_fp8_mma(*args, out=self.out, k_scale=self.ks, v_scale=self.vs,
+                                                      split=self.split)
+        else:
+            self.pkv.paged_attn_prefill_chunk(*args, out=self.out, k_scale=self.ks, v_scale=self.vs)
 
     def step(self, events=None):
         pkv = self.pkv
@@ -376,6 +385,8 @@ class PrefillWorkload:
     def describe(self):
         return {"workload": self.name, "num_seqs": len(self.ctx), "q_len": self.q_len, "n_q_heads": self.n_q,
                 "n_kv_heads": self.n_kv, "d_head": self.d, "block_size": 16, "kv_dtype": self.kind,
+                **({"products": "fp8: q and softmax weights as %s" % ("two E4M3 terms each" if self.split else
+                                                                       "one E4M3 term each")} if self.mma else {}),
                 "mean_ctx": float(np.mean(self.ctx))}
 
 
@@ -701,8 +712,10 @@ def main():
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64, 128, 256],
                     help="decode workloads: tokens per cache block (the same sequences, re-paged)")
     ap.add_argument("--csr", action="store_true", help="decode workloads: pass the page table in CSR form")
-    ap.add_argument("--prefill-kv", choices=["bf16", "fp8"], default="bf16",
-                    help="prefill workload: KV cache element type (fp8: the chunk is quantised on append)")
+    ap.add_argument("--prefill-kv", choices=["bf16", "fp8", "fp8-mma", "fp8-mma-single"], default="bf16",
+                    help="prefill workload: KV cache element type (fp8: the chunk is quantised on append and the "
+                         "codes widened to bf16 for the products; fp8-mma: the same cache with both products in "
+                         "fp8, queries and weights as two E4M3 terms; fp8-mma-single: one term each)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="decode workloads: replay each step from HIP graphs (auto: when the step has several "
@@ -796,15 +809,19 @@ def main():
     if prefill:
         tflops = w.flops / step_s / 1e12
         achieved = w.flops / avg_call_s / 1e12
-        rec = {"metric": "chunked prefill over a paged cache: achieved TFLOP/s (bf16 MFMA)", "value": round(tflops, 3),
+        peak = MFMA_FP8_PEAK_TFLOPS if w.mma else MFMA_BF16_PEAK_TFLOPS
+        rec = {"metric": "chunked prefill over a paged cache: achieved TFLOP/s (%s MFMA)" % ("fp8" if w.mma else "bf16"),
+               "value": round(tflops, 3),
                "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-               "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
+               "vs_baseline": None, "dtype": "fp8" if w.mma else "bf16",
+               "data": "synthetic: seeded N(0,1) q/k/v, random-permutation block tables (no weights or datasets)",
                "config": w.describe(), "timing": timing, "wall_s_with_flushes": round(wall, 4),
-               "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
-                            "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
-                            "kernel": "prefill_kernel", "avg_call_us": round(avg_call_s * 1e6, 2),
-                            "flops_per_call": w.flops},
+               "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                            "kernel": ("prefill_fp8_kernel<%s>" % ("true" if w.split else "false")) if w.mma
+                            else "prefill_kernel",
+                            "avg_call_us": round(avg_call_s * 1e6, 2), "flops_per_call": w.flops},
                "new_tokens_per_s": round(len(w.ctx) * w.q_len / step_s, 1)}
         print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step (median)", file=sys.stderr, flush=True)
         if not args.no_cpu_baseline:

@@ -521,6 +521,40 @@ pkv_status pkv_paged_attn_prefill_chunk_csr(void* out, pkv_dtype out_dtype, cons
                                             int32_t n_q_heads, int32_t n_kv_heads, int32_t d_head,
                                             int32_t block_size, float scale, int32_t causal, void* stream);
 
+/* Chunked prefill over an FP8 cache with both products in FP8 on the matrix
+ * cores (the FP8 attention of FlashAttention-3, [KVP] Problem 5, over the FP8
+ * cache of [MEM] "long context"): the K and V codes enter the products as
+ * stored; each query row is scaled by its own max |q| / 448 and each softmax
+ * weight carries its block's V scale and one factor per workgroup, and both
+ * enter the products in E4M3.  The row sum adds the quantised weights
+ * themselves (each over its V scale), so every output row is a convex
+ * combination of the dequantised V rows and a single visible key returns its
+ * V row exactly; keys of blocks whose V scale is below 2^-3 of what the
+ * weights can use count unquantised weights instead.
+ *   split = 1: queries and weights are each carried as two E4M3 terms, the
+ *     nearest value plus the nearest value to the remainder (relative error
+ *     about 2^-8), at two products per tile pair: within the FP8 tolerance of
+ *     pkv_paged_attn_prefill_chunk's result (about 3e-3 max-abs on N(0,1)
+ *     data).
+ *   split = 0: one E4M3 term each, as FlashAttention-3 does, at half the
+ *     products: faster, with row errors of a few percent (a rounding of up to
+ *     2^-4 per query element and weight); it does not meet the FP8 tolerance.
+ * Arguments as pkv_paged_attn_prefill_chunk (2-D block table, no workspace),
+ * with kv_dtype PKV_FP8_E4M3FN only (else PKV_ERR_UNSUPPORTED); k_scale and
+ * v_scale are required, non-negative and finite (as pkv_kv_append_fp8 writes
+ * them), and a block whose scale is 0 holds zero codes.  Supported: d_head
+ * 128; block_size 8 .. 256; n_q_heads / n_kv_heads divides 128; q BF16; out
+ * F32 or BF16. */
+pkv_status pkv_paged_attn_prefill_chunk_fp8_mma(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                                const int32_t* cu_q_lens, const int32_t* context_lens,
+                                                int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                                const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                                const float* k_scale, const float* v_scale,
+                                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                                                int32_t d_head, int32_t block_size, float scale, int32_t causal,
+                                                int32_t split, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

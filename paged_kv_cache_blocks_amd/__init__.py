@@ -63,6 +63,9 @@ _SIGS = {
     "pkv_paged_attn_prefill_chunk_csr": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                                           ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _vp], ctypes.c_int),
+    "pkv_paged_attn_prefill_chunk_fp8_mma": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _i32, _i32, _i32, _vp,
+                                              _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _i32,
+                                              _f32, _i32, _i32, _vp], ctypes.c_int),
     "pkv_csr_to_block_table": ([_vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_swap_image_bytes": ([_i32, ctypes.c_int, _i32, _i32, _i32], _sz),
     "pkv_swap_out": ([_vp, _vp, ctypes.c_int, _vp, _vp, _i64, _vp, _i32, _vp, _sz, _vp, _i32, _i32, _i32, _vp],
@@ -513,6 +516,27 @@ def paged_attn_prefill_chunk(q, cu_q_lens, context_lens, max_q_len, k_cache, v_c
         _ptr(k_scale), _ptr(v_scale),
         _ptr(block_table), block_table.shape[1], k_cache.shape[0], n_q_heads, n_kv_heads, d_head, block_size,
         float(scale), 1 if causal else 0, None, 0, _stream(stream)))
+    return out
+
+
+def paged_attn_prefill_chunk_fp8_mma(q, cu_q_lens, context_lens, max_q_len, k_cache, v_cache, block_table,
+                                     n_q_heads, n_kv_heads, d_head, block_size, scale, *, k_scale, v_scale,
+                                     causal: bool = True, split: bool = True, out=None,
+                                     out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Chunked prefill over an FP8 cache with both products in FP8: queries
+    and softmax weights in E4M3, as two terms each (split=True, within the FP8
+    tolerance) or one (split=False, faster, row errors of a few percent)."""
+    total_q = q.shape[0]
+    _need(cu_q_lens, torch.int32, "cu_q_lens")
+    _need(context_lens, torch.int32, "context_lens")
+    _need(block_table, torch.int32, "block_table")
+    if out is None:
+        out = torch.empty((total_q, n_q_heads, d_head), dtype=out_dtype, device=q.device)
+    _check(load().pkv_paged_attn_prefill_chunk_fp8_mma(
+        _ptr(out), dtype_code(out), _ptr(q), dtype_code(q), _ptr(cu_q_lens), _ptr(context_lens),
+        context_lens.numel(), total_q, int(max_q_len), _ptr(k_cache), _ptr(v_cache), dtype_code(k_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(block_table), block_table.shape[1], k_cache.shape[0], n_q_heads,
+        n_kv_heads, d_head, block_size, float(scale), 1 if causal else 0, 1 if split else 0, _stream(stream)))
     return out
 
 

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpkv.so")
-SOURCES = ["kv_ops.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "device_check.hip", "pkv_api.cpp"]
+SOURCES = ["kv_ops.hip", "decode.hip", "decode_mfma.hip", "prefill.hip", "prefill_fp8.hip", "device_check.hip", "pkv_api.cpp"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 # Packed FP32 instructions are kept out of the generated code on purpose.

@@ -847,7 +847,8 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype
                         const void* k_cache, const void* v_cache, pkv_dtype kv_dtype, const float* k_scale,
                         const float* v_scale, const int32_t* block_table, const int32_t* indptr,
                         int32_t max_blocks_per_seq, int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
-                        int32_t d_head, int32_t block_size, float scale, int32_t causal, void* stream) {
+                        int32_t d_head, int32_t block_size, float scale, int32_t causal, void* stream,
+                        int fp8_mma = -1) {
   pkv_status st = check_heads(n_q_heads, n_kv_heads);
   if (st != PKV_OK) return st;
   if (!valid_dtype(out_dtype) || !valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
@@ -867,6 +868,8 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype
     return fail(PKV_ERR_UNSUPPORTED, "prefill needs bf16 q and bf16 or fp8 KV");
   if (kv_dtype == PKV_FP8_E4M3FN && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID_ARG, "fp8 caches need k_scale and v_scale");
+  if (fp8_mma >= 0 && kv_dtype != PKV_FP8_E4M3FN)
+    return fail(PKV_ERR_UNSUPPORTED, "fp8 products need an FP8 cache");
   if (out_dtype == PKV_FP8_E4M3FN) return fail(PKV_ERR_UNSUPPORTED, "fp8 output unsupported");
   const int group = n_q_heads / n_kv_heads;
   if (!pkv::prefill_supported_group(group))
@@ -907,6 +910,8 @@ pkv_status prefill_impl(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype
     });
     if (st != PKV_OK) return st;
   }
+  if (fp8_mma >= 0)
+    return hip_status(pkv::launch_prefill_fp8_mma(a, fp8_mma != 0, (hipStream_t)stream), "prefill launch");
   return hip_status(pkv::launch_prefill(a, d_head, (hipStream_t)stream), "prefill launch");
 }
 
@@ -941,6 +946,21 @@ pkv_status pkv_paged_attn_prefill_chunk_csr(void* out, pkv_dtype out_dtype, cons
   return prefill_impl(out, out_dtype, q, q_dtype, cu_q_lens, context_lens, num_seqs, total_q, max_q_len, k_cache,
                       v_cache, kv_dtype, k_scale, v_scale, kv_indices, kv_indptr, max_pages_per_seq, num_blocks,
                       n_q_heads, n_kv_heads, d_head, block_size, scale, causal, stream);
+}
+
+pkv_status pkv_paged_attn_prefill_chunk_fp8_mma(void* out, pkv_dtype out_dtype, const void* q, pkv_dtype q_dtype,
+                                                const int32_t* cu_q_lens, const int32_t* context_lens,
+                                                int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                                const void* k_cache, const void* v_cache, pkv_dtype kv_dtype,
+                                                const float* k_scale, const float* v_scale,
+                                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                                int64_t num_blocks, int32_t n_q_heads, int32_t n_kv_heads,
+                                                int32_t d_head, int32_t block_size, float scale, int32_t causal,
+                                                int32_t split, void* stream) {
+  if (split != 0 && split != 1) return fail(PKV_ERR_INVALID_ARG, "split must be 0 or 1");
+  return prefill_impl(out, out_dtype, q, q_dtype, cu_q_lens, context_lens, num_seqs, total_q, max_q_len, k_cache,
+                      v_cache, kv_dtype, k_scale, v_scale, block_table, nullptr, max_blocks_per_seq, num_blocks,
+                      n_q_heads, n_kv_heads, d_head, block_size, scale, causal, stream, split);
 }
 
 

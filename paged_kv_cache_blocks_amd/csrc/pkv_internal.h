@@ -143,6 +143,9 @@ struct PrefillArgs {
   float scale_log2;
 };
 hipError_t launch_prefill(const PrefillArgs& a, int d, hipStream_t stream);
+// both products in FP8 (prefill_fp8.hip): FP8 KV, d = 128, group divides 128;
+// split: queries and weights carried as two E4M3 terms each
+hipError_t launch_prefill_fp8_mma(const PrefillArgs& a, bool split, hipStream_t stream);
 bool prefill_supported_group(int group);
 
 
