@@ -61,8 +61,17 @@ typedef enum {
 } pkv_status;
 
 /* Element types. FP8 is OCP E4M3FN (bias 7, max 448, S.1111.111 = NaN), with
- * one fp32 scale per (block, KV head): value = e4m3fn(byte) * scale. */
-typedef enum { PKV_F32 = 0, PKV_BF16 = 1, PKV_FP8_E4M3FN = 2 } pkv_dtype;
+ * one fp32 scale per (block, KV head): value = e4m3fn(byte) * scale.  The two
+ * range markers are no element types: they make every int32 value a value of
+ * the type in C++ as in C, so a call given an unknown code rejects it
+ * (PKV_ERR_INVALID_ARG) rather than receive a value outside the enumeration. */
+typedef enum {
+  PKV_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3FN = 2,
+  PKV_DTYPE_RANGE_MAX_ = 2147483647
+} pkv_dtype;
 
 int pkv_abi_version(void);
 const char* pkv_status_string(int status);

@@ -46,8 +46,8 @@ int elem_bytes(pkv_dtype t) {
     case PKV_F32: return 4;
     case PKV_BF16: return 2;
     case PKV_FP8_E4M3FN: return 1;
+    default: return 0;
   }
-  return 0;
 }
 
 bool valid_dtype(int t) { return t == PKV_F32 || t == PKV_BF16 || t == PKV_FP8_E4M3FN; }
