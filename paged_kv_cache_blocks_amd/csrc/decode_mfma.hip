@@ -21,17 +21,22 @@
 // a wave:
 //   loads the K and V rows of its two tiles with coalesced, non-temporal
 //   16-byte loads (issued one chunk ahead, from a scalar base per half),
-//   converts fp8 codes to bf16 (exact), and writes them into its own LDS
-//   region in the swizzled row layout (on a partition's last chunk, V rows
-//   past its end are written as zeros: their zero weights must not meet a
-//   NaN, and only that chunk masks scores);
+//   and writes them into its own LDS region in a swizzled row layout: K as
+//   bf16 (fp8 codes widened, exactly), V as bf16 or as the fp8 codes, which
+//   the value product widens as it reads them (on a partition's last chunk,
+//   V rows past its end are written as zeros: their zero weights must not
+//   meet a NaN, and only that chunk masks scores);
 //   S^T = K q^T: 2 token tiles x 4 d steps, K fragments from LDS, q^T in
 //   registers; the fp8 K scale of each half's block multiplies its scores;
 //   online softmax per head column (in-lane max over the lane's 8 tokens,
 //   then across the four lane rows); weights rounded to bf16, the running sum
 //   adds the same rounded weights, and with fp8 each half's V scale
 //   multiplies its weights before the value product;
-//   O^T += V^T P^T: 8 d tiles, V^T fragments read with ds_read_b64_tr_b16.
+//   O^T += V^T P^T: 8 d tiles, V^T fragments read with ds_read_b64_tr_b16
+//   (bf16) or ds_read_b64_tr_b8 and widened (fp8).
+// With fp8 KV a wave's LDS region is 12 KiB (bf16: 16 KiB), which with 160
+// VGPRs lets three workgroups share a CU: measured 2% faster on the serving
+// mix than two workgroups with two chunks in flight per wave.
 #include "pkv_device.h"
 #include "pkv_internal.h"
 
@@ -44,7 +49,10 @@ constexpr int kB = 16;                 // tokens per tile
 constexpr int kCT = 32;                // tokens per wave chunk (two tiles)
 constexpr int kW = 4;                  // waves per workgroup
 constexpr int kTileB = kCT * 256;      // one K or V chunk in LDS (bf16 rows of 256 bytes)
-constexpr int kWaveB = 2 * kTileB;     // K then V
+constexpr int kTile8B = kCT * 128;     // one V chunk of fp8 codes (rows of 128 bytes)
+// LDS per wave: the K chunk as bf16, then the V chunk as bf16 (bf16 KV) or as
+// the cache's fp8 codes (fp8 KV, widened as the value product reads them)
+template <int KIND> constexpr int wave_lds_bytes() { return kTileB + (KIND == KIND_FP8 ? kTile8B : kTileB); }
 constexpr int kMaxHeads = 16;          // MFMA columns
 constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 constexpr float kSlack = 8.f;          // log2 units: the running max moves only past this
@@ -67,6 +75,18 @@ __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, const PageRow& pr
   return min(max(a.seq_lens[s], 0), pr.n << a.log2_bs);
 }
 
+// Block id of the block holding token tok (as page_block), read without a
+// branch: an entry past the table row reads the valid word `spare` instead
+// and is replaced by block 0.  A guarded load would make the wave wait for it
+// where the branch rejoins; this one is waited for only where it is used.
+__device__ __forceinline__ int page_block_nowait(const DecodeArgs& a, const PageRow& r, int tok,
+                                                 const int32_t* spare) {
+  const int j = tok >> a.log2_bs;
+  const bool in = j < r.n;
+  const int v = *(in ? r.ids + j : spare);
+  return min(max(in ? v : 0, 0), (int)(a.num_blocks - 1));
+}
+
 __device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float v) {
   if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[idx] = (__bf16)v;
   else reinterpret_cast<float*>(a.out)[idx] = v;
@@ -74,10 +94,30 @@ __device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float 
 
 }  // namespace
 
+// Slot permutation of the fp8 V chunk's 128-byte rows (eight 16-byte pieces,
+// piece p of row r in slot p ^ f8(r)): the transposing reads take one piece of
+// rows {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} for g = 0, 1 (or 2, 3) at once,
+// the staging writes eight pieces of two consecutive rows; rows of one parity
+// share a bank half, and f8 is one-to-one over the eight even (and the eight
+// odd) rows of each read.
+__device__ __forceinline__ int f8_slot(int r) { return ((r >> 1) & 3) | (((r >> 4) & 1) << 2); }
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+// ds_read_b64_tr_b8: lane L of a 16-lane group receives byte L of the eight
+// 16-byte rows its lane pairs (2 r, 2 r + 1: bytes 0-7, 8-15 of row r) read
+__device__ __forceinline__ v2i ds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(__attribute__((address_space(3))) char*)(p));
+}
+
+// FP8 KV: three workgroups per CU (48 KiB of LDS each, three waves per SIMD),
+// so a workgroup that starts and waits for its first loads leaves two others
+// streaming; bf16 KV: two.
 template <int KIND, int GW>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(GW >= 1 && GW <= kMaxHeads, "heads per workgroup");
   using SL = Slab<KIND>;
+  constexpr int kWaveB = wave_lds_bytes<KIND>();
   __shared__ __align__(16) char smem[kW * kWaveB];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -107,12 +147,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
   const int p0 = part * a.part_tokens;
   const PageRow pr = page_row(a, s);
-  const int L = seq_len_of(a, pr, s);
-  if (a.n_parts > 1 && p0 >= L) return;
-  const int plen = max(0, min(a.part_tokens, L - p0));  // tokens of this partition
-  const int nblk = (plen + kB - 1) / kB;
-  const int n_chunks = (nblk + 1) / 2;
-  const int n_my = n_chunks > w ? (n_chunks - w + kW - 1) / kW : 0;
 
   // Where this wave's tiles live: lane i holds tile (i & 1) of the wave's
   // chunk i >> 1 (partition chunk w + 4 (i >> 1)), so a partition has at most
@@ -121,28 +155,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // tile past the partition keeps row 0: it is loaded all the same, so the
   // loads need no branch, and its rows, being past the end, are masked (K)
   // or staged as zeros (V).
-  uint32_t my_row[2] = {0u, 0u};
-  float my_ks[2] = {1.f, 1.f}, my_vs[2] = {1.f, 1.f};
-  {
-    const int pb = (w + kW * (lane >> 1)) * 2 + (lane & 1);
-    if (pb < nblk) {
+  // The table entries of every lane's tiles are read before the sequence's
+  // length is known (an entry past the table row reads as block 0), and so
+  // are the queries: neither waits for the other, nor for the length.
+  const int len_raw = a.seq_lens[s];
+  const int pb = (w + kW * (lane >> 1)) * 2 + (lane & 1);
+  int id_of[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int tok = p0 + kB * pb + 8 * h;
-        const int id = page_block(a, pr, tok);
-        my_row[h] = page_row_index(a, id, kvh, tok);
-        // a half wholly past the partition keeps scale 1: its table entry may
-        // be clamped or stale, its scale anything (NaN included), and the zero
-        // weights of its masked tokens must not meet it
-        if constexpr (KIND == KIND_FP8) {
-          if (tok < p0 + plen) {
-            my_ks[h] = a.k_scale[(int64_t)id * a.n_kv + kvh];
-            my_vs[h] = a.v_scale[(int64_t)id * a.n_kv + kvh];
-          }
-        }
-      }
-    }
-  }
+  for (int h = 0; h < 2; ++h) id_of[h] = page_block_nowait(a, pr, p0 + kB * pb + 8 * h, a.seq_lens + s);
 
   // q^T fragments (B operand): lane (n, g) holds head n, d = 32 ks + 8 g .. + 7
   u32x4 qf[4];
@@ -153,6 +173,38 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks) {
       const u32x4 v = ld16(qrow + (32 * ks + 8 * g) * 2);
       qf[ks] = real ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // the loads above stay above the branch below (the compiler would sink
+  // them past it, behind the length's latency); nothing waits for their data
+  asm volatile("" ::: "memory");
+  const int L = min(max(len_raw, 0), pr.n << a.log2_bs);
+  if (a.n_parts > 1 && p0 >= L) return;
+  const int plen = max(0, min(a.part_tokens, L - p0));  // tokens of this partition
+  const int nblk = (plen + kB - 1) / kB;
+  const int n_chunks = (nblk + 1) / 2;
+  const int n_my = n_chunks > w ? (n_chunks - w + kW - 1) / kW : 0;
+
+  // Rows and scales of this lane's tiles, without branches (a branch around a
+  // load makes the wave wait for it where the paths rejoin): the scale reads
+  // use the clamped block id, always inside the pool.  A half wholly past the
+  // partition keeps row 0 and scale 1: its table entry may be clamped or
+  // stale, its scale anything (NaN included), and the zero weights of its
+  // masked tokens must not meet it.
+  uint32_t my_row[2];
+  float my_ks[2] = {1.f, 1.f}, my_vs[2] = {1.f, 1.f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tok = p0 + kB * pb + 8 * h;
+    const int id = id_of[h];
+    my_row[h] = pb < nblk ? page_row_index(a, id, kvh, tok) : 0u;
+    if constexpr (KIND == KIND_FP8) {
+      const bool live = pb < nblk && tok < p0 + plen;
+      const float ks = a.k_scale[(int64_t)id * a.n_kv + kvh];
+      const float vs = a.v_scale[(int64_t)id * a.n_kv + kvh];
+      my_ks[h] = live ? ks : 1.f;
+      my_vs[h] = live ? vs : 1.f;
     }
   }
 
@@ -205,16 +257,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           const int r = kB * b + 8 * i + (lane >> 3);
           const int p8 = lane & 7;
           const bool live = !TAIL || t0 + r < plen;
-          uint32_t kb[8], vb[8];
+          uint32_t kb[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            fp8x4_to_bf16x4(bk[b][i][e], kb[2 * e], kb[2 * e + 1]);
-            fp8x4_to_bf16x4(bv[b][i][e], vb[2 * e], vb[2 * e + 1]);
-          }
+          for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4(bk[b][i][e], kb[2 * e], kb[2 * e + 1]);
           st16(k_lds + swz(r, 2 * p8), u32x4{kb[0], kb[1], kb[2], kb[3]});
           st16(k_lds + swz(r, 2 * p8 + 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
-          st16(v_lds + swz(r, 2 * p8), live ? u32x4{vb[0], vb[1], vb[2], vb[3]} : u32x4{0, 0, 0, 0});
-          st16(v_lds + swz(r, 2 * p8 + 1), live ? u32x4{vb[4], vb[5], vb[6], vb[7]} : u32x4{0, 0, 0, 0});
+          // V codes as loaded (zero codes past the partition: +0)
+          st16(v_lds + r * 128 + ((p8 ^ f8_slot(r)) << 4), live ? bv[b][i] : u32x4{0, 0, 0, 0});
         }
       }
     }
@@ -300,7 +349,23 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // ---- O^T += V^T P^T: lane group g's weights are tokens {4g..4g+3,
     // 16+4g..16+4g+3}; the transposing reads fetch V rows in that order ----
     const u32x4 pf = u32x4{pw[0][0], pw[0][1], pw[1][0], pw[1][1]};
-    {
+    if constexpr (KIND == KIND_FP8) {
+      // lane pair (2 b, 2 b + 1) of group g reads the row of the group's token
+      // b (4 g + b, then 16 + 4 g + b - 4), so lane m receives the eight codes
+      // V[token b][16 dt + m], b = 0..7, in the order of its weights
+      const int b = n >> 1;
+      const int key = (b < 4 ? 4 * g + b : 16 + 4 * g + b - 4);
+      const char* row = v_lds + key * 128 + 8 * (n & 1);
+      const int fs = f8_slot(key);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v2i c = ds_read_tr8(row + ((dt ^ fs) << 4));
+        uint32_t v0, v1, v2, v3;
+        fp8x4_to_bf16x4((uint32_t)c[0], v0, v1);
+        fp8x4_to_bf16x4((uint32_t)c[1], v2, v3);
+        o[dt] = mfma_bf16(u32x4{v0, v1, v2, v3}, pf, o[dt]);
+      }
+    } else {
       const int jj = (lane >> 2) & 3, qq = lane & 3;
       const int key_a = 4 * g + jj, key_b = key_a + 16;
 #pragma unroll
@@ -316,16 +381,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // ---- merge the four waves: lane (n, g) holds O^T[16 dt + 4 g + j][head n] ----
   const float l_head = sum_xor32(sum_xor16(l_run));
   __syncthreads();  // every wave is done with its LDS region
-  float* mo = reinterpret_cast<float*>(smem);     // [wave][head][d]
-  float* mml = mo + kW * kMaxHeads * D;           // [wave][head][2]
+  // rows of kMoRow floats: the 16 head rows a store instruction writes start
+  // 4 banks apart (a 128-float row would put them all on one bank)
+  constexpr int kMoRow = D + 4;
+  float* mo = reinterpret_cast<float*>(smem);     // [wave][head][kMoRow]
+  float* mml = mo + kW * kMaxHeads * kMoRow;      // [wave][head][2]
   if (g == 0) {
     mml[(w * kMaxHeads + n) * 2 + 0] = m_run;
     mml[(w * kMaxHeads + n) * 2 + 1] = l_head;
   }
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mo[(w * kMaxHeads + n) * D + 16 * dt + 4 * g + j] = o[dt][j];
+    *reinterpret_cast<f32x4*>(mo + (w * kMaxHeads + n) * kMoRow + 16 * dt + 4 * g) = o[dt];
   __syncthreads();
   for (int idx = threadIdx.x; idx < GW * D; idx += 256) {
     const int h = idx / D, col = idx % D;
@@ -339,7 +406,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const float mw = mml[(ww * kMaxHeads + h) * 2];
         const float e = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
         lsum = fmaf(e, mml[(ww * kMaxHeads + h) * 2 + 1], lsum);
-        osum = fmaf(e, mo[(ww * kMaxHeads + h) * D + col], osum);
+        osum = fmaf(e, mo[(ww * kMaxHeads + h) * kMoRow + col], osum);
       }
     }
     const int hq = h0 + h;

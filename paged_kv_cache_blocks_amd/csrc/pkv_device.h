@@ -154,14 +154,17 @@ __device__ __forceinline__ void set_priority_for_progress(int done, int total) {
 }
 
 // ---- matrix-core tiles (d = 128, bf16) ----
-// LDS layout of a K or V tile: row r (one token) is 256 bytes, its 16 pieces
-// of 16 bytes with piece c stored in slot c ^ f(r % 16).  f is the
-// permutation 2 (r & 7) + ((r >> 2) ^ (r >> 3)) & 1 of 0..15, chosen so both
-// read patterns hit distinct banks: the score MFMAs read one piece of 16
-// consecutive rows (f is one-to-one, and f & 7 differs within 8 aligned
-// rows), the transposing value reads read pieces {2j, 2j + 1} of 4 (or 8)
-// aligned rows (f >> 1 differs there).
-__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
+// LDS layout of a K or V tile: row r (one token) is 256 bytes (all 64 banks),
+// its 16 pieces of 16 bytes with piece c stored in slot c ^ f(r % 16), f(r) =
+// 2 (r & 7) + (r ^ (r >> 2) ^ (r >> 3)) & 1, a permutation of 0..15 chosen so
+// every access pattern of the kernels hits distinct banks:
+//   the score MFMAs read one piece of 16 consecutive rows (f is one-to-one);
+//   the transposing value reads read pieces {2j, 2j + 1} of 8 aligned rows
+//   (f >> 1 = r & 7 differs there, and the low bit covers both pieces);
+//   the FP8 decode stages two consecutive rows per 16 lanes, eight pieces
+//   2j (or 2j + 1) of each: rows 2k and 2k + 1 differ in the low bit of f, so
+//   the two rows fill the even and the odd slots.
+__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | ((r ^ (r >> 2) ^ (r >> 3)) & 1); }
 __device__ __forceinline__ int swz(int row, int piece) { return row * 256 + ((piece ^ swz_f(row & 15)) << 4); }
 
 // D (16x16, fp32) += A (16x32, bf16) B (32x16, bf16): lane l supplies
@@ -184,9 +187,9 @@ __device__ __forceinline__ u32x2 ds_read_tr(const char* p) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 // 16-byte load marked non-temporal (the nt bit: a streaming access whose
 // lines the caches need not keep), for K/V bytes a kernel reads exactly once.
-// Measured on MI355X: 512 workgroups reading randomly placed 4-16 KiB pieces
-// of a 430 MB region stream at 6.7-6.8 TB/s this way against 5.4-5.9 TB/s
-// with ordinary loads.
+// Measured on MI355X (pkv_read_probe): 512-1024 workgroups reading randomly
+// placed 4-16 KiB pieces of a 430 MB region stream at 6.28-6.50 TB/s this way
+// against 5.33-5.82 TB/s with ordinary loads.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
