@@ -601,8 +601,9 @@ def traffic_from_profile(workload_key):
 
 def read_probe_bench():
     """Read bandwidth a plain kernel gets on this GPU: a 2 GiB buffer read in
-    grid-stride order, and randomly placed slabs (4 KiB: one (block, KV head)
-    slab of a bf16 paged cache; 16 KiB) of its first 430 MB, the size of one
+    grid-stride order, and randomly placed slabs (2 KiB: one (block, KV head)
+    slab of an fp8 paged cache at 16-token blocks; 4 KiB: the same for bf16;
+    16 KiB) of its first 430 MB, the size of one
     8B-shaped decode call, with ordinary and non-temporal loads.  Best of 5
     event-timed launches after one warm-up."""
     import torch
@@ -630,7 +631,7 @@ def read_probe_bench():
             t = timed(lambda: pkv.read_probe(buf, sink, None, 4096, wgs, nt))
             rows.append({"pattern": "sequential", "bytes": nbytes, "workgroups": wgs, "nontemporal": nt,
                          "GB/s": round(nbytes / t / 1e9, 1)})
-    for slab in (4096, 16384):
+    for slab in (2048, 4096, 16384):
         n = region // slab
         perm = torch.from_numpy(np.random.default_rng(7).permutation(n).astype(np.int32)).cuda()
         for nt in (False, True):

@@ -187,7 +187,7 @@ pkv_status pkv_paged_gather(void* k_out, void* v_out, const void* k_cache, const
  * plain kernel gets from HBM, to set beside the decode figures.  Reads the
  * device buffer buf (bytes, a multiple of 16) with 16-byte loads on
  * `workgroups` workgroups of 256 threads: with slab_list == NULL every byte in
- * grid-stride order; otherwise the slabs of slab_bytes (a multiple of 4096)
+ * grid-stride order; otherwise the slabs of slab_bytes (1024, 2048 or a multiple of 4096)
  * named by slab_list (device int32 [n_list], entries clamped into the buffer),
  * workgroup w reading entries w * (n_list / workgroups) onward one slab after
  * another, the pattern of one (block, KV head) slab of a paged cache.

@@ -431,24 +431,44 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const char* __restrict_
       acc ^= v[0] ^ v[3];
     }
   } else {
-    // four slabs at a time, so each thread keeps four loads in flight
     const int32_t* my = slabs + (int64_t)blockIdx.x * per_wg;
     auto slab_at = [&](int j) { return buf + min(max((int64_t)my[j], (int64_t)0), n_slabs - 1) * slab_bytes; };
-    int j = 0;
-    for (; j + 4 <= per_wg; j += 4) {
-      const char* sp[4] = {slab_at(j), slab_at(j + 1), slab_at(j + 2), slab_at(j + 3)};
-      for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
+    if (slab_bytes >= 4096) {
+      // four slabs at a time, so each thread keeps four loads in flight
+      int j = 0;
+      for (; j + 4 <= per_wg; j += 4) {
+        const char* sp[4] = {slab_at(j), slab_at(j + 1), slab_at(j + 2), slab_at(j + 3)};
+        for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
+          u32x4 v[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = probe_ld<NT>(sp[q] + o);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc ^= v[q][0] ^ v[q][3];
+        }
+      }
+      for (; j < per_wg; ++j) {
+        const char* slab = slab_at(j);
+        for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
+          const u32x4 v = probe_ld<NT>(slab + o);
+          acc ^= v[0] ^ v[3];
+        }
+      }
+    } else {
+      // slabs of 1 or 2 KiB: one 4 KiB sweep of the workgroup covers `per`
+      // slabs, thread t reading slab t * 16 / slab_bytes of the sweep at byte
+      // t * 16 % slab_bytes; four sweeps at a time keep four loads in flight
+      const int per = 4096 / slab_bytes;
+      const int sub = (int)(threadIdx.x * 16) / slab_bytes, o = (int)(threadIdx.x * 16) % slab_bytes;
+      int j = 0;
+      for (; j + 4 * per <= per_wg; j += 4 * per) {
         u32x4 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = probe_ld<NT>(sp[q] + o);
+        for (int q = 0; q < 4; ++q) v[q] = probe_ld<NT>(slab_at(j + q * per + sub) + o);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc ^= v[q][0] ^ v[q][3];
       }
-    }
-    for (; j < per_wg; ++j) {
-      const char* slab = slab_at(j);
-      for (int o = threadIdx.x * 16; o < slab_bytes; o += 256 * 16) {
-        const u32x4 v = probe_ld<NT>(slab + o);
+      for (; j + sub < per_wg; j += per) {
+        const u32x4 v = probe_ld<NT>(slab_at(j + sub) + o);
         acc ^= v[0] ^ v[3];
       }
     }

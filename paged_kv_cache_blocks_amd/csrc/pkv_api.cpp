@@ -570,8 +570,9 @@ pkv_status pkv_read_probe(const void* buf, int64_t bytes, const int32_t* slab_li
   if (!buf || !sink) return fail(PKV_ERR_INVALID_ARG, "null pointer");
   if (bytes < 16 || bytes % 16 != 0 || workgroups < 1) return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
   if (slab_list) {
-    if (slab_bytes < 4096 || slab_bytes % 4096 != 0 || slab_bytes > bytes)
-      return fail(PKV_ERR_INVALID_ARG, "slab_bytes must be a multiple of 4096 within the buffer");
+    if (!(slab_bytes == 1024 || slab_bytes == 2048 || (slab_bytes >= 4096 && slab_bytes % 4096 == 0)) ||
+        slab_bytes > bytes)
+      return fail(PKV_ERR_INVALID_ARG, "slab_bytes must be 1024, 2048 or a multiple of 4096 within the buffer");
     if (n_list < workgroups) return fail(PKV_ERR_INVALID_ARG, "fewer slabs than workgroups");
   }
   return hip_status(pkv::launch_read_probe(buf, bytes, slab_list, n_list, slab_bytes, workgroups, nontemporal ? 1 : 0,

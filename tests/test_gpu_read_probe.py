@@ -23,5 +23,7 @@ def test_read_probe_runs(pkv, nt):
     perm = torch.from_numpy(np.random.default_rng(3).permutation((8 << 20) // 16384).astype(np.int32)).cuda()
     pkv.read_probe(buf, sink, perm, 16384, 32, nt)
     pkv.read_probe(buf, sink, perm[:40], 4096, 8, nt)  # list shorter than the 4-slab groups times workgroups
+    pkv.read_probe(buf, sink, perm, 2048, 32, nt)      # slabs smaller than a workgroup's 4 KiB sweep
+    pkv.read_probe(buf, sink, perm[:37], 1024, 4, nt)  # and a remainder of single loads
     torch.cuda.synchronize()
     assert int(sink.item()) == 7
