@@ -94,6 +94,15 @@ __device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float 
 
 }  // namespace
 
+// The decode's LDS tile layout: as swz (pkv_device.h) with the low bit of the
+// permutation taken from r ^ (r >> 2) ^ (r >> 3), which differs between rows
+// 2k and 2k + 1, so the fp8 K staging (eight pieces 2j or 2j + 1 of two
+// consecutive rows per 16 lanes) fills the even and the odd slots.
+__device__ __forceinline__ int dswz(int row, int piece) {
+  const int r = row & 15;
+  return row * 256 + ((piece ^ (((r & 7) << 1) | ((r ^ (r >> 2) ^ (r >> 3)) & 1))) << 4);
+}
+
 // Slot permutation of the fp8 V chunk's 128-byte rows (eight 16-byte pieces,
 // piece p of row r in slot p ^ f8(r)): the transposing reads take one piece of
 // rows {4g .. 4g + 3, 16 + 4g .. 16 + 4g + 3} for g = 0, 1 (or 2, 3) at once,
@@ -251,8 +260,8 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
           const int r = kB * b + 4 * i + (lane >> 4);  // chunk row
           const int pc = lane & 15;
           const bool live = !TAIL || t0 + r < plen;
-          st16(k_lds + swz(r, pc), bk[b][i]);
-          st16(v_lds + swz(r, pc), live ? bv[b][i] : u32x4{0, 0, 0, 0});
+          st16(k_lds + dswz(r, pc), bk[b][i]);
+          st16(v_lds + dswz(r, pc), live ? bv[b][i] : u32x4{0, 0, 0, 0});
         } else {
           const int r = kB * b + 8 * i + (lane >> 3);
           const int p8 = lane & 7;
@@ -260,8 +269,8 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
           uint32_t kb[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4(bk[b][i][e], kb[2 * e], kb[2 * e + 1]);
-          st16(k_lds + swz(r, 2 * p8), u32x4{kb[0], kb[1], kb[2], kb[3]});
-          st16(k_lds + swz(r, 2 * p8 + 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
+          st16(k_lds + dswz(r, 2 * p8), u32x4{kb[0], kb[1], kb[2], kb[3]});
+          st16(k_lds + dswz(r, 2 * p8 + 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
           // V codes as loaded (zero codes past the partition: +0)
           st16(v_lds + r * 128 + ((p8 ^ f8_slot(r)) << 4), live ? bv[b][i] : u32x4{0, 0, 0, 0});
         }
@@ -288,7 +297,7 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
     for (int t = 0; t < 2; ++t) {
       st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) st[t] = mfma_bf16(ld16(k_lds + swz(16 * t + n, 4 * ks + g)), qf[ks], st[t]);
+      for (int ks = 0; ks < 4; ++ks) st[t] = mfma_bf16(ld16(k_lds + dswz(16 * t + n, 4 * ks + g)), qf[ks], st[t]);
     }
 
     // ---- online softmax for head column n over tokens t0 + 16 t + 4 g + j ----
@@ -371,8 +380,8 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const int pc = 2 * dt + (qq >> 1), half = (qq & 1) * 8;
-        const u32x2 lo = ds_read_tr(v_lds + swz(key_a, pc) + half);
-        const u32x2 hi = ds_read_tr(v_lds + swz(key_b, pc) + half);
+        const u32x2 lo = ds_read_tr(v_lds + dswz(key_a, pc) + half);
+        const u32x2 hi = ds_read_tr(v_lds + dswz(key_b, pc) + half);
         o[dt] = mfma_bf16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pf, o[dt]);
       }
     }

@@ -155,16 +155,20 @@ __device__ __forceinline__ void set_priority_for_progress(int done, int total) {
 
 // ---- matrix-core tiles (d = 128, bf16) ----
 // LDS layout of a K or V tile: row r (one token) is 256 bytes (all 64 banks),
-// its 16 pieces of 16 bytes with piece c stored in slot c ^ f(r % 16), f(r) =
-// 2 (r & 7) + (r ^ (r >> 2) ^ (r >> 3)) & 1, a permutation of 0..15 chosen so
-// every access pattern of the kernels hits distinct banks:
-//   the score MFMAs read one piece of 16 consecutive rows (f is one-to-one);
-//   the transposing value reads read pieces {2j, 2j + 1} of 8 aligned rows
-//   (f >> 1 = r & 7 differs there, and the low bit covers both pieces);
-//   the FP8 decode stages two consecutive rows per 16 lanes, eight pieces
-//   2j (or 2j + 1) of each: rows 2k and 2k + 1 differ in the low bit of f, so
-//   the two rows fill the even and the odd slots.
-__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | ((r ^ (r >> 2) ^ (r >> 3)) & 1); }
+// its 16 pieces of 16 bytes with piece c stored in slot c ^ f(r % 16), f a
+// permutation of 0..15 with f >> 1 = r & 7, so both read patterns hit distinct
+// banks: the score MFMAs read one piece of 16 consecutive rows (f is
+// one-to-one), the transposing value reads read pieces {2j, 2j + 1} of 8
+// aligned rows (f >> 1 differs there, and the low bit covers both pieces).
+// The low bit differs per kernel:
+//   prefill, whose direct-to-LDS loads apply the permutation to the global
+//   addresses: ((r >> 2) ^ (r >> 3)) & 1, constant over the four rows of one
+//   load instruction (the alternative below made the prefill 62 % slower);
+//   decode, which stages from registers: (r ^ (r >> 2) ^ (r >> 3)) & 1 (see
+//   dswz in decode_mfma.hip), so that the fp8 staging, two consecutive rows
+//   per 16 lanes and the pieces 2j (or 2j + 1) of each, fills the even and
+//   the odd slots.
+__device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
 __device__ __forceinline__ int swz(int row, int piece) { return row * 256 + ((piece ^ swz_f(row & 15)) << 4); }
 
 // D (16x16, fp32) += A (16x32, bf16) B (32x16, bf16): lane l supplies
