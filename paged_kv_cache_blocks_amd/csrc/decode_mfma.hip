@@ -94,13 +94,15 @@ __device__ __forceinline__ void put_out(const DecodeArgs& a, int64_t idx, float 
 
 }  // namespace
 
-// The decode's LDS tile layout: as swz (pkv_device.h) with the low bit of the
-// permutation taken from r ^ (r >> 2) ^ (r >> 3), which differs between rows
-// 2k and 2k + 1, so the fp8 K staging (eight pieces 2j or 2j + 1 of two
-// consecutive rows per 16 lanes) fills the even and the odd slots.
+// The decode's LDS tile layout: as swz (pkv_device.h), with the permutation
+// f = (r1 ^ r3, r0, r1, r2 ^ r3 in bits 0..3): besides the K and V reads it
+// serves the bf16 staging writes (one row per 16 lanes) and the fp8 K staging
+// writes (eight pieces 2j, or 2j + 1, of two consecutive rows per 16 lanes)
+// without bank conflicts under the 16-byte access rule given there.
 __device__ __forceinline__ int dswz(int row, int piece) {
   const int r = row & 15;
-  return row * 256 + ((piece ^ (((r & 7) << 1) | ((r ^ (r >> 2) ^ (r >> 3)) & 1))) << 4);
+  const int f = ((r & 1) << 1) | (((r >> 1) & 1) << 2) | (((r >> 1) ^ (r >> 3)) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+  return row * 256 + ((piece ^ f) << 4);
 }
 
 // Slot permutation of the fp8 V chunk's 128-byte rows (eight 16-byte pieces,
@@ -266,11 +268,22 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
           const int r = kB * b + 8 * i + (lane >> 3);
           const int p8 = lane & 7;
           const bool live = !TAIL || t0 + r < plen;
+          // Lane p8 widens its 16 codes into bf16 pieces 2 p8 and 2 p8 + 1;
+          // lanes 4-7 of each eight store the odd piece first, so each store
+          // instruction's eight lanes (one pass) cover all eight 16-byte bank
+          // groups of a 128-byte pass
+          const bool odd_first = p8 >= 4;
+          const u32x4 c = bk[b][i];
+          const uint32_t c0 = odd_first ? c[2] : c[0], c1 = odd_first ? c[3] : c[1];
+          const uint32_t c2 = odd_first ? c[0] : c[2], c3 = odd_first ? c[1] : c[3];
           uint32_t kb[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) fp8x4_to_bf16x4(bk[b][i][e], kb[2 * e], kb[2 * e + 1]);
-          st16(k_lds + dswz(r, 2 * p8), u32x4{kb[0], kb[1], kb[2], kb[3]});
-          st16(k_lds + dswz(r, 2 * p8 + 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
+          fp8x4_to_bf16x4(c0, kb[0], kb[1]);
+          fp8x4_to_bf16x4(c1, kb[2], kb[3]);
+          fp8x4_to_bf16x4(c2, kb[4], kb[5]);
+          fp8x4_to_bf16x4(c3, kb[6], kb[7]);
+          const int pc0 = 2 * p8 + (odd_first ? 1 : 0);
+          st16(k_lds + dswz(r, pc0), u32x4{kb[0], kb[1], kb[2], kb[3]});
+          st16(k_lds + dswz(r, pc0 ^ 1), u32x4{kb[4], kb[5], kb[6], kb[7]});
           // V codes as loaded (zero codes past the partition: +0)
           st16(v_lds + r * 128 + ((p8 ^ f8_slot(r)) << 4), live ? bv[b][i] : u32x4{0, 0, 0, 0});
         }
@@ -390,8 +403,9 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
   // ---- merge the four waves: lane (n, g) holds O^T[16 dt + 4 g + j][head n] ----
   const float l_head = sum_xor32(sum_xor16(l_run));
   __syncthreads();  // every wave is done with its LDS region
-  // rows of kMoRow floats: the 16 head rows a store instruction writes start
-  // 4 banks apart (a 128-float row would put them all on one bank)
+  // rows of kMoRow floats: the eight lanes a 16-byte store serves together
+  // (heads n .. n + 7) start 16 bytes apart modulo the 128 bytes of a pass (a
+  // 128-float row would put them on one bank group, 136 on every other)
   constexpr int kMoRow = D + 4;
   float* mo = reinterpret_cast<float*>(smem);     // [wave][head][kMoRow]
   float* mml = mo + kW * kMaxHeads * kMoRow;      // [wave][head][2]

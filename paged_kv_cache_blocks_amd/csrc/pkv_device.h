@@ -156,18 +156,28 @@ __device__ __forceinline__ void set_priority_for_progress(int done, int total) {
 // ---- matrix-core tiles (d = 128, bf16) ----
 // LDS layout of a K or V tile: row r (one token) is 256 bytes (all 64 banks),
 // its 16 pieces of 16 bytes with piece c stored in slot c ^ f(r % 16), f a
-// permutation of 0..15 with f >> 1 = r & 7, so both read patterns hit distinct
-// banks: the score MFMAs read one piece of 16 consecutive rows (f is
-// one-to-one), the transposing value reads read pieces {2j, 2j + 1} of 8
-// aligned rows (f >> 1 differs there, and the low bit covers both pieces).
-// The low bit differs per kernel:
-//   prefill, whose direct-to-LDS loads apply the permutation to the global
-//   addresses: ((r >> 2) ^ (r >> 3)) & 1, constant over the four rows of one
-//   load instruction (the alternative below made the prefill 62 % slower);
-//   decode, which stages from registers: (r ^ (r >> 2) ^ (r >> 3)) & 1 (see
-//   dswz in decode_mfma.hip), so that the fp8 staging, two consecutive rows
-//   per 16 lanes and the pieces 2j (or 2j + 1) of each, fills the even and
-//   the odd slots.
+// permutation of 0..15 (linear over GF(2)).  Measured on gfx950 (a lane-pair probe
+// under rocprofv3's bank-conflict counter): a 16-byte LDS access serves its 64
+// lanes in four passes of 16, pass = (lane >> 5, parity of (lane >> 2) & 7),
+// e.g. lanes 0-3, 12-15 and 20-27 together; an 8-byte access (the transposing
+// reads included) in two passes of 32 consecutive lanes.  Under that rule the
+// patterns to serve are:
+//   the score MFMAs' K reads, one piece per 16 lanes of 16 consecutive rows
+//   (lane (n, g) reads row n, piece 4 s + g): f must map rows {0..3, 12..15}
+//   and {4..11} each onto whole slot pairs {2j, 2j + 1};
+//   the transposing V reads, pieces {2j, 2j + 1} of rows 0..7 (and 8..15):
+//   f >> 1 one-to-one on each;
+//   the prefill's FP8 widening writes (lane l: row l / 4, pieces 4 (l % 4) + i).
+// The prefill's direct-to-LDS loads apply the permutation to global addresses
+// and are fast only if bit 0 of f is the same for the four rows one load
+// instruction brings (a variant without that ran 62 % slower).  The function
+// below keeps that, and leaves 2-way conflicts on the K reads (a third of the
+// prefill's LDS-active cycles): the conflict-free permutation (r0, r1, r2 ^ r3
+// in bits 1, 2, 3 and r2 in bit 0) measured zero conflict cycles and ran 1-3 %
+// slower in same-box runs (449.6 and 457.1 us against 444.5 and 444.3 us),
+// the prefill not being bound by LDS.  The decode, which stages from
+// registers and writes two consecutive fp8 rows per 16 lanes, uses its own
+// conflict-free permutation (dswz in decode_mfma.hip).
 __device__ __forceinline__ int swz_f(int r) { return ((r & 7) << 1) | (((r >> 2) ^ (r >> 3)) & 1); }
 __device__ __forceinline__ int swz(int row, int piece) { return row * 256 + ((piece ^ swz_f(row & 15)) << 4); }
 
