@@ -350,7 +350,12 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(PrefillArgs a) {
       inv_vs[b] = wk ? 0.f : c_w / vcw;  // 1 / vs
     }
 
-    // ---- S^T: eight 16-key tiles x two row tiles, one product each
+    // ---- S^T: eight 16-key tiles x two row tiles, one product each.  A wave
+    // in a product phase is preferred at issue over one in its softmax (value
+    // products most), so the matrix core keeps its queue while the other
+    // wave on the SIMD quantises weights in the slots between (measured 3-5 %
+    // faster than equal priorities)
+    __builtin_amdgcn_s_setprio(1);
     f32x4 sc[8][NT];
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
@@ -367,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(PrefillArgs a) {
     }
 
     // ---- mask, online softmax, quantised weights
+    __builtin_amdgcn_s_setprio(0);
     const int kb = t * KT;
     if ((a.causal && kb + KT - 1 > diag_w) || (kb + KT > total)) {
       no_if_conversion();
@@ -443,6 +449,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(PrefillArgs a) {
       }
     }
 
+    __builtin_amdgcn_s_setprio(2);
     // ---- O^T += V^T W^T: per 16-d tile dt, lane (m, g) needs the bytes
     // V[32 b + 8 g + e][16 dt + m], four transposing reads of the eight keys
     // 32 b + 8 g .. + 7 (lane L of the group reads row L / 2, bytes
@@ -464,6 +471,7 @@ __global__ __launch_bounds__(256, 2) void prefill_fp8_kernel(PrefillArgs a) {
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- normalise and store: lane (nn, g) holds d = 16 dt + 4 g + j of its row
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
