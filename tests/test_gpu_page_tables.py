@@ -4,6 +4,7 @@ fixed partitions and the work-queue split), chunked prefill (bf16 and fp8),
 quantising append, slot indexing / append / gather, and the CSR expansion.
 Expected values come from the oracle, which walks any block size and takes
 CSR rows as per-request page lists."""
+import dataclasses
 import json
 import os
 
@@ -250,3 +251,70 @@ def test_csr_random_fp8(pkv, B):
                                c.n_q, c.n_kv, c.scale)
     assert_parity(got, want, "fp8")
     assert np.all(got[0] == 0)
+
+
+def _stale_fp8(table, need, k_scale, v_scale):
+    """Blocks no sequence uses get non-finite scales (NaN, +inf, -inf in
+    turn: a free block's scale slot may hold anything), and every table entry
+    past a sequence's last block names one of them, as a stale or reused table
+    row would."""
+    nb = k_scale.shape[0]
+    unused = np.setdiff1d(np.arange(nb), table[table >= 0])
+    assert unused.size > 0
+    bad = np.array([np.nan, np.inf, -np.inf], np.float32)
+    ks, vs = k_scale.copy(), v_scale.copy()
+    ks[unused] = bad[np.arange(unused.size) % 3][:, None]
+    vs[unused] = bad[(np.arange(unused.size) + 1) % 3][:, None]
+    tb = table.copy()
+    for s in range(tb.shape[0]):
+        tail = tb.shape[1] - need[s]
+        tb[s, need[s]:] = unused[np.arange(tail) % unused.size]
+    return tb, ks, vs
+
+
+@pytest.mark.parametrize("d,n_q,n_kv", [(128, 64, 8), (64, 8, 2)])
+def test_fp8_decode_ignores_scales_past_the_sequence(pkv, d, n_q, n_kv):
+    """With 8-token blocks a sequence whose length mod 16 is 1..8 ends on a
+    16-token tile whose second half lies wholly past it; the kernels must not
+    let that half's block scale (here non-finite, through a stale table entry)
+    meet the zero weights of its masked keys."""
+    B = 8
+    lens = [1, 8, 17, 24, 100, 257, 2500, 5000]
+    need = [synth.blocks_for(L, B) for L in lens]
+    c = synth.make_decode_case(config=956, layer=d, n_q=n_q, n_kv=n_kv, d=d, seq_lens=lens, kv_dtype="fp8",
+                               block_size=B, num_blocks=sum(need) + 7, max_blocks=max(need) + 3)
+    tb, ks, vs = _stale_fp8(c.block_table, need, c.k_scale, c.v_scale)
+    c = dataclasses.replace(c, block_table=tb, k_scale=ks, v_scale=vs)
+    want = oracle_decode(c)
+    for pt in ((0, 512, -1) if d == 64 else (0, 512)):
+        note(f"fp8 decode d={d} B=8, non-finite scales behind stale entries, partition_tokens={pt}")
+        got = run_decode(pkv, c, partition_tokens=pt)
+        assert np.all(np.isfinite(got))
+        assert_parity(got, want, "fp8")
+
+
+@pytest.mark.parametrize("products", ["widened", "fp8"])
+def test_fp8_prefill_ignores_scales_past_the_keys(pkv, products):
+    B = 8
+    ctx = [0, 3, 17, 40, 300]
+    ql = [1, 5, 7, 33, 100]
+    p = synth.make_prefill_case(config=957, layer=0, n_q=32, n_kv=8, d=128, context_lens=ctx, q_len=ql,
+                                kv_dtype="fp8", block_size=B,
+                                num_blocks=sum(synth.blocks_for(c + q, B) for c, q in zip(ctx, ql)) + 7)
+    need = [synth.blocks_for(c + q, B) for c, q in zip(ctx, ql)]
+    tb, ks, vs = _stale_fp8(p.block_table, need, p.k_scale, p.v_scale)
+    q_lens = np.diff(p.cu_q_lens)
+    args = (dev(p.q, "bf16"), dev(p.cu_q_lens), dev(p.context_lens), int(q_lens.max()), dev(p.k_cache),
+            dev(p.v_cache), dev(tb), p.n_q, p.n_kv, p.d, B, p.scale)
+    kw = dict(causal=True, k_scale=dev(ks), v_scale=dev(vs))
+    note(f"fp8 prefill ({products} products) B=8, non-finite scales behind stale entries")
+    if products == "fp8":
+        out = pkv.paged_attn_prefill_chunk_fp8_mma(*args, **kw)
+    else:
+        out = pkv.paged_attn_prefill_chunk(*args, **kw)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    want = oracle.paged_prefill(p.q, "bf16", p.cu_q_lens, p.context_lens, p.k_cache, p.v_cache, "fp8", ks, vs, tb,
+                                p.n_q, p.n_kv, p.scale, causal=True)
+    assert np.all(np.isfinite(got))
+    assert_parity(got, want, "fp8")
