@@ -6,13 +6,14 @@ A step is one pass of the whole hot path over one batch, on inputs already
 resident in HBM:
   * decode workloads: slot indexing for the batch's current token, the
     step's work order (the batch ranked by length once, shared by every
-    layer), kv_append of that token's K/V rows into every layer's cache, then
-    paged decode attention of every layer, back to back (each layer's append
-    precedes its attention; with no model between the layers the two orders do
-    the same work, and back-to-back calls keep launch gaps out of the decode
-    timing);
-  * prefill workload: slot indexing of the chunk, kv_append of its 8,192
-    new rows, chunked-prefill attention.
+    layer), kv_append of that token's K/V rows into every layer's cache (a
+    one-layer step indexes and appends in one launch, kv_append_positions),
+    then paged decode attention of every layer, back to back (each layer's
+    append precedes its attention; with no model between the layers the two
+    orders do the same work, and back-to-back calls keep launch gaps out of
+    the decode timing);
+  * prefill workload: slot indexing and append of the chunk's 8,192 new rows
+    (one launch), chunked-prefill attention.
 With --fp8-append quantize the FP8 workload's append takes the token's rows
 in bf16 and quantises them into the cache (kv_append_fp8: per-block scale
 update, re-encoding when a scale grows) instead of copying ready-made codes.
@@ -229,9 +230,17 @@ class DecodeWorkload:
     calls_per_event = property(lambda self: self.layers)
 
     def prep(self):
-        """Slot mapping, work order and every layer's append for the batch's current token."""
+        """Slot indexing, work order and every layer's append for the batch's
+        current token.  Several layers share one slot mapping, each layer's
+        append copying through it; a one-layer step indexes and appends in one
+        launch (kv_append_positions, which also stores the slots).  (Measured
+        on the 8B-shaped step: the fused call per layer, re-walking the table
+        32 times, is 0.6 % slower than one slot mapping; on the one-layer step
+        one launch less is 15 % faster.)"""
         pkv = self.pkv
-        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
+        fused = self.layers == 1 and not self.quantize_append
+        if not fused:
+            pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
         if not self.csr:
             # one work order per step, shared by every layer's decode (same batch, same lengths)
             pkv.paged_attn_decode_order(self.seq_lens_t, self.n_q, self.n_kv, self.d, self.max_blocks, self.bs,
@@ -240,6 +249,9 @@ class DecodeWorkload:
             if self.quantize_append:
                 pkv.kv_append_fp8(self.k[layer], self.v[layer], self.ks[layer], self.vs[layer], self.block_table,
                                   self.positions, self.cu_new, 1, self.k_new[layer], self.v_new[layer])
+            elif fused:
+                pkv.kv_append_positions(self.k[layer], self.v[layer], self.block_table, self.seq_ids, self.positions,
+                                        self.k_new[layer], self.v_new[layer], slot_mapping_out=self.slots)
             else:
                 pkv.kv_append(self.k[layer], self.v[layer], self.slots, self.k_new[layer], self.v_new[layer])
 
@@ -369,13 +381,15 @@ class PrefillWorkload:
 
     def step(self, events=None):
         pkv = self.pkv
-        pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
         if self.kind == "fp8":
             # the chunk's bf16 rows are quantised into the cache
+            pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, 16, out=self.slots)
             pkv.kv_append_fp8(self.k, self.v, self.ks, self.vs, self.block_table, self.ctx_t, self.cu, self.q_len,
                               self.k_new, self.v_new)
         else:
-            pkv.kv_append(self.k, self.v, self.slots, self.k_new, self.v_new)
+            # slot indexing and append in one launch
+            pkv.kv_append_positions(self.k, self.v, self.block_table, self.seq_ids, self.positions, self.k_new,
+                                    self.v_new, slot_mapping_out=self.slots)
         if events is not None:
             events[0].record()
         self.attn_call()

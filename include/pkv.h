@@ -133,6 +133,22 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
                          const int64_t* slot_mapping, const void* k, const void* v, int32_t num_tokens,
                          int32_t n_kv_heads, int32_t d_head, int32_t block_size, void* stream);
 
+/* Slot indexing and append in one launch: for every token t,
+ *   slot = block_table[seq_ids[t]][positions[t] / B] * B + positions[t] % B
+ * exactly as pkv_slot_mapping computes it (-1 for a pair outside the table or
+ * a negative entry), then its K and V rows are copied as pkv_kv_append copies
+ * them (a slot < 0 or >= num_blocks * B is skipped).  The result equals
+ * pkv_slot_mapping followed by pkv_kv_append, bit for bit; the pages' append
+ * step ([FP] "Deriving the cache"; [KVP] Problem 4, "The idea") with the
+ * table walk inside.  slot_mapping_out: (device) int64 [num_tokens] receiving
+ * the slots, or NULL.  Other arguments as pkv_slot_mapping and pkv_kv_append.
+ * num_tokens == 0 is a no-op. */
+pkv_status pkv_kv_append_positions(void* k_cache, void* v_cache, pkv_dtype cache_dtype, int64_t num_blocks,
+                                   const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_ids, const int32_t* positions, const void* k, const void* v,
+                                   int32_t num_tokens, int32_t n_kv_heads, int32_t d_head, int32_t block_size,
+                                   int64_t* slot_mapping_out, void* stream);
+
 /* Append with FP8 quantisation ([KVP] Problem 3: an FP8 cache takes half the
  * bytes of a 16-bit one; [MEM] "Long-context optimization": quantising the
  * cached keys and values shrinks the per-token cost).  The pages fix neither

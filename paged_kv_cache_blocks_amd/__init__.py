@@ -35,6 +35,8 @@ _SIGS = {
     "pkv_device_checks": ([], ctypes.c_int),
     "pkv_slot_mapping": ([_vp, _i32, _i32, _vp, _vp, _i32, _i32, _vp, _vp], ctypes.c_int),
     "pkv_kv_append": ([_vp, _vp, ctypes.c_int, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp], ctypes.c_int),
+    "pkv_kv_append_positions": ([_vp, _vp, ctypes.c_int, _i64, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                 _i32, _vp, _vp], ctypes.c_int),
     "pkv_kv_append_fp8": ([_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, ctypes.c_int, _i32,
                            _i32, _i32, _vp], ctypes.c_int),
     "pkv_paged_gather": ([_vp, _vp, _vp, _vp, ctypes.c_int, _i64, _vp, _i32, _vp, _vp, _i64, _i32, _i32, _i32, _i32,
@@ -192,6 +194,33 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: torch.
         raise ValueError("k, v must be [num_tokens, n_kv, d]")
     _check(load().pkv_kv_append(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, _ptr(slot_mapping), _ptr(k),
                              _ptr(v), slot_mapping.numel(), n_kv, d, bs, _stream(stream)))
+
+
+def kv_append_positions(k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        seq_ids: torch.Tensor, positions: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                        slot_mapping_out: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Slot indexing and append in one launch: k[t], v[t] ([num_tokens, n_kv, d])
+    go to position positions[t] of sequence seq_ids[t] through block_table;
+    the slots are also stored in slot_mapping_out (int64) when given."""
+    _need(block_table, torch.int32, "block_table")
+    _need(seq_ids, torch.int32, "seq_ids")
+    _need(positions, torch.int32, "positions")
+    n = seq_ids.numel()
+    if positions.numel() != n:
+        raise ValueError("seq_ids and positions differ in length")
+    nb, n_kv, bs, d = k_cache.shape
+    if k.dtype != k_cache.dtype or v.dtype != v_cache.dtype or v_cache.shape != k_cache.shape:
+        raise TypeError("k/v must match the caches")
+    if k.shape != (n, n_kv, d) or v.shape != k.shape:
+        raise ValueError("k, v must be [num_tokens, n_kv, d]")
+    if slot_mapping_out is not None:
+        _need(slot_mapping_out, torch.int64, "slot_mapping_out")
+        if slot_mapping_out.numel() < n:
+            raise ValueError("slot_mapping_out holds fewer than num_tokens entries")
+    _check(load().pkv_kv_append_positions(_ptr(k_cache), _ptr(v_cache), dtype_code(k_cache), nb, _ptr(block_table),
+                                       block_table.shape[0], block_table.shape[1], _ptr(seq_ids), _ptr(positions),
+                                       _ptr(k), _ptr(v), n, n_kv, d, bs,
+                                       None if slot_mapping_out is None else _ptr(slot_mapping_out), _stream(stream)))
 
 
 def kv_append_fp8(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,

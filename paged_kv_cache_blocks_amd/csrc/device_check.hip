@@ -67,6 +67,27 @@ __global__ __launch_bounds__(256) void check_slots_kernel(const int64_t* __restr
   if (m && (threadIdx.x & 63) == __builtin_ctzll(m)) atomicAdd(err, (int)__builtin_popcountll(m));
 }
 
+// Slots an append through the table would write: one per (sequence id,
+// position) pair, computed as the slot indexing does; a slot at or past
+// `limit` counts as bad (-1, padding, does not).
+__global__ __launch_bounds__(256) void check_positions_kernel(const int32_t* __restrict__ table, int32_t batch,
+                                                              int32_t max_blocks, const int32_t* __restrict__ seq_ids,
+                                                              const int32_t* __restrict__ positions, int32_t n,
+                                                              int32_t block_size, int64_t limit,
+                                                              int32_t* __restrict__ err) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int bad = 0;
+  if (t < n) {
+    const int s = seq_ids[t], p = positions[t];
+    if (s >= 0 && s < batch && p >= 0 && p < max_blocks * block_size) {
+      const int blk = table[(int64_t)s * max_blocks + p / block_size];
+      bad = (blk >= 0 && (int64_t)blk * block_size + p % block_size >= limit) ? 1 : 0;
+    }
+  }
+  const uint64_t m = __builtin_amdgcn_ballot_w64(bad != 0);
+  if (m && (threadIdx.x & 63) == __builtin_ctzll(m)) atomicAdd(err, (int)__builtin_popcountll(m));
+}
+
 // Clears n 32-bit words: a kernel rather than a memset, so that a stream
 // being captured into a graph records a kernel node.
 __global__ __launch_bounds__(256) void zero_words_kernel(int32_t* __restrict__ p, int32_t n) {
@@ -86,6 +107,15 @@ hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t limit, in
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(check_slots_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, slots, n, limit,
                      err);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_positions(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
+                                  const int32_t* positions, int32_t n, int32_t block_size, int64_t limit, int32_t* err,
+                                  hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(check_positions_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, table, batch,
+                     max_blocks, seq_ids, positions, n, block_size, limit, err);
   return hipGetLastError();
 }
 

@@ -11,20 +11,25 @@
 
 namespace pkv {
 
+// Slot of (sequence s, position p), or -1 (padding) for a pair outside the
+// table or a negative table entry.
+__device__ __forceinline__ int64_t slot_of(const int32_t* __restrict__ table, int32_t batch, int32_t max_blocks,
+                                           int s, int p, int32_t block_size) {
+  int64_t slot = -1;
+  if (s >= 0 && s < batch && p >= 0 && p < max_blocks * block_size) {
+    const int blk = table[(int64_t)s * max_blocks + p / block_size];
+    if (blk >= 0) slot = (int64_t)blk * block_size + p % block_size;
+  }
+  return slot;
+}
+
 __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* __restrict__ table, int32_t batch,
                                                            int32_t max_blocks, const int32_t* __restrict__ seq_ids,
                                                            const int32_t* __restrict__ positions, int32_t n,
                                                            int32_t block_size, int64_t* __restrict__ out) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= n) return;
-  const int s = seq_ids[t];
-  const int p = positions[t];
-  int64_t slot = -1;
-  if (s >= 0 && s < batch && p >= 0 && p < max_blocks * block_size) {
-    const int blk = table[(int64_t)s * max_blocks + p / block_size];
-    if (blk >= 0) slot = (int64_t)blk * block_size + p % block_size;
-  }
-  out[t] = slot;
+  out[t] = slot_of(table, batch, max_blocks, seq_ids[t], positions[t], block_size);
 }
 
 // One thread moves 16 bytes; a row of one KV head is row_bytes (a multiple of
@@ -42,6 +47,32 @@ __global__ __launch_bounds__(256) void kv_append_kernel(char* __restrict__ k_cac
   const int h = (int)((i / pieces) % n_kv);
   const int t = (int)(i / ((int64_t)pieces * n_kv));
   const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size, off = slot % block_size;
+  const int64_t dst = ((blk * n_kv + h) * block_size + off) * row_bytes + piece * 16;
+  const int64_t src = ((int64_t)t * n_kv + h) * row_bytes + piece * 16;
+  if (blockIdx.y == 0) st16(k_cache + dst, ld16(k + src));
+  else st16(v_cache + dst, ld16(v + src));
+}
+
+// Slot indexing and append in one pass: each thread finds its token's slot
+// through the table (as slot_mapping_kernel) and moves its 16 bytes (as
+// kv_append_kernel); the threads of piece 0, head 0 of K also store the slot
+// when slots_out is given.  Same grid as kv_append_kernel.
+__global__ __launch_bounds__(256) void kv_append_positions_kernel(
+    char* __restrict__ k_cache, char* __restrict__ v_cache, int64_t num_slots, const int32_t* __restrict__ table,
+    int32_t batch, int32_t max_blocks, const int32_t* __restrict__ seq_ids, const int32_t* __restrict__ positions,
+    const char* __restrict__ k, const char* __restrict__ v, int32_t n, int32_t n_kv, int32_t row_bytes,
+    int32_t block_size, int64_t* __restrict__ slots_out) {
+  const int pieces = row_bytes / 16;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n * n_kv * pieces;
+  if (i >= total) return;
+  const int piece = (int)(i % pieces);
+  const int h = (int)((i / pieces) % n_kv);
+  const int t = (int)(i / ((int64_t)pieces * n_kv));
+  const int64_t slot = slot_of(table, batch, max_blocks, seq_ids[t], positions[t], block_size);
+  if (slots_out && blockIdx.y == 0 && h == 0 && piece == 0) slots_out[t] = slot;
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size, off = slot % block_size;
   const int64_t dst = ((blk * n_kv + h) * block_size + off) * row_bytes + piece * 16;
@@ -327,6 +358,19 @@ hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_blocks, co
   hipLaunchKernelGGL(kv_append_kernel, grid, dim3(256), 0, stream, (char*)k_cache, (char*)v_cache,
                      num_blocks * block_size, slots, (const char*)k, (const char*)v, n, n_kv, row_bytes,
                      block_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_append_positions(void* k_cache, void* v_cache, int64_t num_blocks, const int32_t* table,
+                                      int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
+                                      const int32_t* positions, const void* k, const void* v, int32_t n, int32_t n_kv,
+                                      int32_t row_bytes, int32_t block_size, int64_t* slots_out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const int64_t total = (int64_t)n * n_kv * (row_bytes / 16);
+  dim3 grid((unsigned)((total + 255) / 256), 2);
+  hipLaunchKernelGGL(kv_append_positions_kernel, grid, dim3(256), 0, stream, (char*)k_cache, (char*)v_cache,
+                     num_blocks * block_size, table, batch, max_blocks, seq_ids, positions, (const char*)k,
+                     (const char*)v, n, n_kv, row_bytes, block_size, slots_out);
   return hipGetLastError();
 }
 

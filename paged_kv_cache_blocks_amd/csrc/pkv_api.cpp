@@ -422,6 +422,35 @@ pkv_status pkv_kv_append(void* k_cache, void* v_cache, pkv_dtype cache_dtype, in
                     "kv_append launch");
 }
 
+pkv_status pkv_kv_append_positions(void* k_cache, void* v_cache, pkv_dtype cache_dtype, int64_t num_blocks,
+                                   const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_ids, const int32_t* positions, const void* k, const void* v,
+                                   int32_t num_tokens, int32_t n_kv_heads, int32_t d_head, int32_t block_size,
+                                   int64_t* slot_mapping_out, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens must be >= 0");
+  if (!valid_dtype(cache_dtype)) return fail(PKV_ERR_INVALID_ARG, "unknown cache dtype %d", (int)cache_dtype);
+  if (num_tokens == 0) return ok();
+  if (!k_cache || !v_cache || !block_table || !seq_ids || !positions || !k || !v)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer");
+  if (num_blocks < 1 || batch < 1 || max_blocks_per_seq < 1 || n_kv_heads < 1 || d_head < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "sizes must be positive");
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return fail(PKV_ERR_INVALID_ARG, "table too wide");
+  const int row_bytes = d_head * elem_bytes(cache_dtype);
+  if (row_bytes % 16) return fail(PKV_ERR_UNSUPPORTED, "a row of %d bytes is not a multiple of 16", row_bytes);
+  if (device_checks_on()) {
+    const pkv_status st = run_device_check((hipStream_t)stream, "kv_append_positions", [&](int32_t* cnt) {
+      return pkv::launch_check_positions(block_table, batch, max_blocks_per_seq, seq_ids, positions, num_tokens,
+                                         block_size, num_blocks * block_size, cnt, (hipStream_t)stream);
+    });
+    if (st != PKV_OK) return st;
+  }
+  return hip_status(pkv::launch_kv_append_positions(k_cache, v_cache, num_blocks, block_table, batch,
+                                                    max_blocks_per_seq, seq_ids, positions, k, v, num_tokens,
+                                                    n_kv_heads, row_bytes, block_size, slot_mapping_out,
+                                                    (hipStream_t)stream),
+                    "kv_append_positions launch");
+}
+
 pkv_status pkv_kv_append_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, int64_t num_blocks,
                              const int32_t* block_table, int32_t max_blocks_per_seq, const int32_t* context_lens,
                              const int32_t* cu_new_lens, int32_t batch, int32_t max_new_len, const void* k_new,

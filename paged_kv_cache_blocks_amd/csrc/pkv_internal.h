@@ -74,6 +74,10 @@ hipError_t launch_slot_mapping(const int32_t* table, int32_t batch, int32_t max_
 hipError_t launch_kv_append(void* k_cache, void* v_cache, int64_t num_blocks, const int64_t* slots, const void* k,
                             const void* v, int32_t n, int32_t n_kv, int32_t row_bytes, int32_t block_size,
                             hipStream_t stream);
+hipError_t launch_kv_append_positions(void* k_cache, void* v_cache, int64_t num_blocks, const int32_t* table,
+                                      int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
+                                      const int32_t* positions, const void* k, const void* v, int32_t n, int32_t n_kv,
+                                      int32_t row_bytes, int32_t block_size, int64_t* slots_out, hipStream_t stream);
 hipError_t launch_gather(void* k_out, void* v_out, const void* k_cache, const void* v_cache, int64_t num_blocks,
                          const int32_t* table, int32_t max_blocks, const int32_t* seq_lens, const int64_t* cu,
                          int64_t total_rows, int32_t batch, int32_t n_kv, int32_t row_bytes, int32_t block_size,
@@ -115,6 +119,9 @@ struct SeqCheck {
 };
 hipError_t launch_check_seqs(const SeqCheck& c, int32_t* err, hipStream_t stream);
 hipError_t launch_check_slots(const int64_t* slots, int32_t n, int64_t limit, int32_t* err, hipStream_t stream);
+hipError_t launch_check_positions(const int32_t* table, int32_t batch, int32_t max_blocks, const int32_t* seq_ids,
+                                  const int32_t* positions, int32_t n, int32_t block_size, int64_t limit, int32_t* err,
+                                  hipStream_t stream);
 hipError_t launch_zero_words(int32_t* p, int32_t n, hipStream_t stream);
 
 struct PrefillArgs {

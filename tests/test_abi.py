@@ -193,6 +193,24 @@ def test_other_entry_points_validate(pkv):
     assert lib.pkv_kv_append(None, None, 1, 1, None, None, None, 0, 8, 128, 16, None) == pkv.OK
     assert lib.pkv_kv_append(0x1000, 0x1000, 7, 1, 0x1000, 0x1000, 0x1000, 1, 8, 128, 16, None) == pkv.ERR_INVALID_ARG
     assert lib.pkv_kv_append(0x1000, 0x1000, 2, 1, 0x1000, 0x1000, 0x1000, 1, 8, 8, 16, None) == pkv.ERR_UNSUPPORTED
+    ap = lib.pkv_kv_append_positions
+    good = [0x1000, 0x2000, 1, 4, 0x3000, 2, 8, 0x4000, 0x5000, 0x6000, 0x7000, 3, 8, 128, 16, None, None]
+    args = list(good); args[11] = 0
+    assert ap(*args) == pkv.OK                       # no tokens: no-op
+    args = list(good); args[11] = -1
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # negative token count
+    args = list(good); args[7] = None
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # no sequence ids
+    args = list(good); args[4] = None
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # no table
+    args = list(good); args[2] = 7
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # unknown dtype
+    args = list(good); args[5] = 0
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # no sequences
+    args = list(good); args[2] = 2; args[13] = 8
+    assert ap(*args) == pkv.ERR_UNSUPPORTED          # 8-byte fp8 rows
+    args = list(good); args[6] = 1 << 27
+    assert ap(*args) == pkv.ERR_INVALID_ARG          # table wider than 2^30 tokens
     fa = lib.pkv_kv_append_fp8
     good = [0x1000, 0x2000, 0x3000, 0x4000, 8, 0x5000, 2, 0x6000, 0x7000, 1, 4, 0x8000, 0x9000, 1, 2, 128, 16, None]
     args = list(good); args[10] = 0

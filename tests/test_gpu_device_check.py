@@ -129,6 +129,28 @@ def test_append_bad_slot_rejected(checks):
     assert k_cache.view(torch.int16).flatten()[:d].eq(0x3F80).all()
 
 
+def test_append_positions_bad_entry_rejected(checks):
+    """The fused slot indexing + append: a table entry at or past the pool
+    fails the check; pairs outside the table and negative entries are padding."""
+    pkv = checks
+    nb, n_kv, d = 6, 2, 64
+    k_cache = torch.zeros((nb, n_kv, 16, d), dtype=torch.bfloat16, device="cuda")
+    v_cache = torch.zeros_like(k_cache)
+    k = torch.ones((4, n_kv, d), dtype=torch.bfloat16, device="cuda")
+    table = dev(np.array([[0, nb], [-1, 5]], np.int32))
+    seq = dev(np.array([0, 0, 1, 2], np.int32))
+    pos = dev(np.array([3, 20, 4, 0], np.int32))  # (0, 20) -> entry nb: bad; (1, 4) -> -1; seq 2: padding
+    _expect_check_failure(pkv, lambda: pkv.kv_append_positions(k_cache, v_cache, table, seq, pos, k, k),
+                          "table entry = num_blocks")
+    torch.cuda.synchronize()
+    assert not torch.any(k_cache.view(torch.int16)) and not torch.any(v_cache.view(torch.int16))
+    pos_ok = dev(np.array([3, 5, 4, 0], np.int32))
+    pkv.kv_append_positions(k_cache, v_cache, table, seq, pos_ok, k, k)
+    torch.cuda.synchronize()
+    assert k_cache.view(torch.int16)[0, :, 3].eq(0x3F80).all() and k_cache.view(torch.int16)[0, :, 5].eq(0x3F80).all()
+    assert int(torch.count_nonzero(k_cache.view(torch.int16))) == 2 * n_kv * d
+
+
 def test_prefill_and_fp8_append_rejected(checks):
     pkv = checks
     p = synth.make_prefill_case(config=991, layer=0, n_q=32, n_kv=8, d=128, context_lens=[20, 50], q_len=[10, 30])

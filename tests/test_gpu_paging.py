@@ -107,3 +107,49 @@ def test_check_tables_counts_bad_entries(pkv):
     note("check_tables")
     assert pkv.check_tables(dev(table), dev(lens), num_blocks=8) == 2
     assert pkv.check_tables(dev(table[:1]), dev(lens[:1]), num_blocks=8) == 0
+
+
+@pytest.mark.parametrize("kind,d,B", [("bf16", 128, 16), ("f32", 64, 8), ("fp8", 128, 64), ("bf16", 64, 256)])
+def test_append_positions_equals_slot_mapping_then_append(pkv, kind, d, B):
+    """The fused slot indexing + append writes the pool the oracle's slot
+    mapping + append writes, and the two-call path too, bit for bit; its slot
+    output equals the slot mapping's, padding pairs included (ids and
+    positions outside the table, negative entries, a table entry past the
+    pool)."""
+    r = np.random.default_rng(11 + B)
+    n_kv = 4
+    lens = [1, B, B + 1, 3 * B + 5, 7, 0]
+    nb = sum(synth.blocks_for(L, B) for L in lens) + 3
+    table, _ = synth.build_tables(lens, nb, r.permutation(nb).astype(np.int32), B)
+    table[4, 0] = nb + 2  # an entry past the pool: its slot is computed, its rows are skipped
+    dt = synth.STORAGE_DTYPE[kind]
+    eb = synth.ELEM_BYTES[kind]
+    pool_k = r.integers(0, 256, size=(nb, n_kv, B, d * eb), dtype=np.uint8).view(dt)
+    pool_v = r.integers(0, 256, size=(nb, n_kv, B, d * eb), dtype=np.uint8).view(dt)
+    seq_ids = [s for s, L in enumerate(lens) for _ in range(L)] + [-1, len(lens), 0, 2]
+    pos = [p for L in lens for p in range(L)] + [0, 0, -1, table.shape[1] * B]
+    seq_ids, pos = np.array(seq_ids, np.int32), np.array(pos, np.int32)
+    T = len(seq_ids)
+    kn = r.integers(0, 256, size=(T, n_kv, d * eb), dtype=np.uint8).view(dt)
+    vn = r.integers(0, 256, size=(T, n_kv, d * eb), dtype=np.uint8).view(dt)
+    slots = np.full(T, -1, np.int64)
+    for i, (s, p) in enumerate(zip(seq_ids, pos)):
+        if 0 <= s < len(lens) and 0 <= p < table.shape[1] * B and table[s, p // B] >= 0:
+            slots[i] = oracle.slot_of(table, int(s), int(p), B)
+    live = (slots >= 0) & (slots < nb * B)
+    want_k, want_v = oracle.kv_append(pool_k, pool_v, np.where(live, slots, -1), kn, vn)
+    note(f"append_positions {kind} d={d} B={B} T={T}")
+    tt, ts, tp, tkn, tvn = dev(table), dev(seq_ids), dev(pos), dev(kn, kind), dev(vn, kind)
+    kc, vc = dev(pool_k, kind), dev(pool_v, kind)
+    out = torch.full((T,), 7, dtype=torch.int64, device="cuda")
+    pkv.kv_append_positions(kc, vc, tt, ts, tp, tkn, tvn, slot_mapping_out=out)
+    kc2, vc2 = dev(pool_k, kind), dev(pool_v, kind)
+    s2 = pkv.slot_mapping(tt, ts, tp, B)
+    pkv.kv_append(kc2, vc2, s2, tkn, tvn)
+    kc3, vc3 = dev(pool_k, kind), dev(pool_v, kind)
+    pkv.kv_append_positions(kc3, vc3, tt, ts, tp, tkn, tvn)  # no slot output
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), slots)
+    assert np.array_equal(s2.cpu().numpy(), slots)
+    for c, w in ((kc, want_k), (vc, want_v), (kc2, want_k), (vc2, want_v), (kc3, want_k), (vc3, want_v)):
+        assert np.array_equal(host_bits(c).view(np.uint8), w.view(np.uint8))
