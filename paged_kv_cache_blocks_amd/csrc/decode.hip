@@ -190,8 +190,10 @@ __device__ __forceinline__ void issue_chunk(const DecodeArgs& a, const BlockIds&
   const char* const vc = reinterpret_cast<const char*>(a.v_cache);
 #pragma unroll
   for (int b = 0; b < Ly::CB; ++b) {
-    const int64_t half0 = (int64_t)__builtin_amdgcn_readlane(ids.row[0], c * Ly::CB + b) * Gm::row_bytes;
-    const int64_t half1 = (int64_t)__builtin_amdgcn_readlane(ids.row[1], c * Ly::CB + b) * Gm::row_bytes;
+    // row indices are unsigned 32-bit (the row space reaches 2^32): widen
+    // them without sign extension
+    const int64_t half0 = (int64_t)(uint32_t)__builtin_amdgcn_readlane(ids.row[0], c * Ly::CB + b) * Gm::row_bytes;
+    const int64_t half1 = (int64_t)(uint32_t)__builtin_amdgcn_readlane(ids.row[1], c * Ly::CB + b) * Gm::row_bytes;
 #pragma unroll
     for (int i = 0; i < Gm::NLK; ++i) {
       const int64_t off = (i < LH ? half0 : half1) + (int64_t)((i % LH) * kWave + lane) * Gm::LW;
