@@ -47,6 +47,17 @@ def test_prefill_ragged(pkv, causal, n_q, n_kv):
     assert_parity(got, want, "bf16")
 
 
+def test_prefill_long_chunks(pkv):
+    """Chunks of thousands of tokens (a whole prompt at once: 86 query tiles of
+    one sequence, with and without context before it), where the ordering of
+    query tiles and their placement over the XCDs span many workgroups per
+    (sequence, KV head)."""
+    p = synth.make_prefill_case(config=983, layer=0, n_q=8, n_kv=2, d=128, context_lens=[0, 1000],
+                                q_len=[4096, 2000])
+    note("prefill chunks of 4096 (no context) and 2000 (after 1000) tokens")
+    assert_parity(_run(pkv, p), _oracle(p), "bf16", "long chunks:")
+
+
 def test_prefill_chunk_of_one_matches_decode(pkv):
     p = synth.make_prefill_case(config=401, layer=0, n_q=32, n_kv=8, d=128, context_lens=[37, 500, 0], q_len=1)
     got = _run(pkv, p)
