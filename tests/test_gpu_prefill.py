@@ -58,6 +58,17 @@ def test_prefill_long_chunks(pkv):
     assert_parity(_run(pkv, p), _oracle(p), "bf16", "long chunks:")
 
 
+def test_prefill_many_sequences(pkv):
+    """More sequences than the kernels rank by length in LDS (256): the work
+    order falls back to plain sequence order, with the same results."""
+    r = np.random.default_rng(984)
+    ctx = r.integers(0, 60, size=300).tolist()
+    ql = r.integers(1, 12, size=300).tolist()
+    p = synth.make_prefill_case(config=984, layer=0, n_q=8, n_kv=2, d=128, context_lens=ctx, q_len=ql)
+    note("prefill over 300 short sequences")
+    assert_parity(_run(pkv, p), _oracle(p), "bf16", "300 sequences:")
+
+
 def test_prefill_chunk_of_one_matches_decode(pkv):
     p = synth.make_prefill_case(config=401, layer=0, n_q=32, n_kv=8, d=128, context_lens=[37, 500, 0], q_len=1)
     got = _run(pkv, p)

@@ -182,6 +182,17 @@ def test_fp8_mma_after_fp8_append(pkv):
     _check(pkv, p, t, want)
 
 
+def test_fp8_mma_many_sequences(pkv):
+    """More sequences than the kernel ranks in LDS: plain sequence order."""
+    r = np.random.default_rng(428)
+    ctx = r.integers(0, 60, size=300).tolist()
+    ql = r.integers(1, 12, size=300).tolist()
+    p = synth.make_prefill_case(config=428, layer=0, n_q=8, n_kv=2, d=128, context_lens=ctx, q_len=ql,
+                                kv_dtype="fp8")
+    note("fp8 products over 300 short sequences")
+    _check(pkv, p, _inputs(p), _oracle(p))
+
+
 def test_fp8_mma_rejects_bf16_cache(pkv):
     p = synth.make_prefill_case(config=427, layer=0, n_q=8, n_kv=8, d=128, context_lens=[4], q_len=[4])
     with pytest.raises(pkv.PkvError) as e:
