@@ -195,6 +195,10 @@ class DecodeWorkload:
         self.positions = (self.seq_lens_t - 1).to(torch.int32)
         self.slots = torch.empty(self.batch, dtype=torch.int64, device=dev)
         self.cu_new = torch.arange(self.batch + 1, dtype=torch.int32, device=dev)
+        # The work order balances the split over the CUs and is paid once per
+        # step; a one-layer step of a few sequences (the tiny case: 2) has
+        # nothing to balance, and decodes in plain order without its launch.
+        self.ordered = not self.csr and (self.layers > 1 or self.batch > 8)
         self.order = torch.empty(pkv.paged_attn_decode_order_entries(self.batch, self.n_q, self.n_kv, self.d,
                                                                      self.max_blocks, B, pkv.dtype_code(self.k[0])),
                                  dtype=torch.int32, device=dev)
@@ -225,7 +229,7 @@ class DecodeWorkload:
         self.pkv.paged_attn_decode(self.q[layer], self.k[layer], self.v[layer], self.block_table, self.seq_lens_t,
                                    self.n_q, self.n_kv, self.d, self.bs, self.scale, k_scale=self.ks[layer],
                                    v_scale=self.vs[layer], out=self.out[layer], workspace=self.ws,
-                                   work_order=self.order)
+                                   work_order=self.order if self.ordered else None)
 
     calls_per_event = property(lambda self: self.layers)
 
@@ -241,7 +245,7 @@ class DecodeWorkload:
         fused = self.layers == 1 and not self.quantize_append
         if not fused:
             pkv.slot_mapping(self.block_table, self.seq_ids, self.positions, self.bs, out=self.slots)
-        if not self.csr:
+        if self.ordered:
             # one work order per step, shared by every layer's decode (same batch, same lengths)
             pkv.paged_attn_decode_order(self.seq_lens_t, self.n_q, self.n_kv, self.d, self.max_blocks, self.bs,
                                         pkv.dtype_code(self.k[0]), out=self.order)
