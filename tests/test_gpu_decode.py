@@ -42,7 +42,7 @@ QUEUE = -1  # partition_tokens value that asks for the work-queue split
 
 @pytest.mark.parametrize("split", [0, QUEUE])
 @pytest.mark.parametrize("kind", ["bf16", "fp8", "f32"])
-@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8), (16, 16), (8, 1), (12, 6), (32, 2)])
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (64, 8), (16, 16), (8, 1), (12, 6), (32, 2), (64, 2), (64, 1)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_ragged_shapes(pkv, kind, n_q, n_kv, d, split):
     c = synth.make_decode_case(config=300, layer=n_q * 7 + n_kv + d, n_q=n_q, n_kv=n_kv, d=d, seq_lens=RAGGED,

@@ -36,7 +36,7 @@ def _oracle(p, causal=True):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 2), (8, 1)])
+@pytest.mark.parametrize("n_q,n_kv", [(32, 8), (8, 8), (16, 2), (8, 1), (64, 1), (128, 1)])
 def test_prefill_ragged(pkv, causal, n_q, n_kv):
     ctx = [0, 5, 16, 37, 300, 1000]
     ql = [7, 1, 33, 128, 200, 65]
