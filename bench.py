@@ -116,7 +116,7 @@ def prefill_flops(ctx_lens, q_len, n_q, d):
 
 class DecodeWorkload:
     def __init__(self, cfg_id: int, layers: int = None, fp8_append: str = "copy", block_size: int = 16,
-                 csr: bool = False):
+                 csr: bool = False, shape=None):
         import torch
         import paged_kv_cache_blocks_amd as pkv
         self.pkv, self.torch = pkv, torch
@@ -129,6 +129,12 @@ class DecodeWorkload:
         self.bs, self.csr = block_size, csr
         B = block_size
         self.seq_lens = synth.config_seq_lens(cfg_id)
+        if shape is not None:
+            # the workload's heads and element type, with `batch` sequences of
+            # `length` tokens each
+            batch, length = shape
+            self.seq_lens = np.full(batch, length, dtype=np.int32)
+            self.name = f"{self.name} at batch {batch} x {length} tokens"
         self.batch = len(self.seq_lens)
         dev = torch.device("cuda")
         need = sum(synth.blocks_for(L, B) for L in self.seq_lens)
@@ -731,6 +737,15 @@ def main():
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32, 64, 128, 256],
                     help="decode workloads: tokens per cache block (the same sequences, re-paged)")
     ap.add_argument("--csr", action="store_true", help="decode workloads: pass the page table in CSR form")
+
+    def _shape(text):
+        b, _, n = text.partition("x")
+        if not (b.isdigit() and n.isdigit() and int(b) > 0 and int(n) > 0):
+            raise argparse.ArgumentTypeError("shape is BATCHxTOKENS, e.g. 1x32768")
+        return int(b), int(n)
+    ap.add_argument("--shape", type=_shape, default=None,
+                    help="decode workloads: BATCHxTOKENS sequences of equal length instead of the workload's mix "
+                         "(a shape sweep; the line is not the workload's headline)")
     ap.add_argument("--prefill-kv", choices=["bf16", "fp8", "fp8-mma", "fp8-mma-single"], default="bf16",
                     help="prefill workload: KV cache element type (fp8: the chunk is quantised on append and the "
                          "codes widened to bf16 for the products; fp8-mma: the same cache with both products in "
@@ -778,7 +793,7 @@ def main():
         return
     t_build = time.perf_counter()
     w = (PrefillWorkload(cfg, args.prefill_kv) if prefill
-         else DecodeWorkload(cfg, args.layers, args.fp8_append, args.block_size, args.csr))
+         else DecodeWorkload(cfg, args.layers, args.fp8_append, args.block_size, args.csr, args.shape))
     print(f"[bench] built {args.workload} in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
