@@ -659,7 +659,7 @@ def read_probe_bench():
         n = region // slab
         perm = torch.from_numpy(np.random.default_rng(7).permutation(n).astype(np.int32)).cuda()
         for nt in (False, True):
-            for wgs in (512, 1024):
+            for wgs in (512, 1024, 1536, 2048):
                 per = n // wgs
                 t = timed(lambda: pkv.read_probe(buf, sink, perm, slab, wgs, nt))
                 rows.append({"pattern": f"random {slab // 1024} KiB slabs", "bytes": per * wgs * slab,
