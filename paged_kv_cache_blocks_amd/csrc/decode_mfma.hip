@@ -134,25 +134,34 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int n = lane & 15, g = lane >> 4;
   const int hk = a.n_kv * a.head_chunks;
-  const int kvc = blockIdx.x % hk;
+  // Workgroup -> (unit slot, KV head chunk): the dispatcher deals workgroups
+  // to the eight XCDs in turn (workgroup b to XCD b % 8), so the hk workgroups
+  // of one unit slot are numbered 8 apart and share an XCD and its L2: the
+  // sequence's table entries and, with fp8, each block's line of per-head
+  // scales are then read from memory once per XCD instead of once per KV
+  // head.  The grid rounds the slots up to a multiple of 8.
+  const int xcd = blockIdx.x % 8, jx = blockIdx.x / 8;
+  const int kvc = jx % hk;
+  const int slot = (jx / hk) * 8 + xcd;
+  if (slot >= a.batch * a.n_parts) return;
   // The unit (sequence, partition) of this workgroup; results do not depend
   // on which workgroup takes which unit.  With a unit order (split calls,
-  // pkv_paged_attn_decode_order) entry blockIdx / hk names the unit, longest
-  // first, and -1 marks a unit without tokens, so real second partitions start
-  // early and the empty ones come last.  Otherwise the grid is partition by
-  // partition, its sequence slots mapped through the caller's sequence order if
-  // any (long sequences paired with short ones on a CU, or the longest first).
+  // pkv_paged_attn_decode_order) entry `slot` names the unit, longest first,
+  // and -1 marks a unit without tokens, so real second partitions start early
+  // and the empty ones come last.  Otherwise the slots run partition by
+  // partition, mapped through the caller's sequence order if any (long
+  // sequences paired with short ones on a CU, or the longest first).
   int s, part;
   if (a.work_order && a.order_units) {
-    const int u = __builtin_amdgcn_readfirstlane(a.work_order[blockIdx.x / hk]);
+    const int u = __builtin_amdgcn_readfirstlane(a.work_order[slot]);
     if (u < 0) return;
     const int uc = min(u, a.batch * a.n_parts - 1);
     s = uc / a.n_parts;
     part = uc % a.n_parts;
   } else {
-    s = (blockIdx.x / hk) % a.batch;
+    s = slot % a.batch;
     if (a.work_order) s = __builtin_amdgcn_readfirstlane(min(max(a.work_order[s], 0), a.batch - 1));
-    part = blockIdx.x / (hk * a.batch);
+    part = slot / a.batch;
   }
   const int kvh = kvc / a.head_chunks;
   const int h0 = kvh * a.group + (kvc % a.head_chunks) * GW;
@@ -479,7 +488,8 @@ static hipError_t launch_kind(const DecodeArgs& a, unsigned wgs, hipStream_t str
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int kv_kind, hipStream_t stream) {
-  const int64_t wgs = (int64_t)a.n_parts * a.n_kv * a.head_chunks * a.batch;
+  // unit slots rounded up to a multiple of 8, each with its KV head chunks
+  const int64_t wgs = ((int64_t)a.n_parts * a.batch + 7) / 8 * 8 * a.n_kv * a.head_chunks;
   if (wgs > 0x7fffffff) return hipErrorInvalidValue;
   return kv_kind == KIND_FP8 ? launch_kind<KIND_FP8>(a, (unsigned)wgs, stream)
                              : launch_kind<KIND_BF16>(a, (unsigned)wgs, stream);

@@ -642,7 +642,10 @@ pkv_status pkv_paged_attn_decode_plan(int32_t batch, int32_t n_q_heads, int32_t 
   info[0] = plan.n_wg ? 1 : 0;
   info[1] = plan.part_tokens;
   info[2] = plan.n_parts;
-  info[3] = plan.n_wg ? plan.n_wg : (int32_t)std::min<int64_t>(pairs * plan.n_parts, 0x7fffffff);
+  // (the matrix-core kernel numbers its unit slots in eights, one XCD each)
+  const int64_t slots = (int64_t)batch * plan.n_parts;
+  const int64_t split_wgs = plan.use_mfma ? (slots + 7) / 8 * 8 * (pairs / batch) : pairs * plan.n_parts;
+  info[3] = plan.n_wg ? plan.n_wg : (int32_t)std::min<int64_t>(split_wgs, 0x7fffffff);
   info[4] = (plan.n_wg || plan.n_parts > 1) ? 1 : 0;
   info[5] = (n_q_heads / n_kv_heads) / plan.head_chunks;
   info[6] = plan.use_mfma;

@@ -256,7 +256,8 @@ def test_decode_plan_argument_checks(pkv):
     with pytest.raises(pkv.PkvError):
         pkv.paged_attn_decode_plan(2, 8, 2, 64, 7, 16, pkv.BF16, 300)  # partition not a multiple of 256
     p = pkv.paged_attn_decode_plan(3, 32, 8, 128, 256, 16, pkv.BF16, 1024)
-    assert p == {"split": "partitions", "partition_tokens": 1024, "n_parts": 4, "workgroups": 3 * 8 * 4,
+    # 3 x 4 (sequence, partition) slots, numbered in eights (one XCD each): 16 slots x 8 KV heads
+    assert p == {"split": "partitions", "partition_tokens": 1024, "n_parts": 4, "workgroups": 16 * 8,
                  "merge_pass": True, "heads_per_workgroup": 4, "matrix_cores": True}
     p = pkv.paged_attn_decode_plan(3, 64, 8, 128, 64, 16, pkv.FP8_E4M3FN, 1024)
     assert p["n_parts"] == 1 and not p["merge_pass"] and p["heads_per_workgroup"] == 8 and p["matrix_cores"]
