@@ -14,7 +14,8 @@
 //
 // Work decomposition (as the VALU kernel's partition mode): one workgroup per
 // (sequence, KV head chunk, partition), in the caller's work order if given
-// (sequences, or (sequence, partition) units); its four waves take 32-token chunks
+// (sequences, or (sequence, partition) units), the KV head chunks of one
+// (sequence, partition) on one XCD; its four waves take 32-token chunks
 // (two 16-token tiles) round robin and keep their own running state, merged
 // at the end through LDS.  Each tile is two 8-token halves, each inside one
 // cache block whatever the block size (8 .. 256) and table format.  Per chunk
