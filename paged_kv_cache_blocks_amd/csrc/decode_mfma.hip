@@ -140,7 +140,9 @@ __global__ __launch_bounds__(256, KIND == KIND_FP8 ? 3 : 2) void decode_mfma_ker
   // of one unit slot are numbered 8 apart and share an XCD and its L2: the
   // sequence's table entries and, with fp8, each block's line of per-head
   // scales are then read from memory once per XCD instead of once per KV
-  // head.  The grid rounds the slots up to a multiple of 8.
+  // head.  The grid rounds the slots up to a multiple of 8.  (8 is MI355X's
+  // XCD count in its single-partition mode; with another count only the L2
+  // sharing is lost, never a result.)
   const int xcd = blockIdx.x % 8, jx = blockIdx.x / 8;
   const int kvc = jx % hk;
   const int slot = (jx / hk) * 8 + xcd;
