@@ -665,58 +665,6 @@ __global__ __launch_bounds__(kWave * kCombineHeads) void combine_kernel(DecodeAr
     store_out(a, ((int64_t)s * a.n_q + hq) * D + lane + k * kWave, den > 0.f ? num[k] / den : 0.f);
 }
 
-// The same merge for calls of at most kFewParts partitions per sequence (the
-// 70B-shaped 32K decode has 8, the fp8 serving mix 2): every lane reads all
-// the partitions' (max, sum) pairs together with its output columns, so the
-// merge waits for one round trip after the length instead of one for the
-// maxima and more for the outputs.  Slots past a sequence's partitions read
-// partition 0's words again and are not used.
-constexpr int kFewParts = 8;
-template <int D>
-__global__ __launch_bounds__(kWave * kCombineHeads) void combine_few_kernel(DecodeArgs a) {
-  constexpr int COLS = D / kWave;
-  constexpr int G = kFewParts;
-  const int lane = threadIdx.x % kWave;
-  const int hq = blockIdx.x * (blockDim.x / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int s = blockIdx.y;
-  const int L = clamp_len(a, s);
-  const int nv = min((L + a.part_tokens - 1) / a.part_tokens, G);
-  if (nv == 1 || hq >= a.n_q) return;  // one partition: the split kernel wrote this sequence's output itself
-  const int64_t base = ((int64_t)s * a.n_q + hq) * a.n_parts;
-  const float* ml = a.ws_ml + base * 2;
-  const float* op = a.ws_o + base * D;
-  float mg[G], lg[G], xg[G][COLS];
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-    const int jj = j < nv ? j : 0;
-    mg[j] = ml[2 * jj];
-    lg[j] = ml[2 * jj + 1];
-#pragma unroll
-    for (int k = 0; k < COLS; ++k) xg[j][k] = op[(int64_t)jj * D + lane + k * kWave];
-  }
-  float M = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < G; ++j)
-    if (j < nv) M = fmaxf(M, mg[j]);
-  float den = 0.f, num[COLS];
-#pragma unroll
-  for (int k = 0; k < COLS; ++k) num[k] = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      if (j < nv) {
-        const float e = (mg[j] == -INFINITY) ? 0.f : exp2_fast(mg[j] - M);
-        den = fmaf(e, lg[j], den);
-#pragma unroll
-        for (int k = 0; k < COLS; ++k) num[k] = fmaf(e, xg[j][k], num[k]);
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < COLS; ++k)
-    store_out(a, ((int64_t)s * a.n_q + hq) * D + lane + k * kWave, den > 0.f ? num[k] / den : 0.f);
-}
-
 // ---------------------------------------------------------------------------
 // Work-queue mode.  Every (sequence, KV head chunk) pair is cut into items of
 // U consecutive blocks (the last one shorter), with U chosen on the device so
@@ -1125,12 +1073,8 @@ static hipError_t launch_one(const DecodeArgs& a, hipStream_t stream) {
   }
   if (e != hipSuccess || a.n_parts == 1) return e;
   const int heads = a.n_q < kCombineHeads ? a.n_q : kCombineHeads;
-  if (a.n_parts <= kFewParts)
-    hipLaunchKernelGGL((combine_few_kernel<D>), dim3((a.n_q + heads - 1) / heads, a.batch), dim3(kWave * heads), 0,
-                       stream, a);
-  else
-    hipLaunchKernelGGL((combine_kernel<D>), dim3((a.n_q + heads - 1) / heads, a.batch), dim3(kWave * heads), 0, stream,
-                       a);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((a.n_q + heads - 1) / heads, a.batch), dim3(kWave * heads), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
