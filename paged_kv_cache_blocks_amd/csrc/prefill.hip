@@ -488,9 +488,9 @@ bool prefill_supported_group(int group) {
 // per 16-row tile the wave owns.  Three row tiles (48 rows per wave, 192 per
 // workgroup; the group size must divide 192) cut the fragment reads per
 // product by a third and still fit two waves per SIMD (256 registers, a few
-// spilled outside the key loop).  Measured on the 16 x 512-token chunk this
-// runs 1-2% faster than two row tiles: the kernel is not bound by LDS
-// bandwidth.  FP8 caches keep two tiles (their conversion pass needs the
+// spilled outside the key loop).  Measured on the 16 x 512-token chunk with
+// both builds called in alternation in one process: 425 against 462 us for
+// two row tiles.  FP8 caches keep two tiles (their conversion pass needs the
 // registers).
 static bool three_row_tiles(const PrefillArgs& a) {
   return !a.kv_fp8 && (192 % a.group) == 0;
